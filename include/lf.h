@@ -1,0 +1,171 @@
+/*
+ * lf.h - C ABI of the MI355X (gfx950) Longformer band + global attention library.
+ *
+ * Source of the operations: the page "FasterTransformer Longformer 推理加速实践：
+ * PyTorch 集成、输入约束与端到端性能解析" (cited as [FT-LF]), sections
+ * "使用前提：四条硬性约束" (four hard constraints) and "Longformer Encoder 计算流程"
+ * (encoder computation flow: input list, preprocessing list, per-layer steps 1-6).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers are device pointers to caller-owned, contiguous buffers, unless a
+ *    comment says otherwise.  The library keeps no reference after a call returns.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Every
+ *    call only enqueues work on `stream` and returns without waiting, except
+ *    lf_check_masks, which synchronises.  Keep buffers alive until the stream has
+ *    passed the call.  Outputs must not alias inputs.
+ *  - dtype: one of lf_dtype.  Activations, masks and outputs share it.
+ *  - head_dim is fixed at 64 ([FT-LF] hard constraint 2); it is not a parameter.
+ *  - q, k, v, kg, vg, out are [B, H, S, 64] row-major; qg is [B, H, G, 64];
+ *    local_mask, global_mask and local_bias are [B, S]; global_idx is int32 [B, S];
+ *    global_count is int32 [B].
+ *  - Masks ([FT-LF] input list): local_mask 1.0 = token attends, 0.0 = padding;
+ *    global_mask 0.0 = global token, -10000.0 = ordinary token.
+ *  - Shape rules are checked on the host before anything is enqueued: B, H, S >= 1;
+ *    W even and >= 2; S % W == 0 and S >= 2W ([FT-LF] hard constraint 1);
+ *    0 <= G <= W ([FT-LF] hard constraint 3, in the inclusive form the page says
+ *    the code checks); B*H*S <= 2^31 - 1; pointers non-NULL (qg may be NULL when
+ *    G == 0).  On a violation nothing is enqueued, outputs are untouched, the call
+ *    returns LF_ERR_INVALID_ARGUMENT and lf_last_error() names the rule.
+ *  - Data-dependent preconditions are NOT checked on the fast path (the result is
+ *    unspecified when they are violated): global tokens sit contiguously at the
+ *    head of each sequence ([FT-LF] hard constraint 4); at most G of them per
+ *    sequence; masks hold only the values above.  lf_check_masks verifies them,
+ *    and setting the environment variable LF_DEBUG_CHECK=1 makes lf_attn_forward
+ *    call it first.
+ *  - Return value: an lf_status.  LF_ERR_HIP means a HIP call failed while
+ *    enqueuing; lf_last_error() (thread-local) holds the message.
+ */
+#ifndef LF_H
+#define LF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { LF_F32 = 0, LF_F16 = 1, LF_BF16 = 2 } lf_dtype;
+
+typedef enum {
+  LF_OK = 0,
+  LF_ERR_INVALID_ARGUMENT = 1,
+  LF_ERR_UNSUPPORTED = 2,
+  LF_ERR_HIP = 3,
+  LF_ERR_PRECONDITION = 4
+} lf_status;
+
+/*
+ * Global-token index extraction ([FT-LF] computation flow, preprocessing item 1).
+ * For each batch row b, position s is flagged iff global_mask[b,s] == 0.0.
+ * global_idx[b,:] receives a stable partition of 0..S-1: the flagged positions in
+ * ascending order, then the other positions in descending order (the layout of a
+ * flagged device partition).  global_count[b] receives the number of flagged
+ * positions.  Integer results; bit-exact.
+ */
+int lf_init_global_idx(int dtype, const void* global_mask, int B, int S,
+                       int32_t* global_idx, int32_t* global_count, void* stream);
+
+/*
+ * Local-mask shift ([FT-LF] computation flow, preprocessing item 2):
+ * local_bias = fma(local_mask, 10000, -10000) evaluated in fp32 and stored in
+ * `dtype` with round-to-nearest-even (1 -> 0, 0 -> -10000; bf16 stores -9984).
+ * local_mask and local_bias are [B, S]; any B*S >= 1 is accepted.
+ */
+int lf_mask_shift(int dtype, const void* local_mask, int B, int S, void* local_bias,
+                  void* stream);
+
+/*
+ * Band + global attention ([FT-LF] computation flow, per-layer steps 3 and 4).
+ * With scale c = 1/8 (= 1/sqrt(64)), n_b = number of global tokens of sequence b
+ * (positions 0..n_b-1 under the head-of-sequence precondition) and live keys
+ * those with local_mask == 1:
+ *   - a row with local_mask 0 is written as +0.0;
+ *   - a global row s = r (r < n_b) is softmax_j(c <qg[r], kg[j]>) . vg[j] over
+ *     every live key j of the sequence;
+ *   - any other row s is softmax over the live keys j with |j - s| <= W/2,
+ *     j >= n_b, plus the live global keys j < n_b, of c <q[s], k[j]>, weighting
+ *     v[j].  Global keys are therefore counted once.
+ * Padding enters as the additive -10000 score bias of the mask shift.  Runs the
+ * index extraction and the mask shift itself; needs temporary device memory,
+ * taken with hipMallocAsync on `stream` and returned with hipFreeAsync.
+ * fp16 / bf16 run on MFMA with fp32 accumulation; fp32 runs on fp32 FMA.
+ */
+int lf_attn_forward(int dtype, const void* q, const void* k, const void* v,
+                    const void* qg, const void* kg, const void* vg,
+                    const void* local_mask, const void* global_mask,
+                    int B, int H, int S, int W, int G, void* out, void* stream);
+
+/* Bytes of workspace lf_attn_forward_pre needs for this shape (0 on bad arguments). */
+size_t lf_attn_workspace_bytes(int dtype, int B, int H, int S, int W, int G);
+
+/*
+ * Same computation as lf_attn_forward on already-preprocessed masks: global_idx /
+ * global_count from lf_init_global_idx and local_bias from lf_mask_shift.  It
+ * allocates nothing: `workspace` (device, 256-byte aligned, ws_bytes >=
+ * lf_attn_workspace_bytes) holds the partial results of the global rows; its
+ * contents on entry do not matter.  Calls that share a workspace must not overlap.
+ */
+int lf_attn_forward_pre(int dtype, const void* q, const void* k, const void* v,
+                        const void* qg, const void* kg, const void* vg,
+                        const int32_t* global_idx, const int32_t* global_count,
+                        const void* local_bias, int B, int H, int S, int W, int G,
+                        void* out, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * Synchronous check of the data-dependent preconditions: every local_mask value is
+ * 0 or 1; every global_mask value is 0 or -10000 (as stored in `dtype`); the
+ * global tokens of each sequence are positions 0..n_b-1 with n_b <= G.  Returns
+ * LF_OK or LF_ERR_PRECONDITION (lf_last_error() names the first violation).
+ */
+int lf_check_masks(int dtype, const void* local_mask, const void* global_mask, int B,
+                   int S, int G, void* stream);
+
+/*
+ * Weights of one encoder layer ([FT-LF] computation flow, per-layer steps 1-6).
+ * All are device pointers in the layer dtype.  Matrices are [out, in] row-major
+ * (y = x W^T + b).  w_proj is [5*hidden, hidden]: row blocks Q | K | V |
+ * global-K | global-V, and inside each block head h owns rows 64h .. 64h+63.
+ */
+typedef struct {
+  const void* w_proj; const void* b_proj;   /* [5D, D], [5D] */
+  const void* w_qg;   const void* b_qg;     /* [D, D],  [D]  global query */
+  const void* w_o;    const void* b_o;      /* [D, D],  [D]  attention output */
+  const void* ln1_g;  const void* ln1_b;    /* [D] */
+  const void* w_ffn1; const void* b_ffn1;   /* [F, D],  [F] */
+  const void* w_ffn2; const void* b_ffn2;   /* [D, F],  [D] */
+  const void* ln2_g;  const void* ln2_b;    /* [D] */
+} lf_layer_weights;
+
+/* Workspace bytes lf_encoder_layer needs (0 on bad arguments). */
+size_t lf_encoder_layer_workspace_bytes(int dtype, int B, int S, int hidden, int H, int ffn,
+                                        int W, int G);
+
+/*
+ * One post-LayerNorm Longformer encoder layer ([FT-LF] per-layer steps 1-6):
+ *   [q|k|v|kg|vg] = x W_proj^T + b_proj, split into heads; qg = x[:, :G] W_qg^T + b_qg;
+ *   a  = band + global attention (as lf_attn_forward, scale attn_scale), heads joined;
+ *   h1 = LayerNorm(x + a W_o^T + b_o; ln1)    (biased variance, eps ln_eps)
+ *   y  = LayerNorm(h1 + GELU(h1 W_1^T + b_1) W_2^T + b_2; ln2)   (exact erf GELU)
+ * x, y: [B, S, hidden].  Requires hidden == 64*H and hidden % 64 == 0, ffn % 64 == 0,
+ * plus the attention shape rules.  `workspace` (device, ws_bytes >=
+ * lf_encoder_layer_workspace_bytes) holds the intermediates; the residual stream
+ * is kept in fp32 there.  Currently implemented for LF_F16 and LF_BF16.
+ */
+int lf_encoder_layer(int dtype, const lf_layer_weights* w, const void* x,
+                     const void* local_mask, const void* global_mask, int B, int S,
+                     int hidden, int H, int ffn, int W, int G, float attn_scale,
+                     float ln_eps, void* y, void* workspace, size_t ws_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* lf_status_string(int status);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* lf_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LF_H */

@@ -1,0 +1,282 @@
+// C ABI of the library: argument validation (pure host code, runs before any HIP
+// call), workspace layout, dispatch to the kernels, status / error text.
+//
+// [FT-LF] = the page "FasterTransformer Longformer 推理加速实践：PyTorch 集成、输入约束与
+// 端到端性能解析".  The shape rules are its four hard constraints (section
+// "使用前提：四条硬性约束"); where the page's implementation aborts the process on a
+// violation, these entry points return LF_ERR_INVALID_ARGUMENT instead.
+#include <climits>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "../../include/lf.h"
+#include "lf_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return LF_OK;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(LF_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+size_t dtype_size(int dtype) { return dtype == LF_F32 ? 4 : 2; }
+
+bool known_dtype(int dtype) { return dtype == LF_F32 || dtype == LF_F16 || dtype == LF_BF16; }
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Shape rules of the attention entry points; returns LF_OK or an error code.
+int validate_attn(int dtype, int B, int H, int S, int W, int G) {
+  if (!known_dtype(dtype)) return fail(LF_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+  if (B < 1 || H < 1 || S < 1)
+    return fail(LF_ERR_INVALID_ARGUMENT, "B, H, S must be >= 1 (got %d, %d, %d)", B, H, S);
+  if (W < 2 || (W & 1))
+    return fail(LF_ERR_INVALID_ARGUMENT, "window W must be even and >= 2 (got %d)", W);
+  if (S % W != 0)
+    return fail(LF_ERR_INVALID_ARGUMENT, "S %% W must be 0 (S=%d, W=%d)", S, W);
+  if (S < 2 * W)
+    return fail(LF_ERR_INVALID_ARGUMENT, "S must be >= 2*W (S=%d, W=%d)", S, W);
+  if (G < 0 || G > W)
+    return fail(LF_ERR_INVALID_ARGUMENT, "G must satisfy 0 <= G <= W (G=%d, W=%d)", G, W);
+  if ((int64_t)B * H * S > INT_MAX)
+    return fail(LF_ERR_INVALID_ARGUMENT, "B*H*S exceeds 2^31-1");
+  return LF_OK;
+}
+
+int null_check(const char* names, std::initializer_list<const void*> ptrs) {
+  int i = 0;
+  for (const void* p : ptrs) {
+    if (!p) {
+      // names is a comma-separated list in the same order as ptrs
+      const char* s = names;
+      for (int j = 0; j < i && s; ++j) {
+        s = strchr(s, ',');
+        if (s) ++s;
+      }
+      std::string nm = s ? std::string(s, strcspn(s, ",")) : "?";
+      return fail(LF_ERR_INVALID_ARGUMENT, "null pointer: %s", nm.c_str());
+    }
+    ++i;
+  }
+  return LF_OK;
+}
+
+// Workspace of lf_attn_forward_pre: global-row partials.
+struct AttnWs {
+  size_t partials;
+  int n_split, split_len;
+};
+
+AttnWs attn_ws(int B, int H, int S, int G) {
+  AttnWs w;
+  w.partials = align256(lf::attn_partials_bytes(B, H, S, G, &w.n_split, &w.split_len));
+  return w;
+}
+
+lf::AttnArgs make_args(int dtype, const void* q, const void* k, const void* v, const void* qg,
+                       const void* kg, const void* vg, const int32_t* gidx, const int32_t* gcnt,
+                       const void* bias, int B, int H, int S, int W, int G, void* out,
+                       float* partials, const AttnWs& ws) {
+  lf::AttnArgs a;
+  a.dtype = dtype;
+  a.q = q; a.k = k; a.v = v; a.qg = qg; a.kg = kg; a.vg = vg;
+  a.gidx = gidx; a.gcnt = gcnt; a.bias = bias; a.out = out;
+  a.out_ss = 64;
+  a.out_sh = (int64_t)S * 64;
+  a.out_sb = (int64_t)H * S * 64;
+  a.B = B; a.H = H; a.S = S; a.W = W; a.G = G;
+  a.scale = 0.125f;
+  a.partials = partials;
+  a.n_split = ws.n_split;
+  a.split_len = ws.split_len;
+  return a;
+}
+
+hipError_t run_attention(const lf::AttnArgs& a, hipStream_t st) {
+  return a.dtype == LF_F32 ? lf::launch_attention_fp32(a, st) : lf::launch_attention(a, st);
+}
+
+bool debug_check_enabled() {
+  const char* e = getenv("LF_DEBUG_CHECK");
+  return e && e[0] == '1';
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* lf_status_string(int status) {
+  switch (status) {
+    case LF_OK: return "ok";
+    case LF_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case LF_ERR_UNSUPPORTED: return "unsupported";
+    case LF_ERR_HIP: return "HIP error";
+    case LF_ERR_PRECONDITION: return "precondition violated";
+  }
+  return "unknown status";
+}
+
+const char* lf_last_error(void) { return g_last_error.c_str(); }
+
+int lf_init_global_idx(int dtype, const void* global_mask, int B, int S, int32_t* global_idx,
+                       int32_t* global_count, void* stream) {
+  if (!known_dtype(dtype)) return fail(LF_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+  if (B < 1 || S < 1) return fail(LF_ERR_INVALID_ARGUMENT, "B, S must be >= 1");
+  if ((int64_t)B * S > INT_MAX) return fail(LF_ERR_INVALID_ARGUMENT, "B*S exceeds 2^31-1");
+  if (int e = null_check("global_mask,global_idx,global_count",
+                         {global_mask, global_idx, global_count}))
+    return e;
+  hipError_t he = lf::launch_prep(dtype, global_mask, nullptr, B, S, global_idx, global_count,
+                                  nullptr, (hipStream_t)stream);
+  if (he != hipSuccess) return hip_fail(he, "lf_init_global_idx");
+  return ok();
+}
+
+int lf_mask_shift(int dtype, const void* local_mask, int B, int S, void* local_bias,
+                  void* stream) {
+  if (!known_dtype(dtype)) return fail(LF_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+  if (B < 1 || S < 1) return fail(LF_ERR_INVALID_ARGUMENT, "B, S must be >= 1");
+  if (int e = null_check("local_mask,local_bias", {local_mask, local_bias})) return e;
+  hipError_t he = lf::launch_mask_shift(dtype, local_mask, (int64_t)B * S, local_bias,
+                                        (hipStream_t)stream);
+  if (he != hipSuccess) return hip_fail(he, "lf_mask_shift");
+  return ok();
+}
+
+size_t lf_attn_workspace_bytes(int dtype, int B, int H, int S, int W, int G) {
+  if (validate_attn(dtype, B, H, S, W, G) != LF_OK) return 0;
+  return attn_ws(B, H, S, G).partials;
+}
+
+int lf_attn_forward_pre(int dtype, const void* q, const void* k, const void* v, const void* qg,
+                        const void* kg, const void* vg, const int32_t* global_idx,
+                        const int32_t* global_count, const void* local_bias, int B, int H, int S,
+                        int W, int G, void* out, void* workspace, size_t ws_bytes,
+                        void* stream) {
+  if (int e = validate_attn(dtype, B, H, S, W, G)) return e;
+  if (int e = null_check("q,k,v,kg,vg,global_idx,global_count,local_bias,out,workspace",
+                         {q, k, v, kg, vg, global_idx, global_count, local_bias, out, workspace}))
+    return e;
+  if (G > 0 && !qg) return fail(LF_ERR_INVALID_ARGUMENT, "null pointer: qg (G > 0)");
+  const AttnWs ws = attn_ws(B, H, S, G);
+  if (ws_bytes < ws.partials)
+    return fail(LF_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu", ws_bytes,
+                ws.partials);
+  if (((uintptr_t)workspace) & 255)
+    return fail(LF_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  lf::AttnArgs a = make_args(dtype, q, k, v, qg, kg, vg, global_idx, global_count, local_bias, B,
+                             H, S, W, G, out, (float*)workspace, ws);
+  hipError_t he = run_attention(a, (hipStream_t)stream);
+  if (he != hipSuccess) return hip_fail(he, "lf_attn_forward_pre");
+  return ok();
+}
+
+int lf_check_masks(int dtype, const void* local_mask, const void* global_mask, int B, int S,
+                   int G, void* stream) {
+  if (!known_dtype(dtype)) return fail(LF_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+  if (B < 1 || S < 1 || G < 0) return fail(LF_ERR_INVALID_ARGUMENT, "bad B, S or G");
+  if ((int64_t)B * S >= INT_MAX) return fail(LF_ERR_INVALID_ARGUMENT, "B*S too large");
+  if (int e = null_check("local_mask,global_mask", {local_mask, global_mask})) return e;
+  hipStream_t st = (hipStream_t)stream;
+  int* dflags = nullptr;
+  hipError_t he = hipMallocAsync((void**)&dflags, 4 * sizeof(int), st);
+  if (he != hipSuccess) return hip_fail(he, "lf_check_masks alloc");
+  const int init[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};
+  int flags[4];
+  he = hipMemcpyAsync(dflags, init, sizeof init, hipMemcpyHostToDevice, st);
+  if (he == hipSuccess)
+    he = lf::launch_check_masks(dtype, local_mask, global_mask, B, S, G, dflags, st);
+  if (he == hipSuccess)
+    he = hipMemcpyAsync(flags, dflags, sizeof flags, hipMemcpyDeviceToHost, st);
+  hipError_t he2 = hipFreeAsync(dflags, st);
+  if (he == hipSuccess) he = he2;
+  if (he == hipSuccess) he = hipStreamSynchronize(st);
+  if (he != hipSuccess) return hip_fail(he, "lf_check_masks");
+  if (flags[0] != INT_MAX)
+    return fail(LF_ERR_PRECONDITION, "local_mask[%d] is neither 0 nor 1", flags[0] - 1);
+  if (flags[1] != INT_MAX)
+    return fail(LF_ERR_PRECONDITION, "global_mask[%d] is neither 0 nor -10000", flags[1] - 1);
+  if (flags[2] != INT_MAX)
+    return fail(LF_ERR_PRECONDITION,
+                "global tokens of batch row %d are not contiguous at the sequence head",
+                flags[2] - 1);
+  if (flags[3] != INT_MAX)
+    return fail(LF_ERR_PRECONDITION, "batch row %d has more than G=%d global tokens",
+                flags[3] - 1, G);
+  return ok();
+}
+
+int lf_attn_forward(int dtype, const void* q, const void* k, const void* v, const void* qg,
+                    const void* kg, const void* vg, const void* local_mask,
+                    const void* global_mask, int B, int H, int S, int W, int G, void* out,
+                    void* stream) {
+  if (int e = validate_attn(dtype, B, H, S, W, G)) return e;
+  if (int e = null_check("q,k,v,kg,vg,local_mask,global_mask,out",
+                         {q, k, v, kg, vg, local_mask, global_mask, out}))
+    return e;
+  if (G > 0 && !qg) return fail(LF_ERR_INVALID_ARGUMENT, "null pointer: qg (G > 0)");
+  hipStream_t st = (hipStream_t)stream;
+  if (debug_check_enabled()) {
+    if (int e = lf_check_masks(dtype, local_mask, global_mask, B, S, G, stream)) return e;
+  }
+  const AttnWs ws = attn_ws(B, H, S, G);
+  const size_t n_bs = (size_t)B * S;
+  const size_t off_idx = 0;
+  const size_t off_cnt = align256(off_idx + n_bs * sizeof(int32_t));
+  const size_t off_bias = align256(off_cnt + (size_t)B * sizeof(int32_t));
+  const size_t off_part = align256(off_bias + n_bs * dtype_size(dtype));
+  const size_t total = off_part + ws.partials;
+  char* scratch = nullptr;
+  hipError_t he = hipMallocAsync((void**)&scratch, total, st);
+  if (he != hipSuccess) return hip_fail(he, "lf_attn_forward scratch");
+  int32_t* gidx = (int32_t*)(scratch + off_idx);
+  int32_t* gcnt = (int32_t*)(scratch + off_cnt);
+  void* bias = scratch + off_bias;
+  he = lf::launch_prep(dtype, global_mask, local_mask, B, S, gidx, gcnt, bias, st);
+  if (he == hipSuccess) {
+    lf::AttnArgs a = make_args(dtype, q, k, v, qg, kg, vg, gidx, gcnt, bias, B, H, S, W, G, out,
+                               (float*)(scratch + off_part), ws);
+    he = run_attention(a, st);
+  }
+  hipError_t he2 = hipFreeAsync(scratch, st);
+  if (he != hipSuccess) return hip_fail(he, "lf_attn_forward");
+  if (he2 != hipSuccess) return hip_fail(he2, "lf_attn_forward free");
+  return ok();
+}
+
+size_t lf_encoder_layer_workspace_bytes(int dtype, int B, int S, int hidden, int H, int ffn,
+                                        int W, int G) {
+  (void)dtype; (void)B; (void)S; (void)hidden; (void)H; (void)ffn; (void)W; (void)G;
+  return 0;
+}
+
+int lf_encoder_layer(int dtype, const lf_layer_weights* w, const void* x, const void* local_mask,
+                     const void* global_mask, int B, int S, int hidden, int H, int ffn, int W,
+                     int G, float attn_scale, float ln_eps, void* y, void* workspace,
+                     size_t ws_bytes, void* stream) {
+  (void)dtype; (void)w; (void)x; (void)local_mask; (void)global_mask; (void)B; (void)S;
+  (void)hidden; (void)H; (void)ffn; (void)W; (void)G; (void)attn_scale; (void)ln_eps; (void)y;
+  (void)workspace; (void)ws_bytes; (void)stream;
+  return fail(LF_ERR_UNSUPPORTED, "lf_encoder_layer: not built yet");
+}
+
+}  // extern "C"

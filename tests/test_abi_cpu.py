@@ -1,0 +1,118 @@
+"""CPU-side checks of the C ABI: the library loads, exports every symbol the header
+declares, and rejects bad arguments on the host before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_long_sequence_amd as lf
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lf.h")
+
+INVALID = 1
+UNSUPPORTED = 2
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lf_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(lf.library_path()):
+        pytest.skip("liblf.so not built")
+    return lf.load_library()
+
+
+def test_header_declares_expected_entry_points():
+    assert set(_declared()) == set(lf.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    assert lib.lf_status_string(0) == b"ok"
+    assert lib.lf_status_string(1) == b"invalid argument"
+    assert lib.lf_status_string(4) == b"precondition violated"
+
+
+def _fake(n=1):
+    return ctypes.c_void_p(0x1000)
+
+
+def _attn(lib, dtype=1, B=1, H=2, S=64, W=16, G=2, null=None):
+    p = {n: _fake() for n in ("q", "k", "v", "qg", "kg", "vg", "lm", "gm", "out")}
+    if null:
+        p[null] = None
+    return lib.lf_attn_forward(dtype, p["q"], p["k"], p["v"], p["qg"], p["kg"], p["vg"], p["lm"],
+                               p["gm"], B, H, S, W, G, p["out"], None)
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(S=60, W=16), "S % W"),          # hard constraint 1: divisibility
+    (dict(S=16, W=16), "S must be >= 2*W"),
+    (dict(G=17, W=16), "G must satisfy"),  # hard constraint 3
+    (dict(G=-1), "G must satisfy"),
+    (dict(W=15, S=60), "even"),
+    (dict(W=0), "even"),
+    (dict(B=0), ">= 1"),
+    (dict(H=0), ">= 1"),
+    (dict(dtype=7), "dtype"),
+])
+def test_attn_shape_rules_rejected_on_host(lib, kw, msg):
+    assert _attn(lib, **kw) == INVALID
+    assert msg in lib.lf_last_error().decode()
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "kg", "vg", "lm", "gm", "out", "qg"])
+def test_attn_null_pointers_rejected(lib, name):
+    assert _attn(lib, null=name) == INVALID
+    assert "null pointer" in lib.lf_last_error().decode()
+
+
+def test_qg_may_be_null_without_globals(lib):
+    # G == 0 and qg NULL passes validation; a NULL k still fails, proving no launch happened
+    p = _fake()
+    st = lib.lf_attn_forward(1, p, None, p, None, p, p, p, p, 1, 1, 64, 16, 0, p, None)
+    assert st == INVALID and "k" in lib.lf_last_error().decode()
+
+
+def test_workspace_size_query(lib):
+    assert lib.lf_attn_workspace_bytes(1, 1, 16, 4096, 512, 8) > 0
+    assert lib.lf_attn_workspace_bytes(1, 1, 16, 4095, 512, 8) == 0   # bad shape -> 0
+    assert lib.lf_attn_workspace_bytes(1, 1, 16, 4096, 512, 8) % 256 == 0
+
+
+def test_pre_rejects_small_or_misaligned_workspace(lib):
+    p = _fake()
+    need = lib.lf_attn_workspace_bytes(1, 1, 2, 64, 16, 2)
+    st = lib.lf_attn_forward_pre(1, p, p, p, p, p, p, p, p, p, 1, 2, 64, 16, 2, p, p, need - 1,
+                                 None)
+    assert st == INVALID and "too small" in lib.lf_last_error().decode()
+    st = lib.lf_attn_forward_pre(1, p, p, p, p, p, p, p, p, p, 1, 2, 64, 16, 2, p,
+                                 ctypes.c_void_p(0x1008), need, None)
+    assert st == INVALID and "aligned" in lib.lf_last_error().decode()
+
+
+def test_prep_entry_points_validate(lib):
+    p = _fake()
+    assert lib.lf_init_global_idx(1, p, 0, 8, p, p, None) == INVALID
+    assert lib.lf_init_global_idx(1, None, 1, 8, p, p, None) == INVALID
+    assert lib.lf_init_global_idx(5, p, 1, 8, p, p, None) == INVALID
+    assert lib.lf_mask_shift(1, p, 1, 0, p, None) == INVALID
+    assert lib.lf_mask_shift(1, p, 1, 8, None, None) == INVALID
+    assert lib.lf_check_masks(1, None, p, 1, 8, 2, None) == INVALID
+
+
+def test_python_binding_refuses_cpu_tensors(lib):
+    import torch
+    x = torch.zeros(1, 8, dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU"):
+        lf.mask_shift(x)

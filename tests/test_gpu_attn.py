@@ -1,0 +1,234 @@
+"""GPU parity of band + global attention against the float64 oracle.
+
+[FT-LF] computation flow, per-layer steps 3-4.  Tolerances (max abs error on the
+outputs): fp32 1e-5, fp16 3e-3, bf16 1e-2.  Small and mid-size problems are
+compared element by element over the whole output; the full-size workloads, in
+the launch configuration the benchmark times, are compared on sampled rows the
+oracle computes one by one, plus properties that hold at any size (padded rows
+exactly +0.0, finite outputs, determinism)."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-5, "fp16": 3e-3, "bf16": 1e-2}
+
+
+@pytest.fixture(scope="module")
+def lf():
+    import sparse_long_sequence_amd as m
+    m.load_library()
+    return m
+
+
+def _gpu(inp):
+    return {n: t.cuda() for n, t in inp.items()}
+
+
+def _run(lf, g, W, G, out=None):
+    return lf.attn_forward(g["q"], g["k"], g["v"], g["qg"], g["kg"], g["vg"], g["local_mask"],
+                           g["global_mask"], W, G, out=out)
+
+
+def _oracle(inp, W, G, rows=None):
+    return oracle.attention(inp["q"], inp["k"], inp["v"], inp["qg"], inp["kg"], inp["vg"],
+                            inp["local_mask"], inp["global_mask"], W, G, rows=rows)
+
+
+def _check_padded_zero(out_cpu, lm):
+    live = (lm == 1).numpy()
+    o = out_cpu.float().numpy()
+    B = o.shape[0]
+    for b in range(B):
+        pad = o[b][:, ~live[b]]
+        assert np.all(pad == 0.0) and not np.any(np.signbit(pad)), "padded rows must be +0.0"
+
+
+def _full_compare(lf, inp, W, G, dtype):
+    g = _gpu(inp)
+    out = _run(lf, g, W, G)
+    torch.cuda.synchronize()
+    got = out.cpu()
+    ref = _oracle(inp, W, G)
+    err = np.abs(got.double().numpy() - ref)
+    assert np.isfinite(got.float().numpy()).all()
+    assert err.max() <= TOL[dtype], f"max abs err {err.max():.3e} (tol {TOL[dtype]})"
+    _check_padded_zero(got, inp["local_mask"])
+    return got, ref
+
+
+# ---------------------------------------------------------------- tiny workload (fp32)
+def test_tiny_fp32_workload(lf):
+    wl = workloads.TINY_FP32
+    inp = workloads.make_attention_inputs(wl)
+    _full_compare(lf, inp, wl.W, wl.G, "fp32")
+
+
+# ---------------------------------------------------------------- mid-size, every element
+CASES = [
+    # B, H, S, W, G, pad, n_global (None = G)
+    (1, 2, 64, 16, 2, None, None),       # tiny shape (single ragged tile)
+    (2, 3, 1024, 128, 5, (0.1, 0.25), None),
+    (1, 2, 384, 96, 7, (0.1, 0.3), None),   # S not a multiple of the 128-row tile
+    (1, 2, 1024, 512, 64, None, None),      # a full 64-key global chunk, two 32-row q-blocks
+    (2, 2, 1024, 512, 33, (0.05, 0.1), None),
+    (1, 2, 768, 256, 0, None, None),         # no global tokens at all
+    (1, 1, 256, 2, 1, None, None),           # narrowest window
+    (1, 1, 512, 256, 256, None, None),       # G == W: many global rows
+    (2, 1, 512, 128, 16, None, (3, 0)),      # fewer globals than capacity, one row none
+    (1, 2, 2048, 512, 8, (0.6, 0.7), None),  # heavy padding
+]
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16", "fp32"])
+@pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}H{c[1]}S{c[2]}W{c[3]}G{c[4]}" for c in CASES])
+def test_attention_parity_mid(lf, dtype, case):
+    B, H, S, W, G, pad, ng = case
+    inp = workloads.random_attention_inputs(zlib.crc32(repr(case).encode()) % 100000, B, H, S, W, G, dtype,
+                                            pad_frac=pad, n_global=ng)
+    _full_compare(lf, inp, W, G, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("std", [1.0, 2.0])
+def test_attention_stress_inputs(lf, dtype, std):
+    # larger scores exercise the running-max updates and rescaling
+    B, H, S, W, G = 2, 2, 1024, 256, 12
+    inp = workloads.random_attention_inputs(77, B, H, S, W, G, dtype, std=std,
+                                            pad_frac=(0.1, 0.2))
+    g = _gpu(inp)
+    got = _run(lf, g, W, G).cpu().double().numpy()
+    ref = _oracle(inp, W, G)
+    # the tolerance scales with the output magnitude (values ~ std)
+    err = np.abs(got - ref).max()
+    assert err <= TOL[dtype] * max(1.0, 2 * std), f"max abs err {err:.3e}"
+
+
+# ---------------------------------------------------------------- structure
+@pytest.mark.parametrize("dtype", ["fp16", "bf16", "fp32"])
+def test_identity_values_expose_band_support(lf, dtype):
+    # q = qg = 0 and v = vg = I (S = 64 = head_dim): row s is uniform on its allowed
+    # keys and exactly 0 elsewhere, so any band / exclusion error shows up as a
+    # nonzero entry where the oracle has 0.
+    S, W, G = 64, 16, 2
+    t = workloads.TORCH_DTYPES[dtype]
+    z = torch.zeros(1, 1, S, 64, dtype=t)
+    eye = torch.eye(64, dtype=t).view(1, 1, S, 64)
+    k = torch.randn(1, 1, S, 64, generator=torch.Generator().manual_seed(0)).to(t)
+    lm = torch.ones(1, S, dtype=t)
+    gm = torch.full((1, S), -10000.0).to(t)
+    gm[0, :G] = 0
+    inp = {"q": z, "k": k, "v": eye, "qg": torch.zeros(1, 1, G, 64, dtype=t), "kg": k,
+           "vg": eye, "local_mask": lm, "global_mask": gm}
+    got = _run(lf, _gpu(inp), W, G).cpu().double().numpy()
+    ref = _oracle(inp, W, G)
+    assert np.array_equal(got == 0, ref == 0)
+    assert np.abs(got - ref).max() <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_ones_values_rows_sum_to_one(lf, dtype):
+    B, H, S, W, G = 2, 2, 1024, 256, 9
+    inp = workloads.random_attention_inputs(5, B, H, S, W, G, dtype, std=1.0,
+                                            pad_frac=(0.1, 0.2))
+    inp["v"] = torch.ones_like(inp["v"])
+    inp["vg"] = torch.ones_like(inp["vg"])
+    got = _run(lf, _gpu(inp), W, G).cpu().double()
+    live = inp["local_mask"] == 1
+    for b in range(B):
+        assert torch.all(got[b][:, live[b]] == 1.0)
+        assert torch.all(got[b][:, ~live[b]] == 0.0)
+
+
+def test_deterministic_and_guard_bands_untouched(lf):
+    B, H, S, W, G = 1, 4, 2048, 512, 8
+    inp = workloads.random_attention_inputs(9, B, H, S, W, G, "fp16", pad_frac=(0.1, 0.2))
+    g = _gpu(inp)
+    n = B * H * S * 64
+    guard = 4096
+    buf = torch.full((n + 2 * guard,), float("nan"), dtype=torch.float16, device="cuda")
+    out = buf[guard:guard + n].view(B, H, S, 64)
+    _run(lf, g, W, G, out=out)
+    first = out.clone()
+    _run(lf, g, W, G, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int16), out.view(torch.int16))
+    assert torch.isnan(buf[:guard]).all() and torch.isnan(buf[guard + n:]).all()
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16", "fp32"])
+def test_preprocessed_entry_point_matches(lf, dtype):
+    B, H, S, W, G = 2, 3, 1024, 256, 20
+    inp = workloads.random_attention_inputs(11, B, H, S, W, G, dtype, pad_frac=(0.1, 0.2))
+    g = _gpu(inp)
+    a = _run(lf, g, W, G)
+    idx, cnt = lf.init_global_idx(g["global_mask"])
+    bias = lf.mask_shift(g["local_mask"])
+    b = lf.attn_forward_pre(g["q"], g["k"], g["v"], g["qg"], g["kg"], g["vg"], idx, cnt, bias,
+                            W, G)
+    torch.cuda.synchronize()
+    assert torch.equal(a.cpu().float(), b.cpu().float())
+
+
+def test_check_masks_detects_violations(lf):
+    S, G = 256, 4
+    lm = torch.ones(2, S, dtype=torch.float16, device="cuda")
+    gm = torch.full((2, S), -10000.0, dtype=torch.float16, device="cuda")
+    gm[:, :G] = 0
+    lf.check_masks(lm, gm, G)                       # valid
+    bad = gm.clone()
+    bad[1, 10] = 0                                  # non-leading global
+    with pytest.raises(lf.LFError, match="contiguous"):
+        lf.check_masks(lm, bad, G)
+    with pytest.raises(lf.LFError, match="more than G"):
+        lf.check_masks(lm, gm, G - 1)
+    bad_l = lm.clone()
+    bad_l[0, 3] = 0.5
+    with pytest.raises(lf.LFError, match="neither 0 nor 1"):
+        lf.check_masks(bad_l, gm, G)
+    bad_g = gm.clone()
+    bad_g[0, 100] = -5.0
+    with pytest.raises(lf.LFError, match="neither 0 nor -10000"):
+        lf.check_masks(lm, bad_g, G)
+
+
+# ---------------------------------------------------------------- full-size workloads
+def _sample_rows(wl, lm, rng, n_random=48):
+    rows = set()
+    live = (lm == 1).numpy()
+    for b in range(wl.B):
+        n_live = int(live[b].sum())
+        cand = list(range(min(wl.G + 2, wl.S)))                         # globals + first locals
+        cand += [wl.S - 1, wl.S - 2, n_live - 1, n_live, min(n_live + 1, wl.S - 1)]
+        cand += [127, 128, 255, 256, wl.W // 2, wl.W // 2 + wl.G, wl.W, wl.S // 2]
+        for s in cand:
+            if 0 <= s < wl.S:
+                rows.add((b, int(rng.integers(wl.H)), int(s)))
+        for _ in range(n_random):
+            rows.add((b, int(rng.integers(wl.H)), int(rng.integers(wl.S))))
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("wl", workloads.ATTN_WORKLOADS[1:], ids=lambda w: w.name)
+def test_full_workload_sampled_rows(lf, wl):
+    inp = workloads.make_attention_inputs(wl)
+    g = _gpu(inp)
+    out = _run(lf, g, wl.W, wl.G)
+    out2 = _run(lf, g, wl.W, wl.G)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16)), "not deterministic"
+    assert torch.isfinite(out).all()
+    got = out.cpu()
+    _check_padded_zero(got, inp["local_mask"])
+    rng = np.random.default_rng(wl.seed + 1)
+    rows = _sample_rows(wl, inp["local_mask"], rng)
+    ref = _oracle(inp, wl.W, wl.G, rows=rows)
+    g_rows = np.stack([got[b, h, s].double().numpy() for (b, h, s) in rows])
+    err = np.abs(g_rows - ref).max()
+    assert err <= TOL[wl.dtype], f"{wl.name}: max abs err {err:.3e} over {len(rows)} rows"
