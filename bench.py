@@ -1,0 +1,191 @@
+#!/usr/bin/env python3
+"""Benchmark of Longformer band + global attention on one MI355X.
+
+Workload: the longformer-large-shaped problem (B=1, H=16 heads x 64, S=4096,
+window W=512 i.e. +-256, G=8 leading global tokens, fp16), seeded synthetic
+inputs already resident in HBM.  One step = one lf_attn_forward call: global
+index extraction, mask shift, band + global attention (every step of the path).
+
+Prints ONE JSON line on stdout.  `value` is effective TFLOP/s = algorithmic flops
+(256 per allowed (query, key) pair) / wall time per step.  `roofline` reports the
+dominant kernel (the band + global-row launch) timed by HIP events recorded on its
+own stream around each launch inside the timed region.  `cpu_baseline` times the
+float64 oracle on a bounded sample of the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "band+global attention ms and TFLOP/s (% MFMA peak), B=1 H=16 S=4096 W=512 fp16"
+PEAK_FP16_TFLOPS = 2516.6        # MI355X dense fp16 MFMA: 256 CU x 4 SIMD x 1024 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["sparse_long_sequence_amd/csrc/attn_mfma.hip",
+                  "sparse_long_sequence_amd/csrc/lf_device.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_mfma_longformer_large_fp16_traffic.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def pairs_per_head(S: int, W: int, G: int) -> int:
+    """Allowed (query, key) pairs of one unpadded head with G leading global tokens."""
+    return G * S + (S - G) * (W + 1 + G) - (W // 2) * (W // 2 + 1)
+
+
+def row_pairs(s: int, S: int, W: int, G: int) -> int:
+    if s < G:
+        return S
+    lo, hi = max(G, s - W // 2), min(S - 1, s + W // 2)
+    return G + (hi - lo + 1)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic():
+    """Per-launch HBM bytes of the dominant kernel from the committed counter summary,
+    or None when it is absent or was taken on different kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    txt = open(TRAFFIC_FILE).read()
+    m_src = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", txt)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not (m_src and m_b) or m_src.group(1) != kernel_source_hash():
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(inp, wl, budget_s: float):
+    """Time the float64 oracle (single-threaded) on rows of the workload until the
+    budget is spent; returns throughput in the metric's unit (TFLOP/s)."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    rows, flops, t_total = 0, 0.0, 0.0
+    with threadpool_limits(limits=1):
+        h = 0
+        while t_total < budget_s and h < wl.H:
+            for s0 in range(0, wl.S, 256):
+                rr = [(0, h, s) for s in range(s0, min(wl.S, s0 + 256))]
+                t0 = time.perf_counter()
+                oracle.attention(inp["q"], inp["k"], inp["v"], inp["qg"], inp["kg"], inp["vg"],
+                                 inp["local_mask"], inp["global_mask"], wl.W, wl.G, rows=rr)
+                t_total += time.perf_counter() - t0
+                rows += len(rr)
+                flops += 256.0 * sum(row_pairs(s, wl.S, wl.W, wl.G) for (_, _, s) in rr)
+                if t_total >= budget_s:
+                    break
+            h += 1
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows} query rows of heads 0..{h - 1} (batch 0) of the same workload, "
+                      f"{t_total:.1f} s of float64 numpy oracle time, BLAS limited to 1 thread",
+            "seconds": round(t_total, 2), "host_cpus": os.cpu_count()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="budget of the oracle CPU baseline (0 = skip)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(--gpus {args.gpus} requested). Attention heads shard across GPUs with no "
+              f"communication; see the design notes.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_long_sequence_amd as lf
+    import workloads
+
+    wl = workloads.LARGE_FP16
+    inp = workloads.make_attention_inputs(wl)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = {n: t.to(dev) for n, t in inp.items()}
+    out = torch.empty_like(g["q"])
+
+    def step():
+        lf.attn_forward(g["q"], g["k"], g["v"], g["qg"], g["kg"], g["vg"], g["local_mask"],
+                        g["global_mask"], wl.W, wl.G, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    lf.kernel_timing_start(args.steps)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    n_k, k_ms = lf.kernel_timing_stop()
+    ms = e0.elapsed_time(e1) / args.steps
+    k_avg_ms = k_ms / max(n_k, 1)
+
+    flops = 256.0 * pairs_per_head(wl.S, wl.W, wl.G) * wl.B * wl.H
+    tflops = flops / (ms * 1e-3) / 1e12
+    k_tflops = flops / (k_avg_ms * 1e-3) / 1e12
+    alg_bytes = 2 * (6 * wl.B * wl.H * wl.S * 64 + wl.B * wl.H * wl.G * 64 + 2 * wl.B * wl.S)
+    log(f"step {ms * 1e3:.2f} us, main kernel {k_avg_ms * 1e3:.2f} us over {n_k} launches, "
+        f"{tflops:.1f} TFLOP/s step, {k_tflops:.1f} TFLOP/s kernel, "
+        f"{alg_bytes / (k_avg_ms * 1e-3) / 1e9:.0f} GB/s algorithmic")
+
+    traffic = stored_traffic()
+    res = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "S": wl.S, "W": wl.W, "G": wl.G,
+                   "head_dim": 64},
+        "pct_mfma_peak": round(100.0 * tflops / PEAK_FP16_TFLOPS, 3),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(k_tflops, 3),
+            "peak": PEAK_FP16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(k_tflops / PEAK_FP16_TFLOPS, 5),
+            "traffic": traffic,
+            "kernel": "attn_mfma_kernel (band tiles + global-row splits)",
+            "kernel_avg_us": round(k_avg_ms * 1e3, 3),
+            "algorithmic_flops_per_launch": flops,
+            "algorithmic_bytes_per_launch": alg_bytes,
+        },
+    }
+    if not args.no_cpu_baseline and args.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

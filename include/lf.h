@@ -158,6 +158,18 @@ int lf_encoder_layer(int dtype, const lf_layer_weights* w, const void* x,
                      int hidden, int H, int ffn, int W, int G, float attn_scale,
                      float ln_eps, void* y, void* workspace, size_t ws_bytes, void* stream);
 
+/*
+ * Measurement hook.  After lf_kernel_timing_start(capacity), each of the next
+ * `capacity` lf_attn_forward / lf_attn_forward_pre calls made on this thread
+ * records a HIP event pair on its own stream immediately around its main
+ * attention kernel (the band + global-row launch).  lf_kernel_timing_stop waits
+ * for the recorded events, returns the number of timed launches and their summed
+ * duration in milliseconds, releases the events and ends the recording.
+ * capacity must be in 1 .. 1000000.
+ */
+int lf_kernel_timing_start(int capacity);
+int lf_kernel_timing_stop(int* launches, double* total_ms);
+
 /* Static text for a status code. */
 const char* lf_status_string(int status);
 

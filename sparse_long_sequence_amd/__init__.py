@@ -17,6 +17,7 @@ import torch
 __all__ = ["LFError", "library_path", "load_library", "init_global_idx", "mask_shift",
            "attn_forward", "attn_forward_pre", "attn_workspace_bytes", "check_masks",
            "encoder_layer", "encoder_layer_workspace_bytes", "LAYER_WEIGHT_FIELDS",
+           "kernel_timing_start", "kernel_timing_stop",
            "EXPORTED_SYMBOLS", "dtype_code"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -32,6 +33,7 @@ LAYER_WEIGHT_FIELDS = ["w_proj", "b_proj", "w_qg", "b_qg", "w_o", "b_o", "ln1_g"
 EXPORTED_SYMBOLS = ["lf_init_global_idx", "lf_mask_shift", "lf_attn_forward",
                     "lf_attn_workspace_bytes", "lf_attn_forward_pre", "lf_check_masks",
                     "lf_encoder_layer_workspace_bytes", "lf_encoder_layer",
+                    "lf_kernel_timing_start", "lf_kernel_timing_stop",
                     "lf_status_string", "lf_last_error"]
 
 
@@ -70,12 +72,16 @@ def load_library():
     lib.lf_encoder_layer_workspace_bytes.restype = S
     lib.lf_encoder_layer.argtypes = [I, ctypes.POINTER(_LayerWeights), P, P, P, I, I, I, I, I,
                                      I, I, ctypes.c_float, ctypes.c_float, P, P, S, P]
+    lib.lf_kernel_timing_start.argtypes = [I]
+    lib.lf_kernel_timing_stop.argtypes = [ctypes.POINTER(ctypes.c_int),
+                                          ctypes.POINTER(ctypes.c_double)]
     lib.lf_status_string.argtypes = [I]
     lib.lf_status_string.restype = ctypes.c_char_p
     lib.lf_last_error.argtypes = []
     lib.lf_last_error.restype = ctypes.c_char_p
     for name in ("lf_init_global_idx", "lf_mask_shift", "lf_attn_forward",
-                 "lf_attn_forward_pre", "lf_check_masks", "lf_encoder_layer"):
+                 "lf_attn_forward_pre", "lf_check_masks", "lf_encoder_layer",
+                 "lf_kernel_timing_start", "lf_kernel_timing_stop"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -192,6 +198,19 @@ def attn_forward_pre(q, k, v, qg, kg, vg, global_idx, global_count, local_bias, 
                                    _ptr(local_bias), B, H, S, W, G, _ptr(out), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _stream(dev)))
     return out
+
+
+def kernel_timing_start(capacity: int):
+    """Record HIP events around the main attention kernel of the next `capacity` calls."""
+    _check(load_library().lf_kernel_timing_start(capacity))
+
+
+def kernel_timing_stop():
+    """-> (launches, total_ms) of the main attention kernel since kernel_timing_start."""
+    n = ctypes.c_int(0)
+    ms = ctypes.c_double(0.0)
+    _check(load_library().lf_kernel_timing_stop(ctypes.byref(n), ctypes.byref(ms)))
+    return n.value, ms.value
 
 
 def check_masks(local_mask, global_mask, G: int):

@@ -554,6 +554,10 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
   const int64_t n_global = a.G > 0 ? (int64_t)a.B * a.H * a.n_split * n_qgroups : 0;
   const int64_t grid = n_band + n_global;
   if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (a.ev_begin) {
+    hipError_t e0 = hipEventRecord(a.ev_begin, st);
+    if (e0 != hipSuccess) return e0;
+  }
   if (nqb == 1)
     attn_mfma_kernel<T, 1><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles, (int)n_global,
                                                                 n_qgroups);
@@ -562,6 +566,10 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
                                                                 n_qgroups);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (a.ev_end) {
+    e = hipEventRecord(a.ev_end, st);
+    if (e != hipSuccess) return e;
+  }
   if (a.G > 0) {
     global_combine_kernel<T><<<a.B * a.H, 256, 0, st>>>(a);
     e = hipGetLastError();

@@ -145,19 +145,23 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a, int n_local_t
 
 }  // namespace
 
-hipError_t launch_attention_valu_t(const AttnArgs& a, hipStream_t st, int dtype);
-
 hipError_t launch_attention_fp32(const AttnArgs& a, hipStream_t st) {
   const int n_local = (a.S + kRows - 1) / kRows;
   const int n_global = (a.G + kRows - 1) / kRows;
   const int64_t grid = (int64_t)a.B * a.H * (n_local + n_global);
+  if (a.ev_begin) {
+    hipError_t e0 = hipEventRecord(a.ev_begin, st);
+    if (e0 != hipSuccess) return e0;
+  }
   switch (a.dtype) {
     case 0: attn_valu_kernel<float><<<(unsigned)grid, 64, 0, st>>>(a, n_local, n_global); break;
     case 1: attn_valu_kernel<f16><<<(unsigned)grid, 64, 0, st>>>(a, n_local, n_global); break;
     case 2: attn_valu_kernel<bf16><<<(unsigned)grid, 64, 0, st>>>(a, n_local, n_global); break;
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && a.ev_end) e = hipEventRecord(a.ev_end, st);
+  return e;
 }
 
 }  // namespace lf

@@ -11,6 +11,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "../../include/lf.h"
 #include "lf_internal.h"
@@ -18,6 +19,21 @@
 namespace {
 
 thread_local std::string g_last_error;
+
+// Kernel timing hook state (per thread).
+struct Timing {
+  bool on = false;
+  int cap = 0;
+  int used = 0;
+  std::vector<hipEvent_t> begin, end;
+};
+thread_local Timing g_timing;
+
+void timing_release() {
+  for (hipEvent_t e : g_timing.begin) hipEventDestroy(e);
+  for (hipEvent_t e : g_timing.end) hipEventDestroy(e);
+  g_timing = Timing();
+}
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -108,6 +124,13 @@ lf::AttnArgs make_args(int dtype, const void* q, const void* k, const void* v, c
   a.partials = partials;
   a.n_split = ws.n_split;
   a.split_len = ws.split_len;
+  a.ev_begin = nullptr;
+  a.ev_end = nullptr;
+  if (g_timing.on && g_timing.used < g_timing.cap) {
+    a.ev_begin = g_timing.begin[g_timing.used];
+    a.ev_end = g_timing.end[g_timing.used];
+    ++g_timing.used;
+  }
   return a;
 }
 
@@ -260,6 +283,45 @@ int lf_attn_forward(int dtype, const void* q, const void* k, const void* v, cons
   hipError_t he2 = hipFreeAsync(scratch, st);
   if (he != hipSuccess) return hip_fail(he, "lf_attn_forward");
   if (he2 != hipSuccess) return hip_fail(he2, "lf_attn_forward free");
+  return ok();
+}
+
+int lf_kernel_timing_start(int capacity) {
+  if (capacity < 1 || capacity > 1000000)
+    return fail(LF_ERR_INVALID_ARGUMENT, "timing capacity must be in 1..1000000");
+  timing_release();
+  g_timing.begin.resize(capacity, nullptr);
+  g_timing.end.resize(capacity, nullptr);
+  for (int i = 0; i < capacity; ++i) {
+    hipError_t e = hipEventCreate(&g_timing.begin[i]);
+    if (e == hipSuccess) e = hipEventCreate(&g_timing.end[i]);
+    if (e != hipSuccess) {
+      timing_release();
+      return hip_fail(e, "lf_kernel_timing_start");
+    }
+  }
+  g_timing.cap = capacity;
+  g_timing.on = true;
+  return ok();
+}
+
+int lf_kernel_timing_stop(int* launches, double* total_ms) {
+  if (!launches || !total_ms) return fail(LF_ERR_INVALID_ARGUMENT, "null output pointer");
+  double sum = 0.0;
+  const int n = g_timing.used;
+  for (int i = 0; i < n; ++i) {
+    hipError_t e = hipEventSynchronize(g_timing.end[i]);
+    float ms = 0.0f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, g_timing.begin[i], g_timing.end[i]);
+    if (e != hipSuccess) {
+      timing_release();
+      return hip_fail(e, "lf_kernel_timing_stop");
+    }
+    sum += ms;
+  }
+  timing_release();
+  *launches = n;
+  *total_ms = sum;
   return ok();
 }
 

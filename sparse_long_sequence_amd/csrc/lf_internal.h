@@ -23,6 +23,8 @@ struct AttnArgs {
   float* partials;        // global-row partial states (see attn_workspace_layout)
   int n_split;            // key splits of the global rows
   int split_len;          // keys per split (multiple of 64)
+  hipEvent_t ev_begin;    // if non-null: recorded right before / after the main kernel
+  hipEvent_t ev_end;
 };
 
 // Global-row partial states: [B*H][n_split][G][66] fp32 = (m, l, o[64]).

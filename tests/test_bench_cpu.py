@@ -1,0 +1,28 @@
+"""bench.py's algorithmic work accounting agrees with the oracle's pair count."""
+import numpy as np
+import pytest
+
+import bench
+import oracle
+
+
+@pytest.mark.parametrize("S,W,G", [(4096, 512, 8), (64, 16, 2), (16384, 512, 64), (1024, 128, 0)])
+def test_pair_counts_match_oracle(S, W, G):
+    lm = np.ones((1, S))
+    gm = np.full((1, S), -10000.0)
+    gm[0, :G] = 0.0
+    assert bench.pairs_per_head(S, W, G) == oracle.allowed_pairs(lm, gm, W, G)
+    assert sum(bench.row_pairs(s, S, W, G) for s in range(S)) == bench.pairs_per_head(S, W, G)
+
+
+def test_multi_gpu_request_exits_with_message(capsys):
+    import sys
+    argv = sys.argv
+    sys.argv = ["bench.py", "--gpus", "4"]
+    try:
+        with pytest.raises(SystemExit) as e:
+            bench.main()
+        assert e.value.code == 2
+    finally:
+        sys.argv = argv
+    assert "one GPU" in capsys.readouterr().err
