@@ -24,8 +24,8 @@
  *  - Shape rules are checked on the host before anything is enqueued: B, H, S >= 1;
  *    W even and >= 2; S % W == 0 and S >= 2W ([FT-LF] hard constraint 1);
  *    0 <= G <= W ([FT-LF] hard constraint 3, in the inclusive form the page says
- *    the code checks); B*H*S <= 2^31 - 1; pointers non-NULL (qg may be NULL when
- *    G == 0).  On a violation nothing is enqueued, outputs are untouched, the call
+ *    the code checks); B*H*S <= 2^31 - 1; S < 2^24 for fp16 / bf16; pointers
+ *    non-NULL (qg may be NULL when G == 0).  On a violation nothing is enqueued, outputs are untouched, the call
  *    returns LF_ERR_INVALID_ARGUMENT and lf_last_error() names the rule.
  *  - Data-dependent preconditions are NOT checked on the fast path (the result is
  *    unspecified when they are violated): global tokens sit contiguously at the
@@ -103,9 +103,12 @@ size_t lf_attn_workspace_bytes(int dtype, int B, int H, int S, int W, int G);
 /*
  * Same computation as lf_attn_forward on already-preprocessed masks: global_idx /
  * global_count from lf_init_global_idx and local_bias from lf_mask_shift.  It
- * allocates nothing: `workspace` (device, 256-byte aligned, ws_bytes >=
- * lf_attn_workspace_bytes) holds the partial results of the global rows; its
- * contents on entry do not matter.  Calls that share a workspace must not overlap.
+ * allocates nothing and is one kernel launch.  `workspace` (device, 256-byte
+ * aligned, ws_bytes >= lf_attn_workspace_bytes) starts with B*H int32 split
+ * tickets followed by the partial results of the global rows.  The tickets must be
+ * zero before the first call that uses the workspace (zero-fill it once after
+ * allocating it); every call leaves them zero again, the rest of the workspace may
+ * hold anything.  Calls that share a workspace must not overlap in time.
  */
 int lf_attn_forward_pre(int dtype, const void* q, const void* k, const void* v,
                         const void* qg, const void* kg, const void* vg,

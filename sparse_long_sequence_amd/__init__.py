@@ -191,7 +191,8 @@ def attn_forward_pre(q, k, v, qg, kg, vg, global_idx, global_count, local_bias, 
         out = torch.empty_like(q)
     nbytes = attn_workspace_bytes(q.dtype, B, H, S, W, G)
     if workspace is None:
-        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        # the leading split tickets must start at zero; the library leaves them zero
+        workspace = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
     _dev(out, workspace)
     _check(lib.lf_attn_forward_pre(dtype_code(q.dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(qg),
                                    _ptr(kg), _ptr(vg), _ptr(global_idx), _ptr(global_count),
@@ -239,7 +240,8 @@ def encoder_layer(x, weights: dict, local_mask, global_mask, H: int, W: int, G: 
         out = torch.empty_like(x)
     nbytes = encoder_layer_workspace_bytes(x.dtype, B, S, D, H, F, W, G)
     if workspace is None:
-        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        # the leading split tickets must start at zero; the library leaves them zero
+        workspace = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
     _dev(out, workspace)
     lw = _LayerWeights(*[t.data_ptr() for t in ws])
     _check(lib.lf_encoder_layer(dtype_code(x.dtype), ctypes.byref(lw), _ptr(x), _ptr(local_mask),

@@ -1,4 +1,4 @@
-// fp16 / bf16 band + global attention on the gfx950 matrix cores.
+// fp16 / bf16 band + global attention on the gfx950 matrix cores, one launch.
 //
 // [FT-LF] = the page "FasterTransformer Longformer 推理加速实践：PyTorch 集成、输入约束与
 // 端到端性能解析", section "Longformer Encoder 计算流程":
@@ -6,29 +6,43 @@
 //   per-layer step 4  one masked softmax: a local token normalises over its window
 //                     and the global tokens, a global token over the whole
 //                     sequence, padded rows are zeroed;
-//   preprocessing 2   the shifted local mask is an additive score bias.
-// The page's own design (three window-GEMM segments with score buffers, then a
-// separate softmax kernel) is not followed: here scores never leave registers.
+//   preprocessing 1/2 the global-token count and positions, and the local-mask
+//                     shift that turns padding into an excluded key.
+// The page's design (three window-GEMM segments writing score buffers, a separate
+// softmax kernel, a separate global-row pass, preprocessing kernels in front) is
+// not followed: scores never leave registers and one launch does everything.  In
+// "raw" mode the kernel reads the two masks itself (the count of leading global
+// tokens and the live-key test are evaluated where they are used); in "pre" mode
+// it reads global_count / the shifted mask produced by the preprocessing entry
+// points.
 //
-// Work split (one launch, two kinds of 256-thread workgroups):
-//  * band workgroup = 128 query rows of one (b, h), 32 per wave.  Keys stream
-//    through LDS in 64-row chunks, double-buffered: first the global keys
-//    (gathered through global_idx), then the band [max(n_b, t0-W/2),
-//    min(S-1, t0+127+W/2)].  K is kept row-major, V is written transposed so
-//    both MFMA operands read contiguous 8-element fragments.
-//  * global workgroup = one key split of one (b, h) for up to 64 global rows;
-//    each wave streams its own 64-key chunks (K straight from memory into MFMA
-//    fragments, V through a per-wave transposed LDS tile), the four wave states
-//    are merged in LDS and one partial (m, l, o[64]) per row goes to the
-//    workspace; a small combine kernel merges the splits.
+// Band workgroup: 4 waves = 128 query rows of one (b, h); wave w owns rows
+// r0 + 32w .. r0 + 32w + 31.  Keys move in blocks of 32 rows (K row-major, V
+// transposed, plus a per-key 0 / -inf validity term) through a 5-slot LDS ring.
+// The key list of a workgroup is
+//     [ceil(G/32) global-key blocks][band blocks 0 .. nband+2]
+// where band block j holds keys r0 - W/2 + 32j ..; wave w needs band blocks
+// w .. w + nband - 1 (nband = (W + 63) / 32).  At step t every wave reads entry t
+// (global phase) or t + w (band phase: the waves walk the band on a diagonal, so
+// none of them idles); entry t + 4 is written into the ring from registers and the
+// loads of entry t + 4 + kDepth are issued (kDepth register sets in flight: memory
+// latency is ~1-2 us against ~0.2 us of work per step).  One barrier per step.
 //
-// Per chunk and wave: S^T = K Q^T (8 x v_mfma_f32_32x32x16), so each lane holds
-// 32 scores of ONE query; row max = in-lane max + one lane^32 exchange; the
-// online-softmax state (m in log2 units, l, O^T) is per lane; the running max is
-// only moved when it grows by more than 8 (p <= 2^8 then, exact in fp16/bf16 range),
-// so rescaling the 32 O^T accumulators is rare; P is rounded to the input type and
-// its row sum is taken from the rounded values (v_dot2), then O^T += V^T P^T
-// (8 more MFMAs).
+// Per block and wave: S^T = K Q^T (4 x v_mfma_f32_32x32x16), so each lane holds
+// 16 scores of ONE query (lanes n and n + 32 share a query); the running max is
+// kept in scaled log2 units and only moved when it grows by more than 8 (then
+// p <= 2^8, exact range for fp16 / bf16), so rescaling the accumulators is rare;
+// P is rounded to the input type, its row sum is taken from the rounded values
+// (v_dot2), then O^T += V^T P^T (4 more MFMAs).
+//
+// Global rows (r < n_b) attend to all live keys through kg / vg.  The first
+// n_split tiles of each (b, h) also take one key split of those rows (split_len
+// keys, 32 per wave per round) before their band work: the four wave states are
+// merged in LDS and one partial (m, l, o[64]) per row is published with
+// agent-scope atomic stores (coherent across XCDs without cache maintenance);
+// after them the workgroup takes an atomic ticket, and the one that completes the
+// (b, h) reads all partials with agent-scope atomic loads, writes the global rows
+// and resets the ticket.
 #include "lf_device.h"
 #include "lf_internal.h"
 
@@ -36,559 +50,668 @@ namespace lf {
 
 namespace {
 
-constexpr int kChunk = 64;
-constexpr int kKld = 72;   // LDS row pitch of K (elements): 144 B, conflict-free 16 B reads
-constexpr int kVld = 68;   // LDS row pitch of V^T (elements): 136 B, conflict-free 8 B reads
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kNegBig = -1.0e30f;   // running-max start: finite, so exp2 never sees inf-inf
-constexpr float kLazy = 8.0f;         // rescale only when the max grows by more than 2^8
-constexpr int kThreads = 256;
 constexpr int kWaves = 4;
-constexpr int kTileRows = 32 * kWaves;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTile = 32 * kWaves;   // query rows per workgroup
+constexpr int kBlk = 32;             // keys per block
+constexpr int kKld = 72;             // LDS row pitch of K (elements): 144 B, conflict-free reads
+constexpr int kVld = 36;             // LDS row pitch of V^T (elements): 72 B, conflict-free reads
+constexpr int kRing = 6;             // LDS block slots
+constexpr int kAhead = kWaves + 1;   // entry t + kAhead is written at step t
+constexpr int kDepth = 4;            // register sets of loads in flight
+constexpr int kStPitch = 67;         // floats per row of a wave state in LDS: m, l, o[64], pad
+constexpr int kCombinePairs = 4096;  // (row, split) pairs per combine chunk (2 x 16 KB of LDS)
+constexpr int kMaxSplit = 32;        // at most this many key splits per (b, h)
+constexpr int kSc1 = 16;             // cache-policy bit of coherent (write-through / bypass) access
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegBig = -1.0e30f;  // running-max start: finite, so exp2 never sees inf-inf
+constexpr float kLazy = 8.0f;        // move the max only when it grows by more than 2^8
 
 template <typename T>
-struct ChunkBuf {
-  T k[kChunk * kKld];
-  T vt[64 * kVld];
-  float bias2[kChunk];   // key bias * log2(e); -inf for empty slots
-  int flag;              // nonzero: some slot has a nonzero bias
+struct Slot {
+  T k[kBlk * kKld];     // K rows of the block
+  T vt[64 * kVld];      // V^T: row d holds the 32 keys of the block
+  float bias2[kBlk];    // 0 for a live key, -inf for an empty / excluded / padded slot
+  int flag;             // 0: every key live, 1: some, 2: none
   int pad[3];
 };
 
-template <typename T>
-struct WaveBuf {
-  T vt[64 * kVld];
-  float bias2[kChunk];
-};
-
-// ---------------------------------------------------------------- staging (band)
-template <typename T>
-struct StageRegs {
-  u32x4 k0, k1, v0, v1;
-  float bias2;
-};
-
-// Thread t stages rows 2*(t/8) and 2*(t/8)+1, columns 8*(t%8)..+7, of the chunk;
-// threads 0..63 also stage the key bias of slot t.
-template <typename T>
-__device__ inline void stage_load(StageRegs<T>& r, const T* __restrict__ kh,
-                                  const T* __restrict__ vh, const T* __restrict__ bias_row,
-                                  const int32_t* __restrict__ gidx, bool gather, int first,
-                                  int count, int S) {
-  const int t = threadIdx.x;
-  const int rp = t >> 3, col = t & 7;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int slot = 2 * rp + e;
-    int key = -1;
-    if (slot < count) key = gather ? gidx[first + slot] : first + slot;
-    const bool ok = key >= 0 && key < S;
-    u32x4 kk = zero, vv = zero;
-    if (ok) {
-      kk = *(const u32x4*)(kh + (size_t)key * 64 + col * 8);
-      vv = *(const u32x4*)(vh + (size_t)key * 64 + col * 8);
-    }
-    if (e == 0) { r.k0 = kk; r.v0 = vv; } else { r.k1 = kk; r.v1 = vv; }
-  }
-  if (t < kChunk) {
-    int key = -1;
-    if (t < count) key = gather ? gidx[first + t] : first + t;
-    r.bias2 = (key >= 0 && key < S) ? Elem<T>::to_f(bias_row[key]) * kLog2e : -INFINITY;
-  }
-}
+static_assert(32 * kStPitch * 4 <= sizeof(Slot<_Float16>), "a wave state fits in one slot");
+static_assert(2 * kCombinePairs * 4 <= kRing * sizeof(Slot<_Float16>), "combine buffers fit the ring");
 
 template <typename T>
-__device__ inline void stage_store(ChunkBuf<T>& buf, const StageRegs<T>& r) {
-  const int t = threadIdx.x;
-  const int rp = t >> 3, col = t & 7;
-  *(u32x4*)&buf.k[(2 * rp) * kKld + col * 8] = r.k0;
-  *(u32x4*)&buf.k[(2 * rp + 1) * kKld + col * 8] = r.k1;
-  // transpose: element e of rows (2rp, 2rp+1) -> V^T[8col+e][2rp..2rp+1] as one dword
-  const uint32_t* a = (const uint32_t*)&r.v0;
-  const uint32_t* b = (const uint32_t*)&r.v1;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t lo = (a[w] & 0xffffu) | (b[w] << 16);
-    const uint32_t hi = (a[w] >> 16) | (b[w] & 0xffff0000u);
-    *(uint32_t*)&buf.vt[(col * 8 + 2 * w) * kVld + 2 * rp] = lo;
-    *(uint32_t*)&buf.vt[(col * 8 + 2 * w + 1) * kVld + 2 * rp] = hi;
-  }
-  if (t < kChunk) {
-    buf.bias2[t] = r.bias2;
-    const uint64_t any = __ballot(r.bias2 != 0.0f);
-    if (t == 0) buf.flag = any != 0ull;
-  }
-}
-
-// ---------------------------------------------------------------- per-wave math
-template <typename T>
-struct Frags {
+struct Frag {
   typedef typename Elem<T>::vec8 v8;
   typedef typename Elem<T>::vec4 v4;
   typedef typename Elem<T>::vec2 v2;
 };
 
-// Scores -> probabilities for one chunk, update of the lane's online-softmax state,
-// and the P^T operand fragments for the PV product.
-template <typename T, bool MASK, bool BIAS>
-__device__ inline void softmax_chunk(f32x16& s0, f32x16& s1, const float* __restrict__ bias2,
-                                     int key0, int srow, int half, int S, float c2,
-                                     float& m_run, float& l_run, f32x16* o, int n_o,
-                                     typename Frags<T>::v8 pf[4]) {
-  const int g = lane_id() >> 5;
-  float x[32];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    x[v] = s0[v] * c2;
-    x[16 + v] = s1[v] * c2;
+// ------------------------------------------------------------------ staging
+// Loads go through buffer resources sized to one head: a key outside [0, S) is an
+// out-of-range offset and reads zeros, so staging has no branches.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ inline rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ inline int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// A key with mask value x is live: raw local mask x == 1, shifted mask x == 0.
+template <bool RAW>
+__device__ inline bool mask_live(float x) {
+  return RAW ? x == 1.0f : x == 0.0f;
+}
+
+// Thread t stages K row t/8 (16 B at column 8*(t%8)), V rows 2*(t/16), 2*(t/16)+1
+// (8 B each at column 4*(t%16)) and, for t < 32, the mask value of key slot t.
+template <typename T>
+struct Stage {
+  u32x4 k;
+  u32x2 v0, v1;
+  unsigned short mask_bits;
+};
+
+// Block of keys base .. base + 31.  Every thread issues the same four loads (no
+// branch), so the compiler can keep later entries in flight while it waits for
+// this one.  K / V rows are loaded for every in-range key (a dead key's score is
+// masked to -inf, so its data never matters).
+template <typename T>
+__device__ inline void stage_load(Stage<T>& s, rsrc_t rk, rsrc_t rv, rsrc_t rm, int base) {
+  const int t = threadIdx.x;
+  const int koff = (t >> 3) * 128 + 16 * (t & 7);
+  const int voff = (t >> 4) * 256 + 8 * (t & 15);
+  const int b128 = base * 128;
+  s.k = __builtin_amdgcn_raw_buffer_load_b128(rk, b128 + koff, 0, 0);
+  s.v0 = __builtin_amdgcn_raw_buffer_load_b64(rv, b128 + voff, 0, 0);
+  s.v1 = __builtin_amdgcn_raw_buffer_load_b64(rv, b128 + voff + 128, 0, 0);
+  s.mask_bits = __builtin_amdgcn_raw_buffer_load_b16(rm, t < kBlk ? 2 * (base + t) : -1, 0, 0);
+}
+
+// Write a staged block; key base + j is live iff lo <= key < hi and its mask says so.
+template <typename T, bool RAW>
+__device__ inline void stage_store(Slot<T>& sl, const Stage<T>& s, int base, int lo, int hi) {
+  const int t = threadIdx.x;
+  const int kr = t >> 3, kc = t & 7, vp = t >> 4, vc = t & 15;
+  *(u32x4*)&sl.k[kr * kKld + 8 * kc] = s.k;
+  uint32_t* vt = (uint32_t*)sl.vt;
+  constexpr int P = kVld / 2;   // pitch in dwords
+  // element i of keys (2vp, 2vp+1) -> V^T[4vc + i][2vp .. 2vp+1] as one dword
+  vt[(4 * vc + 0) * P + vp] = (s.v0[0] & 0xffffu) | (s.v1[0] << 16);
+  vt[(4 * vc + 1) * P + vp] = (s.v0[0] >> 16) | (s.v1[0] & 0xffff0000u);
+  vt[(4 * vc + 2) * P + vp] = (s.v0[1] & 0xffffu) | (s.v1[1] << 16);
+  vt[(4 * vc + 3) * P + vp] = (s.v0[1] >> 16) | (s.v1[1] & 0xffff0000u);
+  if (wave_id() == 0) {
+    const int lane = lane_id();
+    const int key = base + lane;
+    const bool live = lane < kBlk && key >= lo && key < hi &&
+                      mask_live<RAW>(Elem<T>::to_f(__builtin_bit_cast(T, s.mask_bits)));
+    const uint64_t bal = __ballot(live);
+    if (lane < kBlk) sl.bias2[lane] = live ? 0.0f : -INFINITY;
+    if (lane == 0) sl.flag = bal == 0xffffffffull ? 0 : (bal == 0ull ? 2 : 1);
   }
-  if (BIAS) {
+}
+
+// ------------------------------------------------------------------ per-wave math
+__device__ inline float cross_half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ inline float cross_half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <typename T>
+__device__ inline typename Frag<T>::v2 cvt_pair(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 x = {a, b};
+  return __builtin_convertvector(x, typename Frag<T>::v2);
+}
+
+// S^T of one 32-key block for the wave's 32 queries (4 MFMAs; the result is not
+// waited for here).
+template <typename T>
+__device__ inline f32x16 qk_block(const Slot<T>& sl, const typename Frag<T>::v8 qf[4]) {
+  typedef typename Frag<T>::v8 v8;
+  const int lane = lane_id();
+  const int n = lane & 31, g = lane >> 5;
+  f32x16 s = f32x16{};
 #pragma unroll
-    for (int q4 = 0; q4 < 8; ++q4) {
-      const int kl = (q4 >> 2) * 32 + (q4 & 3) * 8 + 4 * g;
-      const f32x4 bb = *(const f32x4*)&bias2[kl];
+  for (int t = 0; t < 4; ++t) {
+    const v8 a = *(const v8*)&sl.k[n * kKld + 16 * t + 8 * g];
+    s = mfma32(a, qf[t], s);
+  }
+  return s;
+}
+
+// Online-softmax update with the scores s of one block, then O^T += V^T P^T.
+// flag (uniform): 0 every key live, else add the per-key 0 / -inf term.
+// band (uniform): apply |j - s| <= W/2 with c = band_c + 8*(v/4) + (v%4) in 0..W.
+// Every block runs the same code on the accumulators (a block without a live key
+// adds exact zeros), so the only branch that touches them is the rare rescale.
+template <typename T>
+__device__ inline void softmax_pv(const Slot<T>& sl, const f32x16& s, int flag, f32x16 o[2],
+                                  float& m_run, float& l_run, float c2, bool band, int band_c,
+                                  int W) {
+  typedef typename Frag<T>::v8 v8;
+  typedef typename Frag<T>::v4 v4;
+  typedef typename Frag<T>::v2 v2;
+  const int lane = lane_id();
+  const int n = lane & 31, g = lane >> 5;
+  float x[16];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[4 * q4 + i] += bb[i];
+  for (int v = 0; v < 16; ++v) x[v] = s[v];
+  if (flag) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const f32x4 bb = *(const f32x4*)&sl.bias2[8 * jj + 4 * g];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[4 * jj + i] += bb[i];
     }
   }
-  if (MASK) {
+  if (band) {
 #pragma unroll
-    for (int e = 0; e < 32; ++e) {
-      const int kl = (e >> 4) * 32 + ((e & 15) >> 2) * 8 + 4 * g + (e & 3);
-      const int j = key0 + kl;
-      const bool ok = (j - srow <= half) && (srow - j <= half) && (j < S);
-      x[e] = ok ? x[e] : -INFINITY;
+    for (int v = 0; v < 16; ++v) {
+      const int c = band_c + 8 * (v >> 2) + (v & 3);
+      x[v] = (unsigned)c <= (unsigned)W ? x[v] : -INFINITY;
     }
   }
   float mx = x[0];
 #pragma unroll
-  for (int e = 1; e < 32; ++e) mx = fmaxf(mx, x[e]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-  const bool need = mx > m_run + kLazy;
-  if (__ballot(need)) {
-    const float m_new = need ? mx : m_run;
+  for (int v = 1; v < 16; ++v) mx = fmaxf(mx, x[v]);
+  mx = cross_half_max(mx);
+  const float ms = mx * c2;
+  const bool need = ms > m_run + kLazy;
+  if (__builtin_expect(__ballot(need) != 0ull, 0)) {
+    const float m_new = need ? ms : m_run;
     const float alpha = fast_exp2(m_run - m_new);
     l_run *= alpha;
-    for (int i = 0; i < n_o; ++i) o[i] *= alpha;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      o[0][v] *= alpha;
+      o[1][v] *= alpha;
+    }
     m_run = m_new;
   }
-  typedef typename Frags<T>::v2 v2;
+  v8 pf[2];
   float lsum = 0.0f;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
-    for (int i = 0; i < 8; i += 2) {
-      const int e = 16 * (s >> 1) + 8 * (s & 1) + i;
-      const T p0 = Elem<T>::from_f(fast_exp2(x[e] - m_run));
-      const T p1 = Elem<T>::from_f(fast_exp2(x[e + 1] - m_run));
-      pf[s][i] = p0;
-      pf[s][i + 1] = p1;
-      v2 pp = {p0, p1};
+    for (int e = 0; e < 8; e += 2) {
+      const float p0 = fast_exp2(fmaf(x[8 * h2 + e], c2, -m_run));
+      const float p1 = fast_exp2(fmaf(x[8 * h2 + e + 1], c2, -m_run));
+      const v2 pp = cvt_pair<T>(p0, p1);
+      pf[h2][e] = pp[0];
+      pf[h2][e + 1] = pp[1];
       lsum = dot2_ones(pp, lsum);
     }
   }
   l_run += lsum;
-}
-
-// O^T[mb] += V^T P^T over one chunk; V^T rows (d) in LDS with pitch kVld.
-template <typename T>
-__device__ inline void pv_chunk(const T* __restrict__ vt, const typename Frags<T>::v8 pf[4],
-                                f32x16 o[2]) {
-  typedef typename Frags<T>::v8 v8;
-  typedef typename Frags<T>::v4 v4;
-  const int n = lane_id() & 31, g = lane_id() >> 5;
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      const T* row = vt + (32 * mb + n) * kVld + 16 * s + 4 * g;
+      const T* row = sl.vt + (32 * mb + n) * kVld + 16 * h2 + 4 * g;
       const v4 lo = *(const v4*)row;
       const v4 hi = *(const v4*)(row + 8);
       const v8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      o[mb] = mfma32(va, pf[s], o[mb]);
+      o[mb] = mfma32(va, pf[h2], o[mb]);
     }
   }
 }
 
-// S^T for a chunk whose K rows sit in LDS (pitch kKld).
+// One whole block (used where there is nothing to overlap it with).
 template <typename T>
-__device__ inline void qk_chunk_lds(const T* __restrict__ k, const typename Frags<T>::v8 qf[4],
-                                    f32x16& s0, f32x16& s1) {
-  typedef typename Frags<T>::v8 v8;
-  const int n = lane_id() & 31, g = lane_id() >> 5;
-  s0 = f32x16{};
-  s1 = f32x16{};
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const v8 a0 = *(const v8*)&k[n * kKld + 16 * t + 8 * g];
-    const v8 a1 = *(const v8*)&k[(32 + n) * kKld + 16 * t + 8 * g];
-    s0 = mfma32(a0, qf[t], s0);
-    s1 = mfma32(a1, qf[t], s1);
-  }
+__device__ inline void block_step(const Slot<T>& sl, const typename Frag<T>::v8 qf[4],
+                                  f32x16 o[2], float& m_run, float& l_run, float c2, bool band,
+                                  int band_c, int W) {
+  const int flag = __builtin_amdgcn_readfirstlane(sl.flag);
+  const f32x16 s = qk_block<T>(sl, qf);
+  softmax_pv<T>(sl, s, flag, o, m_run, l_run, c2, band, band_c, W);
 }
 
 template <typename T>
-__device__ inline void store_rows(const AttnArgs& a, int b, int h, int srow, bool write,
-                                  bool live, const f32x16 o[2], float l_tot) {
-  if (!write) return;
+__device__ inline void load_q(typename Frag<T>::v8 qf[4], const T* __restrict__ rowp, bool ok) {
+  typedef typename Frag<T>::v8 v8;
   const int g = lane_id() >> 5;
-  T* dst = (T*)a.out + (size_t)b * a.out_sb + (size_t)h * a.out_sh + (size_t)srow * a.out_ss;
-  const float inv = live ? 1.0f / l_tot : 0.0f;
-  typedef typename Frags<T>::v4 v4;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v4 w;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = Elem<T>::from_f(live ? o[mb][4 * j + i] * inv : 0.0f);
-      *(v4*)(dst + 32 * mb + 8 * j + 4 * g) = w;
-    }
-  }
+  for (int t = 0; t < 4; ++t) qf[t] = ok ? *(const v8*)(rowp + 16 * t + 8 * g) : v8{};
 }
 
-// ---------------------------------------------------------------- band workgroup
+// ------------------------------------------------------------------ workgroup context
 template <typename T>
-__device__ void band_tile(const AttnArgs& a, int bh, int tile, ChunkBuf<T>* bufs) {
-  typedef typename Frags<T>::v8 v8;
-  const int lane = lane_id();
-  const int wave = threadIdx.x >> 6;
-  const int n = lane & 31, g = lane >> 5;
-  const int b = bh / a.H, h = bh % a.H;
-  const int S = a.S, half = a.W >> 1;
-  const int nb = a.gcnt[b];
-  const int t0 = tile * kTileRows;
-  const int tlo = max(t0, nb), thi = min(t0 + kTileRows - 1, S - 1);
-  if (tlo > thi) return;   // whole tile is global rows: written by the global path
-  const int row0 = t0 + 32 * wave;
-  const int srow = row0 + n;
-  const int r_lo = max(row0, nb), r_hi = min(row0 + 31, S - 1);
-  const bool wave_active = r_lo <= r_hi;
+struct Ctx {
+  int b, h, bh, tile, S, W, G, nb, ngb, r0, kbase, n_list;
+  int n_sp;                  // split entries after the list (4 if this tile carries one)
+  int sp_lo, sp_hi;          // key range of the split
+  const T *kh, *vh;          // k, v of this head
+  const T *kgh, *vgh;        // kg, vg of this head (split tiles; else k, v)
+  const T* mask;             // that mask row (raw local mask, or the shifted one)
+};
 
-  const size_t head = (size_t)bh * S * 64;
-  const T* qh = (const T*)a.q + head;
-  const T* kh = (const T*)a.k + head;
-  const T* vh = (const T*)a.v + head;
-  const T* bias_row = (const T*)a.bias + (size_t)b * S;
-  const int32_t* gidx = a.gidx + (size_t)b * S;
-
-  v8 qf[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    if (srow < S)
-      qf[t] = *(const v8*)(qh + (size_t)srow * 64 + 16 * t + 8 * g);
-    else
-      qf[t] = v8{};
-  }
-  const int n_g = (nb + kChunk - 1) / kChunk;
-  const int lo = max(nb, tlo - half), hi = min(S - 1, thi + half);
-  const int n_b = (hi - lo + kChunk) / kChunk;
-  const int total = n_g + n_b;
-  const float c2 = a.scale * kLog2e;
-
-  f32x16 o[2] = {f32x16{}, f32x16{}};
-  float m_run = kNegBig, l_run = 0.0f;
-
-  auto chunk_first = [&](int c) { return c < n_g ? c * kChunk : lo + (c - n_g) * kChunk; };
-  auto chunk_count = [&](int c) {
-    return c < n_g ? min(kChunk, nb - c * kChunk) : min(kChunk, hi - chunk_first(c) + 1);
-  };
-
-  StageRegs<T> r;
-  stage_load<T>(r, kh, vh, bias_row, gidx, 0 < n_g, chunk_first(0), chunk_count(0), S);
-  stage_store<T>(bufs[0], r);
-  __syncthreads();
-  for (int c = 0; c < total; ++c) {
-    const bool more = c + 1 < total;
-    if (more)
-      stage_load<T>(r, kh, vh, bias_row, gidx, c + 1 < n_g, chunk_first(c + 1),
-                    chunk_count(c + 1), S);
-    ChunkBuf<T>& cb = bufs[c & 1];
-    if (wave_active) {
-      const bool is_band = c >= n_g;
-      const int kb = chunk_first(c);
-      bool touch = true, interior = true;
-      if (is_band) {
-        touch = kb <= r_hi + half && kb + kChunk - 1 >= r_lo - half;
-        interior = kb >= r_hi - half && kb + kChunk - 1 <= r_lo + half && kb + kChunk - 1 < S;
-      }
-      if (touch) {
-        f32x16 s0, s1;
-        qk_chunk_lds<T>(cb.k, qf, s0, s1);
-        v8 pf[4];
-        const bool bias = cb.flag != 0;
-        if (interior) {
-          if (bias)
-            softmax_chunk<T, false, true>(s0, s1, cb.bias2, kb, srow, half, S, c2, m_run, l_run,
-                                          o, 2, pf);
-          else
-            softmax_chunk<T, false, false>(s0, s1, cb.bias2, kb, srow, half, S, c2, m_run,
-                                           l_run, o, 2, pf);
-        } else {
-          if (bias)
-            softmax_chunk<T, true, true>(s0, s1, cb.bias2, kb, srow, half, S, c2, m_run, l_run,
-                                         o, 2, pf);
-          else
-            softmax_chunk<T, true, false>(s0, s1, cb.bias2, kb, srow, half, S, c2, m_run, l_run,
-                                          o, 2, pf);
-        }
-        pv_chunk<T>(cb.vt, pf, o);
-      }
-    }
-    if (more) stage_store<T>(bufs[(c + 1) & 1], r);
-    __syncthreads();
-  }
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  const bool write = srow < S && srow >= nb;
-  const bool live = write && Elem<T>::to_f(bias_row[write ? srow : 0]) == 0.0f;
-  store_rows<T>(a, b, h, srow, write, live, o, l_tot);
+// List entry i: global-key block i (positions 32i.., live below n_b; under the
+// head-of-sequence precondition the global positions are 0 .. n_b - 1), band
+// block i - ngb (keys kbase + 32(i - ngb).., live in [n_b, S)), or, right after
+// the list, the first round of this tile's global-row split (kg / vg keys
+// sp_lo + 32(i - n_list).., live in [sp_lo, sp_hi)), which the pipeline thus
+// prefetches during the last band steps.  Further entries read out of range (no
+// memory traffic) and are never read back.
+// (Conditional expressions below pick copied values, never two fields of the
+// context: selecting between field addresses would keep the context in memory.)
+template <typename T>
+__device__ inline int entry_base(const Ctx<T>& c, int i) {
+  const int ngb = c.ngb, n_list = c.n_list, S = c.S;
+  const int base = i < ngb ? kBlk * i : c.kbase + kBlk * (i - ngb);
+  const int sp = c.sp_lo + kBlk * (i - n_list);
+  return i < n_list ? base : (i < n_list + c.n_sp ? sp : S);
 }
 
-// ---------------------------------------------------------------- global workgroup
-// Rows r_base .. r_base + 32*NQB - 1 of the global queries of (b, h), keys of one split.
-template <typename T, int NQB>
-__device__ void global_split(const AttnArgs& a, int bh, int split, int qgroup, char* smem) {
-  typedef typename Frags<T>::v8 v8;
+template <typename T>
+__device__ inline void load_entry(Stage<T>& s, const Ctx<T>& c, int i) {
+  // the choice is uniform: select the (scalar) base pointers, then build the
+  // resources, so nothing about the load becomes per-lane
+  const bool band = i < c.n_list;
+  const uint32_t bytes = (uint32_t)c.S * 128u;
+  // select values, not the fields' addresses (keeps the context in registers)
+  const T* kp = c.kh;
+  const T* vp = c.vh;
+  const T* kgp = c.kgh;
+  const T* vgp = c.vgh;
+  stage_load<T>(s, make_rsrc(band ? kp : kgp, bytes), make_rsrc(band ? vp : vgp, bytes),
+                make_rsrc(c.mask, (uint32_t)c.S * 2u), entry_base(c, i));
+}
+
+template <typename T, bool RAW>
+__device__ inline void store_entry(Slot<T>& sl, const Stage<T>& s, const Ctx<T>& c, int i) {
+  const int nb = c.nb, S = c.S, sp_lo = c.sp_lo, sp_hi = c.sp_hi;
+  const bool glob = i < c.ngb, band = i < c.n_list;
+  const int lo = glob ? 0 : (band ? nb : sp_lo);
+  const int hi = glob ? nb : (band ? S : sp_hi);
+  stage_store<T, RAW>(sl, s, entry_base(c, i), lo, hi);
+}
+
+// ------------------------------------------------------------------ global rows
+// Key split `sp` of the global rows of (b, h): partial states into the workspace,
+// then the ticket; the workgroup that completes the ticket writes the rows.  The
+// first round's four blocks are already in the ring (list entries n_list ..
+// n_list + 3); later rounds / query blocks load theirs here.
+template <typename T, bool RAW>
+__device__ void global_split(const AttnArgs& a, const Ctx<T>& c, int sp, Slot<T>* ring) {
+  typedef typename Frag<T>::v8 v8;
+  const int t = threadIdx.x;
   const int lane = lane_id();
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();   // uniform: index math on the scalar unit
   const int n = lane & 31, g = lane >> 5;
-  const int b = bh / a.H, h = bh % a.H;
-  const int S = a.S;
-  const int nb = a.gcnt[b];
-  const int r_base = qgroup * 32 * NQB;
-  if (r_base >= nb) return;
-  const int k0 = split * a.split_len;
-  const int k1 = min(S, k0 + a.split_len);
-
-  const size_t head = (size_t)bh * S * 64;
-  const T* kh = (const T*)a.kg + head;
-  const T* vh = (const T*)a.vg + head;
-  const T* qgh = (const T*)a.qg + (size_t)bh * a.G * 64;
-  const T* bias_row = (const T*)a.bias + (size_t)b * S;
-  WaveBuf<T>* wb = (WaveBuf<T>*)smem + wave;
-
-  v8 qf[NQB][4];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const int r = r_base + 32 * qb + n;
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      qf[qb][t] = r < nb ? *(const v8*)(qgh + (size_t)r * 64 + 16 * t + 8 * g) : v8{};
-  }
-  f32x16 o[NQB][2];
-  float m_run[NQB], l_run[NQB];
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    o[qb][0] = f32x16{};
-    o[qb][1] = f32x16{};
-    m_run[qb] = kNegBig;
-    l_run[qb] = 0.0f;
-  }
+  const int G = c.G, nb = c.nb;
+  const T* qgh = (const T*)a.qg + (size_t)c.bh * G * 64;
+  const int k_lo = c.sp_lo, k_hi = c.sp_hi;
+  const int n_rounds = a.split_len / (kBlk * kWaves);
   const float c2 = a.scale * kLog2e;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  for (int kb = k0 + kChunk * wave; kb < k1; kb += kChunk * kWaves) {
-    // K fragments straight from memory: lane (key n (+32), d-half g)
-    v8 ka[2][4];
+  float* part = a.partials + ((size_t)c.bh * a.n_split + sp) * (size_t)G * kPartPitch;
+  const rsrc_t rpart = make_rsrc(part, (uint32_t)G * kPartPitch * 4u);
+
+  for (int qb = 0; qb * 32 < nb; ++qb) {
+    v8 qf[4];
+    const int r = 32 * qb + n;
+    load_q<T>(qf, qgh + (size_t)(r < nb ? r : 0) * 64, r < nb);
+    f32x16 o[2] = {f32x16{}, f32x16{}};
+    float m_run = kNegBig, l_run = 0.0f;
+    for (int u = 0; u < n_rounds; ++u) {
+      int slot = (c.n_list + wave) % kRing;
+      if (qb > 0 || u > 0) {
+        Stage<T> st[kWaves];
 #pragma unroll
-    for (int kblk = 0; kblk < 2; ++kblk) {
-      const int key = kb + 32 * kblk + n;
+        for (int w = 0; w < kWaves; ++w)
+          stage_load<T>(st[w], make_rsrc(c.kgh, (uint32_t)c.S * 128u),
+                        make_rsrc(c.vgh, (uint32_t)c.S * 128u), make_rsrc(c.mask, (uint32_t)c.S * 2u),
+                        k_lo + kBlk * (kWaves * u + w));
+        __syncthreads();   // earlier readers of the slots are done
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        ka[kblk][t] = key < k1 ? *(const v8*)(kh + (size_t)key * 64 + 16 * t + 8 * g) : v8{};
+        for (int w = 0; w < kWaves; ++w)
+          stage_store<T, RAW>(ring[w], st[w], k_lo + kBlk * (kWaves * u + w), k_lo, k_hi);
+        __syncthreads();
+        slot = wave;
+      }
+      block_step<T>(ring[slot], qf, o, m_run, l_run, c2, false, 0, 0);
     }
-    // V chunk -> transposed per-wave LDS tile
-    u32x4 va[4], vb[4];
+    __syncthreads();   // every wave is done with its block before the states go in
+    float* stp = (float*)&ring[wave];
+    const float l_tot = cross_half_sum(l_run);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int task = lane + 64 * i;
-      const int rp = task >> 3, col = task & 7;
-      const int key = kb + 2 * rp;
-      va[i] = key < k1 ? *(const u32x4*)(vh + (size_t)key * 64 + col * 8) : zero;
-      vb[i] = key + 1 < k1 ? *(const u32x4*)(vh + (size_t)(key + 1) * 64 + col * 8) : zero;
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        stp[n * kStPitch + 2 + 32 * mb + 8 * (v >> 2) + 4 * g + (v & 3)] = o[mb][v];
+    if (g == 0) {
+      stp[n * kStPitch + 0] = m_run;
+      stp[n * kStPitch + 1] = l_tot;
     }
-    const int bkey = kb + lane;
-    const float bias2 = bkey < k1 ? Elem<T>::to_f(bias_row[bkey]) * kLog2e : -INFINITY;
-    const bool any_bias = __ballot(bias2 != 0.0f) != 0ull;
-    __builtin_amdgcn_wave_barrier();   // previous chunk's LDS reads issued before rewriting
+    __syncthreads();
+    // merge the four wave states: thread -> (query q, 8 dims); publish with
+    // agent-scope atomic stores (write-through, coherent across XCDs)
+    {
+      const int q = t >> 3, d0 = (t & 7) * 8;
+      const int rr = 32 * qb + q;
+      float mw[kWaves], M = kNegBig;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int task = lane + 64 * i;
-      const int rp = task >> 3, col = task & 7;
-      const uint32_t* pa = (const uint32_t*)&va[i];
-      const uint32_t* pb = (const uint32_t*)&vb[i];
+      for (int w = 0; w < kWaves; ++w) {
+        mw[w] = ((const float*)&ring[w])[q * kStPitch];
+        M = fmaxf(M, mw[w]);
+      }
+      float L = 0.0f, acc[8];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        *(uint32_t*)&wb->vt[(col * 8 + 2 * w) * kVld + 2 * rp] = (pa[w] & 0xffffu) | (pb[w] << 16);
-        *(uint32_t*)&wb->vt[(col * 8 + 2 * w + 1) * kVld + 2 * rp] =
-            (pa[w] >> 16) | (pb[w] & 0xffff0000u);
+      for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float* sw = (const float*)&ring[w] + q * kStPitch;
+        const float f = fast_exp2(mw[w] - M);
+        L += sw[1] * f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += sw[2 + d0 + i] * f;
+      }
+      if (rr < nb) {
+        // write-through (sc1) stores: visible to every XCD once complete
+        const int off = (rr * kPartPitch + 4 + d0) * 4;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{acc[0], acc[1], acc[2], acc[3]}),
+                                               rpart, off, 0, kSc1);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{acc[4], acc[5], acc[6], acc[7]}),
+                                               rpart, off + 16, 0, kSc1);
+        if ((t & 7) == 0) {
+          const u32x2 ml = {__float_as_uint(M), __float_as_uint(L)};
+          __builtin_amdgcn_raw_buffer_store_b64(ml, rpart, rr * kPartPitch * 4, 0, kSc1);
+        }
       }
     }
-    wb->bias2[lane] = bias2;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      f32x16 s0 = f32x16{}, s1 = f32x16{};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        s0 = mfma32(ka[0][t], qf[qb][t], s0);
-        s1 = mfma32(ka[1][t], qf[qb][t], s1);
-      }
-      v8 pf[4];
-      if (any_bias)
-        softmax_chunk<T, false, true>(s0, s1, wb->bias2, kb, 0, 0, S, c2, m_run[qb], l_run[qb],
-                                      o[qb], 2, pf);
-      else
-        softmax_chunk<T, false, false>(s0, s1, wb->bias2, kb, 0, 0, S, c2, m_run[qb], l_run[qb],
-                                       o[qb], 2, pf);
-      pv_chunk<T>(wb->vt, pf, o[qb]);
-    }
-    (void)zero;
+    __syncthreads();   // slots free again
   }
-  // merge the four wave states in LDS (reusing the per-wave tiles), then write one
-  // partial (m, l, o[64]) per valid row
-  float* mbuf = (float*)smem;   // [NQB*32][66]
+
+  // ticket: every partial store of this workgroup has completed (write-through)
+  // before the ticket is taken
+  __shared__ int s_last;
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int w = 0; w < kWaves; ++w) {
-    if (wave == w) {
+  if (t == 0) {
+    const int old = __hip_atomic_fetch_add(a.counters + c.bh, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    s_last = old == a.n_split - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  // merge every split's partial: rows in chunks, (m, l) of all (row, split) pairs
+  // into LDS, per-row weights exp2(m - M) / L, then the output dims as weighted
+  // sums.  Partials are read with coherent (sc1) loads, all of a thread's loads in
+  // flight together; splits past n_split read out of range (zeros, weight 0).
+  const int ns = a.n_split;
+  const float* pbase = a.partials + (size_t)c.bh * ns * (size_t)G * kPartPitch;
+  const rsrc_t rall = make_rsrc(pbase, (uint32_t)ns * G * kPartPitch * 4u);
+  const int sstride = G * kPartPitch * 4;   // bytes between splits
+  T* outh = (T*)a.out + (size_t)c.b * a.out_sb + (size_t)c.h * a.out_sh;
+  float* mw = (float*)ring;                        // [rows][kMaxSplit]: m, then the weight
+  float* lw = mw + kCombinePairs;                  // [rows][kMaxSplit]: l
+  constexpr int rows_per_chunk = kCombinePairs / kMaxSplit;
+  for (int r0 = 0; r0 < nb; r0 += rows_per_chunk) {
+    const int nr = min(rows_per_chunk, nb - r0);
+    for (int i = t; i < nr * kMaxSplit; i += kThreads) {
+      const int rr = r0 + i / kMaxSplit, s2 = i % kMaxSplit;
+      const u32x2 ml = __builtin_amdgcn_raw_buffer_load_b64(
+          rall, s2 < ns ? s2 * sstride + rr * kPartPitch * 4 : -1, 0, kSc1);
+      mw[i] = s2 < ns ? __uint_as_float(ml[0]) : kNegBig;
+      lw[i] = __uint_as_float(ml[1]);
+    }
+    __syncthreads();
+    for (int rr = t; rr < nr; rr += kThreads) {
+      const float* m_r = mw + rr * kMaxSplit;
+      float M = kNegBig;
+      for (int s2 = 0; s2 < kMaxSplit; ++s2) M = fmaxf(M, m_r[s2]);
+      float L = 0.0f;
+      for (int s2 = 0; s2 < kMaxSplit; ++s2) L += lw[rr * kMaxSplit + s2] * fast_exp2(m_r[s2] - M);
+      const int pos = RAW ? r0 + rr : a.gidx[(size_t)c.b * c.S + r0 + rr];
+      const float inv = mask_live<RAW>(Elem<T>::to_f(c.mask[pos])) ? 1.0f / L : 0.0f;
+      for (int s2 = 0; s2 < kMaxSplit; ++s2)
+        mw[rr * kMaxSplit + s2] = s2 < ns ? fast_exp2(m_r[s2] - M) * inv : 0.0f;
+    }
+    __syncthreads();
+    for (int idx = t; idx < nr * 16; idx += kThreads) {
+      const int rl = idx >> 4, d4 = (idx & 15) * 4;
+      const int off0 = ((r0 + rl) * kPartPitch + 4 + d4) * 4;
+      f32x4 O = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        const int q = 32 * qb + n;
-        float* row = mbuf + q * 66;
-        const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
-        float mm = m_run[qb], ll = l_tot, f_old = 0.0f, f_new = 1.0f;
-        if (w > 0) {
-          const float m_old = row[0];
-          mm = fmaxf(m_old, m_run[qb]);
-          f_old = fast_exp2(m_old - mm);
-          f_new = fast_exp2(m_run[qb] - mm);
-          ll = row[1] * f_old + l_tot * f_new;
-        }
+      for (int h = 0; h < kMaxSplit; h += 16) {
+        u32x4 pv[16];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int j = 0; j < 16; ++j)
+          pv[j] = __builtin_amdgcn_raw_buffer_load_b128(
+              rall, h + j < ns ? off0 + (h + j) * sstride : -1, 0, kSc1);
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int d = 32 * mb + 8 * (v >> 2) + 4 * g + (v & 3);
-            const float prev = w > 0 ? row[2 + d] : 0.0f;
-            row[2 + d] = prev * f_old + o[qb][mb][v] * f_new;
-          }
-        if (g == 0) {
-          row[0] = mm;
-          row[1] = ll;
-        }
+        for (int j = 0; j < 16; ++j) O += __builtin_bit_cast(f32x4, pv[j]) * mw[rl * kMaxSplit + h + j];
       }
+      typename Frag<T>::v4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = Elem<T>::from_f(O[i]);
+      const int pos = RAW ? r0 + rl : a.gidx[(size_t)c.b * c.S + r0 + rl];
+      *(typename Frag<T>::v4*)(outh + (size_t)pos * a.out_ss + d4) = w;
     }
     __syncthreads();
   }
-  // 256 threads write NQB*32 rows x 66 floats
-  const int rows = min(32 * NQB, nb - r_base);
-  float* dst = a.partials + ((size_t)bh * a.n_split + split) * (size_t)a.G * 66 + (size_t)r_base * 66;
-  for (int i = threadIdx.x; i < rows * 66; i += kThreads) dst[i] = mbuf[i];
+  if (t == 0) __hip_atomic_store(a.counters + c.bh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// XCD-aware order: consecutive workgroup ids go round-robin over the 8 XCDs, so
-// give each XCD a contiguous run of logical tiles (neighbouring tiles of one head
-// share K/V rows in that XCD's L2).
+// ------------------------------------------------------------------ band work
+// Entry of wave `wave` at step t: global phase entry t, band phase entry t + wave.
+template <typename T>
+__device__ inline int wave_entry(const Ctx<T>& c, int t, int wave) {
+  return t < c.ngb ? t : t + wave;
+}
+
 __device__ inline int xcd_remap(int i, int n) {
+  // consecutive workgroup ids go round-robin over the 8 XCDs: give each XCD a
+  // contiguous run of logical tiles, so neighbouring tiles of one head share K / V
+  // rows in that XCD's L2
   const int per = n / 8;
   const int full = per * 8;
   if (i >= full) return i;
   return (i % 8) * per + i / 8;
 }
 
-template <typename T, int NQB>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_mfma_kernel(AttnArgs a, int n_tiles,
-                                                             int n_global_wg, int n_qgroups) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * sizeof(ChunkBuf<T>)];
-  static_assert(kWaves * sizeof(WaveBuf<T>) <= 2 * sizeof(ChunkBuf<T>), "lds");
-  static_assert(NQB * 32 * 66 * 4 <= 2 * sizeof(ChunkBuf<T>), "lds");
-  const int id = blockIdx.x;
-  if (id < n_global_wg) {
-    const int per_bh = a.n_split * n_qgroups;
-    const int bh = id / per_bh;
-    const int rem = id % per_bh;
-    global_split<T, NQB>(a, bh, rem / n_qgroups, rem % n_qgroups, smem);
-  } else {
-    const int n_band = a.B * a.H * n_tiles;
-    const int li = xcd_remap(id - n_global_wg, n_band);
-    band_tile<T>(a, li / n_tiles, li % n_tiles, (ChunkBuf<T>*)smem);
-  }
+// Number of global tokens of batch row b: raw mode counts the zeros among the first
+// G global-mask values (the tokens are leading, so this is their number); pre mode
+// reads global_count.
+template <typename T, bool RAW>
+__device__ inline int count_globals(const AttnArgs& a, int b) {
+  if (!RAW) return min(a.gcnt[b], a.G);
+  __shared__ int s_cnt;
+  if (threadIdx.x == 0) s_cnt = 0;
+  const T* gm = (const T*)a.global_mask + (size_t)b * a.S;
+  int cnt = 0;
+  for (int s = threadIdx.x; s < a.G; s += kThreads) cnt += Elem<T>::to_f(gm[s]) == 0.0f;
+  __syncthreads();
+  if (cnt) atomicAdd(&s_cnt, cnt);
+  __syncthreads();
+  return s_cnt;
 }
 
-// Merge the split partials of each global row; one wave per (b, h, r), lane = d.
-template <typename T>
-__global__ __launch_bounds__(256) void global_combine_kernel(AttnArgs a) {
-  const int bh = blockIdx.x;
-  const int b = bh / a.H, h = bh % a.H;
-  const int nb = a.gcnt[b];
-  (void)h;
-  const int d = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const T* bias_row = (const T*)a.bias + (size_t)b * a.S;
-  for (int r = wave; r < nb; r += 4) {
-    const float* p = a.partials + (size_t)bh * a.n_split * a.G * 66 + (size_t)r * 66;
-    float M = kNegBig;
-    for (int sp = 0; sp < a.n_split; ++sp) M = fmaxf(M, p[(size_t)sp * a.G * 66]);
-    float L = 0.0f, O = 0.0f;
-    for (int sp = 0; sp < a.n_split; ++sp) {
-      const float* q = p + (size_t)sp * a.G * 66;
-      const float f = fast_exp2(q[0] - M);
-      L += q[1] * f;
-      O += q[2 + d] * f;
-    }
-    const int s = a.gidx[(size_t)b * a.S + r];
-    const bool live = Elem<T>::to_f(bias_row[s]) == 0.0f;
-    T* dst = (T*)a.out + (size_t)b * a.out_sb + (size_t)h * a.out_sh + (size_t)s * a.out_ss;
-    dst[d] = Elem<T>::from_f(live ? O / L : 0.0f);
+template <typename T, bool RAW>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_mfma_kernel(AttnArgs a, int n_tiles) {
+  __shared__ __attribute__((aligned(16))) Slot<T> ring[kRing];
+  typedef typename Frag<T>::v8 v8;
+  const int t = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = wave_id();   // uniform: index math on the scalar unit
+  const int n = lane & 31, g = lane >> 5;
+  const int n_wg = a.B * a.H * n_tiles;
+  // the integer divides below run on the vector ALU; readfirstlane keeps their
+  // (uniform) results, and everything derived from them, in scalar registers
+  const int li = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, n_wg));
+
+  Ctx<T> c;
+  c.bh = __builtin_amdgcn_readfirstlane(li / n_tiles);
+  c.tile = __builtin_amdgcn_readfirstlane(li % n_tiles);
+  c.b = __builtin_amdgcn_readfirstlane(c.bh / a.H);
+  c.h = __builtin_amdgcn_readfirstlane(c.bh % a.H);
+  c.S = a.S;
+  c.W = a.W;
+  c.G = a.G;
+  c.ngb = (a.G + kBlk - 1) / kBlk;
+  c.r0 = c.tile * kTile;
+  c.kbase = c.r0 - (a.W >> 1);
+  const int nband = (c.W + 2 * kBlk - 1) / kBlk;
+  const int n_steps = c.ngb + nband;
+  c.n_list = n_steps + kWaves - 1;
+  const size_t head = (size_t)c.bh * c.S * 64;
+  c.mask = (const T*)(RAW ? a.local_mask : a.bias) + (size_t)c.b * c.S;
+  const float c2 = a.scale * kLog2e;
+  const bool split = a.G > 0 && c.tile < a.n_split;
+  c.n_sp = split ? kWaves : 0;
+  c.sp_lo = split ? c.tile * a.split_len : 0;
+  c.sp_hi = split ? min(c.S, c.sp_lo + a.split_len) : 0;
+  c.kh = (const T*)a.k + head;
+  c.vh = (const T*)a.v + head;
+  c.kgh = split ? (const T*)a.kg + head : c.kh;
+  c.vgh = split ? (const T*)a.vg + head : c.vh;
+
+  // every load the prologue needs is issued before anything waits
+  Stage<T> pro[kAhead];
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) load_entry<T>(pro[i], c, i);
+  // Q before the register sets: in the loop its wait count then never holds back
+  // the sets in flight
+  const int srow = c.r0 + 32 * wave + n;
+  v8 qf[4];
+  load_q<T>(qf, (const T*)a.q + head + (size_t)(srow < c.S ? srow : 0) * 64, srow < c.S);
+  __builtin_amdgcn_sched_barrier(0);
+  Stage<T> st[kDepth];   // entry e lives in set e % kDepth
+#pragma unroll
+  for (int u = 0; u < kDepth; ++u) {
+    load_entry<T>(st[(kAhead + u) % kDepth], c, kAhead + u);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  c.nb = count_globals<T, RAW>(a, c.b);
+
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) store_entry<T, RAW>(ring[i], pro[i], c, i);
+  __syncthreads();
+
+  f32x16 o[2] = {f32x16{}, f32x16{}};
+  float m_run = kNegBig, l_run = 0.0f;
+
+  // Software pipeline over the wave's blocks: at step t the scores of the next
+  // block (entry e(t+1)) go on the matrix cores while the softmax of the current
+  // one (entry e(t), scores from the previous step) runs on the vector ALUs, then
+  // its PV product is queued.  Entries t .. t+4 are readable at step t; entry t+5
+  // is written into the slot entry t-1 used (read for the last time before the
+  // previous barrier) and the loads of entry t+5+kDepth are issued into the same
+  // register set.  Entries past the list are written and read too (zeros /
+  // discarded scores), which keeps the step free of branches around memory
+  // operations.  Full groups of kDepth steps run without guards (so the wait
+  // counts stay those of the steady state); the remaining steps run once, guarded.
+  f32x16 sc[2];
+  int fl[2];
+  {
+    const Slot<T>& s0 = ring[wave_entry(c, 0, wave) % kRing];
+    fl[0] = __builtin_amdgcn_readfirstlane(s0.flag);
+    sc[0] = qk_block<T>(s0, qf);
+  }
+  auto step = [&](int tt, Stage<T>& set, f32x16& s_cur, int& f_cur, f32x16& s_nxt, int& f_nxt) {
+    const int e = tt + kAhead;
+    store_entry<T, RAW>(ring[e % kRing], set, c, e);
+    __builtin_amdgcn_sched_barrier(0);
+    load_entry<T>(set, c, e + kDepth);
+    __builtin_amdgcn_sched_barrier(0);
+    const Slot<T>& nx = ring[wave_entry(c, tt + 1, wave) % kRing];
+    f_nxt = __builtin_amdgcn_readfirstlane(nx.flag);
+    s_nxt = qk_block<T>(nx, qf);
+    const bool glob = tt < c.ngb;
+    const int tb = tt - c.ngb;
+    const bool inner = tb >= 1 && kBlk * tb + kBlk - 1 <= c.W;
+    softmax_pv<T>(ring[wave_entry(c, tt, wave) % kRing], s_cur, f_cur, o, m_run, l_run, c2,
+                  !glob && !inner, kBlk * tb + 4 * g - n, c.W);
+    __syncthreads();
+  };
+  static_assert(kDepth % 2 == 0, "score buffers alternate within a group of steps");
+  int t0 = 0;
+  for (; t0 + kDepth <= n_steps; t0 += kDepth) {
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u)
+      step(t0 + u, st[(u + kAhead) % kDepth], sc[u & 1], fl[u & 1], sc[(u + 1) & 1],
+           fl[(u + 1) & 1]);
+  }
+  // remaining steps, then two drain steps that only write the last two list
+  // entries (the split's blocks n_list + 2, n_list + 3, still in registers)
+#pragma unroll
+  for (int u = 0; u < kDepth + 1; ++u) {
+    const int tt = t0 + u;
+    if (tt < n_steps) {
+      step(tt, st[(u + kAhead) % kDepth], sc[u & 1], fl[u & 1], sc[(u + 1) & 1],
+           fl[(u + 1) & 1]);
+    } else if (tt < n_steps + 2) {
+      const int e = tt + kAhead;
+      store_entry<T, RAW>(ring[e % kRing], st[(u + kAhead) % kDepth], c, e);
+    }
+  }
+  __syncthreads();
+
+  // epilogue: normalise and store the local rows
+  const float l_tot = cross_half_sum(l_run);
+  const bool write = srow < c.S && srow >= c.nb;
+  if (write) {
+    const bool live = mask_live<RAW>(Elem<T>::to_f(c.mask[srow]));
+    const float inv = live ? 1.0f / l_tot : 0.0f;
+    T* dst = (T*)a.out + (size_t)c.b * a.out_sb + (size_t)c.h * a.out_sh + (size_t)srow * a.out_ss;
+    typedef typename Frag<T>::v4 v4;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        v4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = Elem<T>::from_f(live ? o[mb][4 * jj + i] * inv : 0.0f);
+        *(v4*)(dst + 32 * mb + 8 * jj + 4 * g) = w;
+      }
+    }
+  }
+
+  if (split && c.nb > 0) global_split<T, RAW>(a, c, c.tile, ring);
 }
 
 template <typename T>
 hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
-  const int n_tiles = (a.S + kTileRows - 1) / kTileRows;
-  const int64_t n_band = (int64_t)a.B * a.H * n_tiles;
-  const int nqb = a.G <= 32 ? 1 : 2;
-  const int n_qgroups = a.G > 0 ? (a.G + 32 * nqb - 1) / (32 * nqb) : 0;
-  const int64_t n_global = a.G > 0 ? (int64_t)a.B * a.H * a.n_split * n_qgroups : 0;
-  const int64_t grid = n_band + n_global;
+  const int n_tiles = (a.S + kTile - 1) / kTile;
+  const int64_t grid = (int64_t)a.B * a.H * n_tiles;
   if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (a.G > 0 && (a.split_len % (kBlk * kWaves) != 0 || a.n_split > n_tiles))
+    return hipErrorInvalidConfiguration;
+  if ((int64_t)a.S * 128 > 0x7fffffff) return hipErrorInvalidValue;   // per-head buffer range
   if (a.ev_begin) {
     hipError_t e0 = hipEventRecord(a.ev_begin, st);
     if (e0 != hipSuccess) return e0;
   }
-  if (nqb == 1)
-    attn_mfma_kernel<T, 1><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles, (int)n_global,
-                                                                n_qgroups);
+  if (a.raw)
+    attn_mfma_kernel<T, true><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles);
   else
-    attn_mfma_kernel<T, 2><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles, (int)n_global,
-                                                                n_qgroups);
+    attn_mfma_kernel<T, false><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.ev_end) {
-    e = hipEventRecord(a.ev_end, st);
-    if (e != hipSuccess) return e;
-  }
-  if (a.G > 0) {
-    global_combine_kernel<T><<<a.B * a.H, 256, 0, st>>>(a);
-    e = hipGetLastError();
-  }
+  if (a.ev_end) e = hipEventRecord(a.ev_end, st);
   return e;
 }
 
 }  // namespace
 
-size_t attn_partials_bytes(int B, int H, int S, int G, int* n_split, int* split_len) {
-  // about 512 global workgroups in total, at least 256 keys each
-  int64_t len = ((int64_t)B * H * S / 512 + 63) / 64 * 64;
-  if (len < 256) len = 256;
-  const int64_t s64 = ((int64_t)S + 63) / 64 * 64;
-  if (len > s64) len = s64;
-  const int ns = (int)((S + len - 1) / len);
-  if (n_split) *n_split = ns;
-  if (split_len) *split_len = (int)len;
-  return (size_t)B * H * ns * (size_t)(G > 0 ? G : 1) * 66 * sizeof(float);
+void attn_split_plan(int S, int* n_split, int* split_len) {
+  // one split per 128-row tile, at most 32 splits per (b, h); splits are whole
+  // rounds of 4 x 32 keys
+  const int n_tiles = (S + kTile - 1) / kTile;
+  const int want = n_tiles < kMaxSplit ? n_tiles : kMaxSplit;
+  const int unit = kBlk * kWaves;
+  int len = (S + want - 1) / want;
+  len = (len + unit - 1) / unit * unit;
+  *split_len = len;
+  *n_split = (S + len - 1) / len;
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {

@@ -10,7 +10,10 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "../../include/lf.h"
@@ -75,6 +78,8 @@ int validate_attn(int dtype, int B, int H, int S, int W, int G) {
     return fail(LF_ERR_INVALID_ARGUMENT, "G must satisfy 0 <= G <= W (G=%d, W=%d)", G, W);
   if ((int64_t)B * H * S > INT_MAX)
     return fail(LF_ERR_INVALID_ARGUMENT, "B*H*S exceeds 2^31-1");
+  if (dtype != LF_F32 && (int64_t)S * 128 > INT_MAX)
+    return fail(LF_ERR_INVALID_ARGUMENT, "S must be < 2^24 for fp16 / bf16 (got %d)", S);
   return LF_OK;
 }
 
@@ -96,32 +101,39 @@ int null_check(const char* names, std::initializer_list<const void*> ptrs) {
   return LF_OK;
 }
 
-// Workspace of lf_attn_forward_pre: global-row partials.
+// Attention workspace: [B*H int split tickets][global-row partial states].
 struct AttnWs {
-  size_t partials;
+  size_t partials_off;  // bytes; the tickets start at offset 0
+  size_t total;
   int n_split, split_len;
 };
 
 AttnWs attn_ws(int B, int H, int S, int G) {
   AttnWs w;
-  w.partials = align256(lf::attn_partials_bytes(B, H, S, G, &w.n_split, &w.split_len));
+  lf::attn_split_plan(S, &w.n_split, &w.split_len);
+  w.partials_off = align256((size_t)B * H * sizeof(int));
+  w.total = w.partials_off + align256((size_t)B * H * w.n_split * (size_t)(G > 0 ? G : 1) *
+                                      lf::kPartPitch * sizeof(float));
   return w;
 }
 
 lf::AttnArgs make_args(int dtype, const void* q, const void* k, const void* v, const void* qg,
                        const void* kg, const void* vg, const int32_t* gidx, const int32_t* gcnt,
                        const void* bias, int B, int H, int S, int W, int G, void* out,
-                       float* partials, const AttnWs& ws) {
+                       char* workspace, const AttnWs& ws, size_t partials_off) {
   lf::AttnArgs a;
   a.dtype = dtype;
+  a.raw = 0;
   a.q = q; a.k = k; a.v = v; a.qg = qg; a.kg = kg; a.vg = vg;
+  a.local_mask = nullptr; a.global_mask = nullptr;
   a.gidx = gidx; a.gcnt = gcnt; a.bias = bias; a.out = out;
   a.out_ss = 64;
   a.out_sh = (int64_t)S * 64;
   a.out_sb = (int64_t)H * S * 64;
   a.B = B; a.H = H; a.S = S; a.W = W; a.G = G;
   a.scale = 0.125f;
-  a.partials = partials;
+  a.counters = (int*)workspace;
+  a.partials = (float*)(workspace + partials_off);
   a.n_split = ws.n_split;
   a.split_len = ws.split_len;
   a.ev_begin = nullptr;
@@ -132,6 +144,54 @@ lf::AttnArgs make_args(int dtype, const void* q, const void* k, const void* v, c
     ++g_timing.used;
   }
   return a;
+}
+
+// Workspace of lf_attn_forward (fp16 / bf16), cached per (device, stream): the
+// split tickets [ticket_cap ints, zeroed when allocated and left zero by every
+// call] followed by the partial states.  Calls on one stream are ordered, so they
+// can share it; a call that needs more memory than the cache holds waits for the
+// stream, frees it and allocates a larger one (so the first calls on a stream
+// allocate, later ones do not).
+struct WsCache {
+  char* ptr = nullptr;
+  size_t ticket_cap = 0;   // ints
+  size_t part_bytes = 0;
+};
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, WsCache> g_ws;
+
+int cached_workspace(hipStream_t st, size_t tickets, size_t part_bytes, char** base,
+                     size_t* part_off) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  WsCache& w = g_ws[std::make_pair(dev, st)];
+  if (!w.ptr || w.ticket_cap < tickets || w.part_bytes < part_bytes) {
+    if (w.ptr) {
+      e = hipStreamSynchronize(st);
+      if (e != hipSuccess) return hip_fail(e, "workspace resize (stream sync)");
+      (void)hipFree(w.ptr);
+      w = WsCache();
+    }
+    const size_t cap = tickets < 1024 ? 1024 : tickets;
+    const size_t pb = part_bytes < 65536 ? 65536 : part_bytes;
+    const size_t bytes = align256(cap * sizeof(int)) + pb;
+    char* p = nullptr;
+    e = hipMalloc((void**)&p, bytes);
+    if (e != hipSuccess) return hip_fail(e, "workspace allocation");
+    e = hipMemsetAsync(p, 0, bytes, st);
+    if (e != hipSuccess) {
+      (void)hipFree(p);
+      return hip_fail(e, "workspace zero-fill");
+    }
+    w.ptr = p;
+    w.ticket_cap = cap;
+    w.part_bytes = pb;
+  }
+  *base = w.ptr;
+  *part_off = align256(w.ticket_cap * sizeof(int));
+  return LF_OK;
 }
 
 hipError_t run_attention(const lf::AttnArgs& a, hipStream_t st) {
@@ -169,7 +229,7 @@ int lf_init_global_idx(int dtype, const void* global_mask, int B, int S, int32_t
                          {global_mask, global_idx, global_count}))
     return e;
   hipError_t he = lf::launch_prep(dtype, global_mask, nullptr, B, S, global_idx, global_count,
-                                  nullptr, (hipStream_t)stream);
+                                  nullptr, nullptr, 0, (hipStream_t)stream);
   if (he != hipSuccess) return hip_fail(he, "lf_init_global_idx");
   return ok();
 }
@@ -187,7 +247,7 @@ int lf_mask_shift(int dtype, const void* local_mask, int B, int S, void* local_b
 
 size_t lf_attn_workspace_bytes(int dtype, int B, int H, int S, int W, int G) {
   if (validate_attn(dtype, B, H, S, W, G) != LF_OK) return 0;
-  return attn_ws(B, H, S, G).partials;
+  return attn_ws(B, H, S, G).total;
 }
 
 int lf_attn_forward_pre(int dtype, const void* q, const void* k, const void* v, const void* qg,
@@ -201,13 +261,12 @@ int lf_attn_forward_pre(int dtype, const void* q, const void* k, const void* v, 
     return e;
   if (G > 0 && !qg) return fail(LF_ERR_INVALID_ARGUMENT, "null pointer: qg (G > 0)");
   const AttnWs ws = attn_ws(B, H, S, G);
-  if (ws_bytes < ws.partials)
-    return fail(LF_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu", ws_bytes,
-                ws.partials);
+  if (ws_bytes < ws.total)
+    return fail(LF_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu", ws_bytes, ws.total);
   if (((uintptr_t)workspace) & 255)
     return fail(LF_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
   lf::AttnArgs a = make_args(dtype, q, k, v, qg, kg, vg, global_idx, global_count, local_bias, B,
-                             H, S, W, G, out, (float*)workspace, ws);
+                             H, S, W, G, out, (char*)workspace, ws, ws.partials_off);
   hipError_t he = run_attention(a, (hipStream_t)stream);
   if (he != hipSuccess) return hip_fail(he, "lf_attn_forward_pre");
   return ok();
@@ -262,22 +321,38 @@ int lf_attn_forward(int dtype, const void* q, const void* k, const void* v, cons
     if (int e = lf_check_masks(dtype, local_mask, global_mask, B, S, G, stream)) return e;
   }
   const AttnWs ws = attn_ws(B, H, S, G);
+  if (dtype != LF_F32) {
+    // one launch: the kernel reads both masks itself (count of the leading global
+    // tokens, live-key test of the shifted mask)
+    char* base = nullptr;
+    size_t part_off = 0;
+    if (int e = cached_workspace(st, (size_t)B * H, ws.total - ws.partials_off, &base, &part_off))
+      return e;
+    lf::AttnArgs a = make_args(dtype, q, k, v, qg, kg, vg, nullptr, nullptr, nullptr, B, H, S, W,
+                               G, out, base, ws, part_off);
+    a.raw = 1;
+    a.local_mask = local_mask;
+    a.global_mask = global_mask;
+    hipError_t he = run_attention(a, st);
+    if (he != hipSuccess) return hip_fail(he, "lf_attn_forward");
+    return ok();
+  }
+  // fp32: preprocessing kernel, then the vector-ALU attention kernel
   const size_t n_bs = (size_t)B * S;
   const size_t off_idx = 0;
   const size_t off_cnt = align256(off_idx + n_bs * sizeof(int32_t));
   const size_t off_bias = align256(off_cnt + (size_t)B * sizeof(int32_t));
-  const size_t off_part = align256(off_bias + n_bs * dtype_size(dtype));
-  const size_t total = off_part + ws.partials;
+  const size_t total = align256(off_bias + n_bs * dtype_size(dtype));
   char* scratch = nullptr;
   hipError_t he = hipMallocAsync((void**)&scratch, total, st);
   if (he != hipSuccess) return hip_fail(he, "lf_attn_forward scratch");
   int32_t* gidx = (int32_t*)(scratch + off_idx);
   int32_t* gcnt = (int32_t*)(scratch + off_cnt);
   void* bias = scratch + off_bias;
-  he = lf::launch_prep(dtype, global_mask, local_mask, B, S, gidx, gcnt, bias, st);
+  he = lf::launch_prep(dtype, global_mask, local_mask, B, S, gidx, gcnt, bias, nullptr, 0, st);
   if (he == hipSuccess) {
     lf::AttnArgs a = make_args(dtype, q, k, v, qg, kg, vg, gidx, gcnt, bias, B, H, S, W, G, out,
-                               (float*)(scratch + off_part), ws);
+                               nullptr, ws, 0);
     he = run_attention(a, st);
   }
   hipError_t he2 = hipFreeAsync(scratch, st);

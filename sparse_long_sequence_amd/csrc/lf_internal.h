@@ -12,26 +12,37 @@ namespace lf {
 // head-joined [B, S, H*64] layout directly.
 struct AttnArgs {
   int dtype;
+  int raw;                // 1: read local_mask / global_mask; 0: read gidx / gcnt / bias
   const void *q, *k, *v, *qg, *kg, *vg;
-  const int32_t* gidx;    // [B, S]
-  const int32_t* gcnt;    // [B]
-  const void* bias;       // [B, S] shifted local mask, dtype
+  const void* local_mask;   // [B, S] dtype (raw mode)
+  const void* global_mask;  // [B, S] dtype (raw mode)
+  const int32_t* gidx;    // [B, S] (pre mode)
+  const int32_t* gcnt;    // [B]    (pre mode)
+  const void* bias;       // [B, S] shifted local mask, dtype (pre mode)
   void* out;
   int64_t out_sb, out_sh, out_ss;
   int B, H, S, W, G;
   float scale;
-  float* partials;        // global-row partial states (see attn_workspace_layout)
+  float* partials;        // global-row partial states [B*H][n_split][G][kPartPitch]
+  int* counters;          // [B*H] split tickets: zero on entry, left zero on exit
   int n_split;            // key splits of the global rows
-  int split_len;          // keys per split (multiple of 64)
+  int split_len;          // keys per split (multiple of 128)
   hipEvent_t ev_begin;    // if non-null: recorded right before / after the main kernel
   hipEvent_t ev_end;
 };
 
-// Global-row partial states: [B*H][n_split][G][66] fp32 = (m, l, o[64]).
-size_t attn_partials_bytes(int B, int H, int S, int G, int* n_split, int* split_len);
+// Floats per global-row partial state: m (scaled log2 units), l, 2 pad, o[64].
+constexpr int kPartPitch = 68;
 
+// Key splits of the global rows for sequence length S (fp16 / bf16 kernel).
+void attn_split_plan(int S, int* n_split, int* split_len);
+
+// Global-index partition + count (when global_mask != NULL), mask shift (when
+// local_mask != NULL) and, when tickets != NULL, zeroing of B * tickets_per_row
+// attention tickets; one launch.
 hipError_t launch_prep(int dtype, const void* global_mask, const void* local_mask, int B, int S,
-                       int32_t* gidx, int32_t* gcnt, void* bias, hipStream_t st);
+                       int32_t* gidx, int32_t* gcnt, void* bias, int* tickets,
+                       int tickets_per_row, hipStream_t st);
 hipError_t launch_mask_shift(int dtype, const void* local_mask, int64_t n, void* bias,
                              hipStream_t st);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);

@@ -25,25 +25,47 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const T* __restrict_
                                                             const T* __restrict__ lmask, int S,
                                                             int32_t* __restrict__ gidx,
                                                             int32_t* __restrict__ gcnt,
-                                                            T* __restrict__ bias) {
+                                                            T* __restrict__ bias,
+                                                            int* __restrict__ tickets,
+                                                            int tickets_per_row) {
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  if (PART) {
-    __shared__ int s_off[kSlices * kPrepWaves];
-    __shared__ int s_total;
-    const T* gm = gmask + (size_t)b * S;
-    int32_t* out = gidx + (size_t)b * S;
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int carry = 0;
-    for (int base = 0; base < S; base += kSlices * kPrepThreads) {
+  // zero the attention kernel's per-(b, h) tickets of this batch row
+  if (tickets)
+    for (int i = tid; i < tickets_per_row; i += kPrepThreads)
+      tickets[(size_t)b * tickets_per_row + i] = 0;
+  __shared__ int s_off[kSlices * kPrepWaves];
+  __shared__ int s_total;
+  const T* gm = gmask + (size_t)b * S;
+  const T* lm = lmask + (size_t)b * S;
+  int32_t* out = gidx + (size_t)b * S;
+  T* bo = bias + (size_t)b * S;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int carry = 0;
+  for (int base = 0; base < S; base += kSlices * kPrepThreads) {
+    // every load of the pass is issued before any result is used
+    T gv[kSlices], lv[kSlices];
+#pragma unroll
+    for (int e = 0; e < kSlices; ++e) {
+      const int pos = base + e * kPrepThreads + tid;
+      if (PART) gv[e] = pos < S ? gm[pos] : Elem<T>::from_f(1.0f);
+      if (SHIFT) lv[e] = pos < S ? lm[pos] : Elem<T>::from_f(0.0f);
+    }
+    if (SHIFT) {
+#pragma unroll
+      for (int e = 0; e < kSlices; ++e) {
+        const int pos = base + e * kPrepThreads + tid;
+        if (pos < S) bo[pos] = Elem<T>::from_f(fmaf(Elem<T>::to_f(lv[e]), 10000.0f, -10000.0f));
+      }
+    }
+    if (PART) {
       bool f[kSlices];
       uint64_t bal[kSlices];
 #pragma unroll
       for (int e = 0; e < kSlices; ++e) {
-        const int pos = base + e * kPrepThreads + tid;
-        f[e] = pos < S && Elem<T>::to_f(gm[pos]) == 0.0f;
+        f[e] = Elem<T>::to_f(gv[e]) == 0.0f;
         bal[e] = __ballot(f[e]);
       }
       if (lane == 0) {
@@ -72,14 +94,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const T* __restrict_
       carry += s_total;
       __syncthreads();
     }
-    if (tid == 0) gcnt[b] = carry;
   }
-  if (SHIFT) {
-    const T* lm = lmask + (size_t)b * S;
-    T* bo = bias + (size_t)b * S;
-    for (int pos = tid; pos < S; pos += kPrepThreads)
-      bo[pos] = Elem<T>::from_f(fmaf(Elem<T>::to_f(lm[pos]), 10000.0f, -10000.0f));
-  }
+  if (PART && tid == 0) gcnt[b] = carry;
 }
 
 // Elementwise shift over n values, 8 per thread per step (16-byte loads for 16-bit types).
@@ -144,16 +160,17 @@ __global__ __launch_bounds__(256) void check_masks_kernel(const T* __restrict__ 
 
 template <typename T>
 hipError_t prep_t(const void* g, const void* l, int B, int S, int32_t* idx, int32_t* cnt,
-                  void* bias, hipStream_t st) {
+                  void* bias, int* tickets, int tickets_per_row, hipStream_t st) {
   if (g && l)
     prep_kernel<T, true, true><<<B, kPrepThreads, 0, st>>>((const T*)g, (const T*)l, S, idx, cnt,
-                                                          (T*)bias);
+                                                          (T*)bias, tickets, tickets_per_row);
   else if (g)
     prep_kernel<T, true, false><<<B, kPrepThreads, 0, st>>>((const T*)g, nullptr, S, idx, cnt,
-                                                           nullptr);
+                                                           nullptr, tickets, tickets_per_row);
   else
     prep_kernel<T, false, true><<<B, kPrepThreads, 0, st>>>(nullptr, (const T*)l, S, nullptr,
-                                                           nullptr, (T*)bias);
+                                                           nullptr, (T*)bias, tickets,
+                                                           tickets_per_row);
   return hipGetLastError();
 }
 
@@ -176,11 +193,12 @@ hipError_t check_t(const void* l, const void* g, int B, int S, int G, int* flags
 }  // namespace
 
 hipError_t launch_prep(int dtype, const void* global_mask, const void* local_mask, int B, int S,
-                       int32_t* gidx, int32_t* gcnt, void* bias, hipStream_t st) {
+                       int32_t* gidx, int32_t* gcnt, void* bias, int* tickets,
+                       int tickets_per_row, hipStream_t st) {
   switch (dtype) {
-    case 0: return prep_t<float>(global_mask, local_mask, B, S, gidx, gcnt, bias, st);
-    case 1: return prep_t<f16>(global_mask, local_mask, B, S, gidx, gcnt, bias, st);
-    case 2: return prep_t<bf16>(global_mask, local_mask, B, S, gidx, gcnt, bias, st);
+    case 0: return prep_t<float>(global_mask, local_mask, B, S, gidx, gcnt, bias, tickets, tickets_per_row, st);
+    case 1: return prep_t<f16>(global_mask, local_mask, B, S, gidx, gcnt, bias, tickets, tickets_per_row, st);
+    case 2: return prep_t<bf16>(global_mask, local_mask, B, S, gidx, gcnt, bias, tickets, tickets_per_row, st);
   }
   return hipErrorInvalidValue;
 }
