@@ -172,36 +172,75 @@ __device__ inline typename Frag<T>::v2 cvt_pair(float a, float b) {
   return __builtin_convertvector(x, typename Frag<T>::v2);
 }
 
-// S^T of one 32-key block for the wave's 32 queries (4 MFMAs; the result is not
-// waited for here).
+// Operand fragments of one 32-key block, read from LDS.  K: A operand of
+// S^T = K Q^T (lane (n, g) holds key n, dims 16t + 8g ..); V^T: A operand of
+// O^T += V^T P^T (lane holds dim 32mb + n, keys 16h + 4g .. +3 and 16h + 8 + 4g ..).
 template <typename T>
-__device__ inline f32x16 qk_block(const Slot<T>& sl, const typename Frag<T>::v8 qf[4]) {
+struct KFrag {
+  typename Frag<T>::v8 a[4];
+};
+template <typename T>
+struct VFrag {
+  typename Frag<T>::v8 a[2][2];   // [h][mb]
+};
+
+template <typename T>
+__device__ inline void read_k(KFrag<T>& f, const Slot<T>& sl) {
   typedef typename Frag<T>::v8 v8;
   const int lane = lane_id();
   const int n = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) f.a[t] = *(const v8*)&sl.k[n * kKld + 16 * t + 8 * g];
+}
+
+template <typename T>
+__device__ inline void read_v(VFrag<T>& f, const Slot<T>& sl) {
+  typedef typename Frag<T>::v4 v4;
+  const int lane = lane_id();
+  const int n = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const T* row = sl.vt + (32 * mb + n) * kVld + 16 * h + 4 * g;
+      const v4 lo = *(const v4*)row;
+      const v4 hi = *(const v4*)(row + 8);
+      f.a[h][mb] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+  }
+}
+
+// S^T of one block for the wave's 32 queries (4 MFMAs).
+template <typename T>
+__device__ inline f32x16 qk_frag(const KFrag<T>& kf, const typename Frag<T>::v8 qf[4]) {
   f32x16 s = f32x16{};
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const v8 a = *(const v8*)&sl.k[n * kKld + 16 * t + 8 * g];
-    s = mfma32(a, qf[t], s);
-  }
+  for (int t = 0; t < 4; ++t) s = mfma32(kf.a[t], qf[t], s);
   return s;
 }
 
-// Online-softmax update with the scores s of one block, then O^T += V^T P^T.
-// flag (uniform): 0 every key live, else add the per-key 0 / -inf term.
+// O^T += V^T P^T (4 MFMAs).
+template <typename T>
+__device__ inline void pv_frag(const VFrag<T>& vf, const typename Frag<T>::v8 pf[2], f32x16 o[2]) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) o[mb] = mfma32(vf.a[h][mb], pf[h], o[mb]);
+  }
+}
+
+// Online-softmax update with the scores s of one block; returns the P^T operand.
+// flag (uniform): 0 every key live, else add the per-key 0 / -inf term of `sl`.
 // band (uniform): apply |j - s| <= W/2 with c = band_c + 8*(v/4) + (v%4) in 0..W.
 // Every block runs the same code on the accumulators (a block without a live key
 // adds exact zeros), so the only branch that touches them is the rare rescale.
 template <typename T>
-__device__ inline void softmax_pv(const Slot<T>& sl, const f32x16& s, int flag, f32x16 o[2],
-                                  float& m_run, float& l_run, float c2, bool band, int band_c,
-                                  int W) {
-  typedef typename Frag<T>::v8 v8;
-  typedef typename Frag<T>::v4 v4;
+__device__ inline void softmax_p(const Slot<T>& sl, const f32x16& s, int flag, f32x16 o[2],
+                                 float& m_run, float& l_run, float c2, bool band, int band_c,
+                                 int W, typename Frag<T>::v8 pf[2]) {
   typedef typename Frag<T>::v2 v2;
   const int lane = lane_id();
-  const int n = lane & 31, g = lane >> 5;
+  const int g = lane >> 5;
   float x[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) x[v] = s[v];
@@ -220,9 +259,12 @@ __device__ inline void softmax_pv(const Slot<T>& sl, const f32x16& s, int flag, 
       x[v] = (unsigned)c <= (unsigned)W ? x[v] : -INFINITY;
     }
   }
-  float mx = x[0];
+  // max as a tree (short dependency chains)
+  float m4[4];
 #pragma unroll
-  for (int v = 1; v < 16; ++v) mx = fmaxf(mx, x[v]);
+  for (int i = 0; i < 4; ++i)
+    m4[i] = fmaxf(fmaxf(x[4 * i], x[4 * i + 1]), fmaxf(x[4 * i + 2], x[4 * i + 3]));
+  float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
   mx = cross_half_max(mx);
   const float ms = mx * c2;
   const bool need = ms > m_run + kLazy;
@@ -237,8 +279,7 @@ __device__ inline void softmax_pv(const Slot<T>& sl, const f32x16& s, int flag, 
     }
     m_run = m_new;
   }
-  v8 pf[2];
-  float lsum = 0.0f;
+  float ls[2] = {0.0f, 0.0f};   // two independent row-sum chains
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
@@ -248,21 +289,10 @@ __device__ inline void softmax_pv(const Slot<T>& sl, const f32x16& s, int flag, 
       const v2 pp = cvt_pair<T>(p0, p1);
       pf[h2][e] = pp[0];
       pf[h2][e + 1] = pp[1];
-      lsum = dot2_ones(pp, lsum);
+      ls[h2] = dot2_ones(pp, ls[h2]);
     }
   }
-  l_run += lsum;
-#pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2) {
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const T* row = sl.vt + (32 * mb + n) * kVld + 16 * h2 + 4 * g;
-      const v4 lo = *(const v4*)row;
-      const v4 hi = *(const v4*)(row + 8);
-      const v8 va = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      o[mb] = mfma32(va, pf[h2], o[mb]);
-    }
-  }
+  l_run += ls[0] + ls[1];
 }
 
 // One whole block (used where there is nothing to overlap it with).
@@ -270,9 +300,16 @@ template <typename T>
 __device__ inline void block_step(const Slot<T>& sl, const typename Frag<T>::v8 qf[4],
                                   f32x16 o[2], float& m_run, float& l_run, float c2, bool band,
                                   int band_c, int W) {
+  typedef typename Frag<T>::v8 v8;
   const int flag = __builtin_amdgcn_readfirstlane(sl.flag);
-  const f32x16 s = qk_block<T>(sl, qf);
-  softmax_pv<T>(sl, s, flag, o, m_run, l_run, c2, band, band_c, W);
+  KFrag<T> kf;
+  read_k<T>(kf, sl);
+  const f32x16 s = qk_frag<T>(kf, qf);
+  VFrag<T> vf;
+  read_v<T>(vf, sl);
+  v8 pf[2];
+  softmax_p<T>(sl, s, flag, o, m_run, l_run, c2, band, band_c, W, pf);
+  pv_frag<T>(vf, pf, o);
 }
 
 template <typename T>
@@ -609,27 +646,42 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // discarded scores), which keeps the step free of branches around memory
   // operations.  Full groups of kDepth steps run without guards (so the wait
   // counts stay those of the steady state); the remaining steps run once, guarded.
+  // step order: every LDS read of the step first (V^T of the current block, K and
+  // flag of the next), then the staging, then the softmax on the vector ALUs
+  // (hiding the reads' latency), then the next block's QK^T and the current
+  // block's PV on the matrix cores, then the barrier.
   f32x16 sc[2];
-  int fl[2];
+  int fl[2];   // flag of the block whose scores sit in sc[] (a lane value until used)
   {
     const Slot<T>& s0 = ring[wave_entry(c, 0, wave) % kRing];
-    fl[0] = __builtin_amdgcn_readfirstlane(s0.flag);
-    sc[0] = qk_block<T>(s0, qf);
+    fl[0] = s0.flag;
+    KFrag<T> kf;
+    read_k<T>(kf, s0);
+    sc[0] = qk_frag<T>(kf, qf);
   }
   auto step = [&](int tt, Stage<T>& set, f32x16& s_cur, int& f_cur, f32x16& s_nxt, int& f_nxt) {
+    typedef typename Frag<T>::v8 v8;
+    const Slot<T>& cs = ring[wave_entry(c, tt, wave) % kRing];
+    const Slot<T>& nx = ring[wave_entry(c, tt + 1, wave) % kRing];
+    VFrag<T> vf;
+    read_v<T>(vf, cs);
+    KFrag<T> kf;
+    read_k<T>(kf, nx);
+    f_nxt = nx.flag;
+    __builtin_amdgcn_sched_barrier(0);
     const int e = tt + kAhead;
     store_entry<T, RAW>(ring[e % kRing], set, c, e);
     __builtin_amdgcn_sched_barrier(0);
     load_entry<T>(set, c, e + kDepth);
     __builtin_amdgcn_sched_barrier(0);
-    const Slot<T>& nx = ring[wave_entry(c, tt + 1, wave) % kRing];
-    f_nxt = __builtin_amdgcn_readfirstlane(nx.flag);
-    s_nxt = qk_block<T>(nx, qf);
     const bool glob = tt < c.ngb;
     const int tb = tt - c.ngb;
     const bool inner = tb >= 1 && kBlk * tb + kBlk - 1 <= c.W;
-    softmax_pv<T>(ring[wave_entry(c, tt, wave) % kRing], s_cur, f_cur, o, m_run, l_run, c2,
-                  !glob && !inner, kBlk * tb + 4 * g - n, c.W);
+    v8 pf[2];
+    softmax_p<T>(cs, s_cur, __builtin_amdgcn_readfirstlane(f_cur), o, m_run, l_run, c2,
+                 !glob && !inner, kBlk * tb + 4 * g - n, c.W, pf);
+    s_nxt = qk_frag<T>(kf, qf);
+    pv_frag<T>(vf, pf, o);
     __syncthreads();
   };
   static_assert(kDepth % 2 == 0, "score buffers alternate within a group of steps");
