@@ -16,33 +16,35 @@
 // it reads global_count / the shifted mask produced by the preprocessing entry
 // points.
 //
-// Band workgroup: 4 waves = 128 query rows of one (b, h); wave w owns rows
-// r0 + 32w .. r0 + 32w + 31.  Keys move in blocks of 32 rows (K row-major, V
-// transposed, plus a per-key 0 / -inf validity term) through a 5-slot LDS ring.
-// The key list of a workgroup is
-//     [ceil(G/32) global-key blocks][band blocks 0 .. nband+2]
-// where band block j holds keys r0 - W/2 + 32j ..; wave w needs band blocks
-// w .. w + nband - 1 (nband = (W + 63) / 32).  At step t every wave reads entry t
-// (global phase) or t + w (band phase: the waves walk the band on a diagonal, so
-// none of them idles); entry t + 4 is written into the ring from registers and the
-// loads of entry t + 4 + kDepth are issued (kDepth register sets in flight: memory
-// latency is ~1-2 us against ~0.2 us of work per step).  One barrier per step.
+// Band workgroup: 8 waves = 256 query rows of one (b, h), two waves per SIMD (one
+// wave's vector work overlaps the other's matrix work).  Wave w owns the 32 rows
+// r0 + 64 (w % 4) + 32 (w / 4) ..: row group w % 4, sub-block w / 4.  Keys move in
+// blocks of 32 rows (K row-major, V transposed, plus a per-key 0 / -inf term)
+// through a 10-slot LDS ring.  The key list of a workgroup is
+//     [ceil(G/32) global-key blocks][band blocks 0 .. nband+6]
+// where band block j holds keys r0 - W/2 + 32j ..; row group rg needs band blocks
+// 2rg .. 2rg + nband (nband = (W + 63) / 32).  At step t every wave reads entry t
+// (global phase) or t + 2rg (band phase: the row groups walk the band on a
+// diagonal, so none of them idles); entry t + 9 is written into the ring from
+// registers and the loads of entry t + 11 are issued.  One barrier per step.
 //
-// Per block and wave: S^T = K Q^T (4 x v_mfma_f32_32x32x16), so each lane holds
-// 16 scores of ONE query (lanes n and n + 32 share a query); the running max is
-// kept in scaled log2 units and only moved when it grows by more than 8 (then
-// p <= 2^8, exact range for fp16 / bf16), so rescaling the accumulators is rare;
-// P is rounded to the input type, its row sum is taken from the rounded values
-// (v_dot2), then O^T += V^T P^T (4 more MFMAs).
+// Per block and wave: S^T = K Q^T (4 x v_mfma_f32_32x32x16, accumulator initialised
+// with the per-key term, so dead keys cost no vector work), so each lane holds 16
+// scores of ONE query (lanes n and n + 32 share a query); the running max is kept in
+// scaled log2 units and only moved when it grows by more than 8 (then p <= 2^8,
+// exact range for fp16 / bf16), so rescaling the accumulators is rare; P is rounded
+// to the input type, its row sum is taken from the rounded values (v_dot2), and
+// O^T += V^T P^T (4 more MFMAs) runs one step later, next to the QK^T of the
+// following block, while the vector ALUs work on the softmax.
 //
 // Global rows (r < n_b) attend to all live keys through kg / vg.  The first
 // n_split tiles of each (b, h) also take one key split of those rows (split_len
-// keys, 32 per wave per round) before their band work: the four wave states are
+// keys, 32 per wave per round) after their band work: the eight wave states are
 // merged in LDS and one partial (m, l, o[64]) per row is published with
-// agent-scope atomic stores (coherent across XCDs without cache maintenance);
-// after them the workgroup takes an atomic ticket, and the one that completes the
-// (b, h) reads all partials with agent-scope atomic loads, writes the global rows
-// and resets the ticket.
+// write-through stores (coherent across XCDs without cache maintenance); after
+// them the workgroup takes an atomic ticket, and the one that completes the (b, h)
+// reads all partials with coherent loads, writes the global rows and resets the
+// ticket.
 #include "lf_device.h"
 #include "lf_internal.h"
 
@@ -50,15 +52,17 @@ namespace lf {
 
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kTile = 32 * kWaves;   // query rows per workgroup
+constexpr int kRowsW = 32;           // query rows per wave
+constexpr int kTile = kRowsW * kWaves;  // query rows per workgroup
 constexpr int kBlk = 32;             // keys per block
 constexpr int kKld = 72;             // LDS row pitch of K (elements): 144 B, conflict-free reads
-constexpr int kVld = 36;             // LDS row pitch of V^T (elements): 72 B, conflict-free reads
-constexpr int kRing = 6;             // LDS block slots
-constexpr int kAhead = kWaves + 1;   // entry t + kAhead is written at step t
-constexpr int kDepth = 4;            // register sets of loads in flight
+constexpr int kVld = 40;             // LDS row pitch of V^T (elements): 80 B, 16-B aligned rows
+constexpr int kRing = 10;            // LDS block slots
+constexpr int kAhead = 9;            // entry t + kAhead is written at step t
+constexpr int kSpPref = 8;           // split blocks prefetched through the list
+constexpr int kDepth = 2;            // register sets of loads in flight
 constexpr int kStPitch = 67;         // floats per row of a wave state in LDS: m, l, o[64], pad
 constexpr int kCombinePairs = 4096;  // (row, split) pairs per combine chunk (2 x 16 KB of LDS)
 constexpr int kMaxSplit = 32;        // at most this many key splits per (b, h)
@@ -103,44 +107,49 @@ __device__ inline bool mask_live(float x) {
   return RAW ? x == 1.0f : x == 0.0f;
 }
 
-// Thread t stages K row t/8 (16 B at column 8*(t%8)), V rows 2*(t/16), 2*(t/16)+1
-// (8 B each at column 4*(t%16)) and, for t < 32, the mask value of key slot t.
+// Thread t stages K row t/16 (8 B at column 4*(t%16)), dims 2*(t%32) .. +1 of the
+// key pair 2*(t/32), 2*(t/32)+1 of V (4 B each) and, for t < 32, the mask value of
+// key slot t.  Every thread does the same work; no branch.
 template <typename T>
 struct Stage {
-  u32x4 k;
-  u32x2 v0, v1;
+  u32x2 k;
+  uint32_t v0, v1;
   unsigned short mask_bits;
 };
 
-// Block of keys base .. base + 31.  Every thread issues the same four loads (no
-// branch), so the compiler can keep later entries in flight while it waits for
-// this one.  K / V rows are loaded for every in-range key (a dead key's score is
-// masked to -inf, so its data never matters).
+// Block of keys base .. base + 31.  Every thread issues the same four loads, so the
+// compiler can keep later entries in flight while it waits for this one.  K / V
+// rows are loaded for every in-range key (a dead key's score is masked to -inf, so
+// its data never matters).
 template <typename T>
 __device__ inline void stage_load(Stage<T>& s, rsrc_t rk, rsrc_t rv, rsrc_t rm, int base) {
   const int t = threadIdx.x;
-  const int koff = (t >> 3) * 128 + 16 * (t & 7);
-  const int voff = (t >> 4) * 256 + 8 * (t & 15);
   const int b128 = base * 128;
-  s.k = __builtin_amdgcn_raw_buffer_load_b128(rk, b128 + koff, 0, 0);
-  s.v0 = __builtin_amdgcn_raw_buffer_load_b64(rv, b128 + voff, 0, 0);
-  s.v1 = __builtin_amdgcn_raw_buffer_load_b64(rv, b128 + voff + 128, 0, 0);
+  const int voff = (t >> 5) * 256 + 4 * (t & 31);
+  s.k = __builtin_amdgcn_raw_buffer_load_b64(rk, b128 + (t >> 4) * 128 + 8 * (t & 15), 0, 0);
+  s.v0 = __builtin_amdgcn_raw_buffer_load_b32(rv, b128 + voff, 0, 0);
+  s.v1 = __builtin_amdgcn_raw_buffer_load_b32(rv, b128 + voff + 128, 0, 0);
   s.mask_bits = __builtin_amdgcn_raw_buffer_load_b16(rm, t < kBlk ? 2 * (base + t) : -1, 0, 0);
+}
+
+// Position of key kk (0..31) inside a V^T row: within each 16-key half, lane group g
+// of the PV MFMA needs keys 4g .. 4g+3 and 8+4g .. 8+4g+3 (the row order of the
+// score fragment), so those eight are stored together and read as 16 bytes.
+__device__ inline int vt_pos(int kk) {
+  return (kk & 16) + (kk & 3) + 4 * ((kk >> 3) & 1) + 8 * ((kk >> 2) & 1);
 }
 
 // Write a staged block; key base + j is live iff lo <= key < hi and its mask says so.
 template <typename T, bool RAW>
 __device__ inline void stage_store(Slot<T>& sl, const Stage<T>& s, int base, int lo, int hi) {
   const int t = threadIdx.x;
-  const int kr = t >> 3, kc = t & 7, vp = t >> 4, vc = t & 15;
-  *(u32x4*)&sl.k[kr * kKld + 8 * kc] = s.k;
-  uint32_t* vt = (uint32_t*)sl.vt;
+  *(u32x2*)&sl.k[(t >> 4) * kKld + 4 * (t & 15)] = s.k;
+  // dims 2c, 2c+1 of keys 2vp, 2vp+1 -> V^T rows 2c, 2c+1, one dword (a key pair) each
+  const int vp = t >> 5, cc = t & 31;
+  uint32_t* vt = (uint32_t*)sl.vt + vt_pos(2 * vp) / 2;
   constexpr int P = kVld / 2;   // pitch in dwords
-  // element i of keys (2vp, 2vp+1) -> V^T[4vc + i][2vp .. 2vp+1] as one dword
-  vt[(4 * vc + 0) * P + vp] = (s.v0[0] & 0xffffu) | (s.v1[0] << 16);
-  vt[(4 * vc + 1) * P + vp] = (s.v0[0] >> 16) | (s.v1[0] & 0xffff0000u);
-  vt[(4 * vc + 2) * P + vp] = (s.v0[1] & 0xffffu) | (s.v1[1] << 16);
-  vt[(4 * vc + 3) * P + vp] = (s.v0[1] >> 16) | (s.v1[1] & 0xffff0000u);
+  vt[(2 * cc) * P] = __builtin_amdgcn_perm(s.v1, s.v0, 0x05040100u);
+  vt[(2 * cc + 1) * P] = __builtin_amdgcn_perm(s.v1, s.v0, 0x07060302u);
   if (wave_id() == 0) {
     const int lane = lane_id();
     const int key = base + lane;
@@ -153,10 +162,12 @@ __device__ inline void stage_store(Slot<T>& sl, const Stage<T>& s, int base, int
 }
 
 // ------------------------------------------------------------------ per-wave math
+__device__ inline float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ inline float cross_half_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ inline float cross_half_sum(float x) {
@@ -174,7 +185,8 @@ __device__ inline typename Frag<T>::v2 cvt_pair(float a, float b) {
 
 // Operand fragments of one 32-key block, read from LDS.  K: A operand of
 // S^T = K Q^T (lane (n, g) holds key n, dims 16t + 8g ..); V^T: A operand of
-// O^T += V^T P^T (lane holds dim 32mb + n, keys 16h + 4g .. +3 and 16h + 8 + 4g ..).
+// O^T += V^T P^T (lane holds dim 32mb + n, keys 16h + 4g .. +3 and 16h + 8 + 4g ..,
+// stored side by side).
 template <typename T>
 struct KFrag {
   typename Frag<T>::v8 a[4];
@@ -195,18 +207,14 @@ __device__ inline void read_k(KFrag<T>& f, const Slot<T>& sl) {
 
 template <typename T>
 __device__ inline void read_v(VFrag<T>& f, const Slot<T>& sl) {
-  typedef typename Frag<T>::v4 v4;
+  typedef typename Frag<T>::v8 v8;
   const int lane = lane_id();
   const int n = lane & 31, g = lane >> 5;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const T* row = sl.vt + (32 * mb + n) * kVld + 16 * h + 4 * g;
-      const v4 lo = *(const v4*)row;
-      const v4 hi = *(const v4*)(row + 8);
-      f.a[h][mb] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
+    for (int mb = 0; mb < 2; ++mb)
+      f.a[h][mb] = *(const v8*)(sl.vt + (32 * mb + n) * kVld + 16 * h + 8 * g);
   }
 }
 
@@ -217,6 +225,32 @@ __device__ inline f32x16 qk_frag(const KFrag<T>& kf, const typename Frag<T>::v8 
 #pragma unroll
   for (int t = 0; t < 4; ++t) s = mfma32(kf.a[t], qf[t], s);
   return s;
+}
+
+// S^T of one block plus the per-key term (0 / -inf) as accumulator init: dead keys
+// come out at -inf with no vector-ALU work.
+template <typename T>
+__device__ inline f32x16 qk_frag_c(const KFrag<T>& kf, const typename Frag<T>::v8 qf[4],
+                                   const f32x16& c) {
+  f32x16 s = c;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) s = mfma32(kf.a[t], qf[t], s);
+  return s;
+}
+
+// Per-key term of a block in the accumulator layout (lane (n, g), v -> key
+// 8 (v / 4) + 4 g + v % 4).
+template <typename T>
+__device__ inline f32x16 read_bias(const Slot<T>& sl) {
+  const int g = lane_id() >> 5;
+  f32x16 c;
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const f32x4 bb = *(const f32x4*)&sl.bias2[8 * jj + 4 * g];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[4 * jj + i] = bb[i];
+  }
+  return c;
 }
 
 // O^T += V^T P^T (4 MFMAs).
@@ -259,12 +293,13 @@ __device__ inline void softmax_p(const Slot<T>& sl, const f32x16& s, int flag, f
       x[v] = (unsigned)c <= (unsigned)W ? x[v] : -INFINITY;
     }
   }
-  // max as a tree (short dependency chains)
-  float m4[4];
+  // max as a tree of three-input maxima (NaN-propagating maximum: no operand
+  // canonicalisation, the scores are never NaN)
+  float m5[5];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    m4[i] = fmaxf(fmaxf(x[4 * i], x[4 * i + 1]), fmaxf(x[4 * i + 2], x[4 * i + 3]));
-  float mx = fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3]));
+  for (int i = 0; i < 5; ++i) m5[i] = vmax(vmax(x[3 * i], x[3 * i + 1]), x[3 * i + 2]);
+  float mx = vmax(vmax(m5[0], m5[1]), vmax(m5[2], x[15]));
+  mx = vmax(vmax(mx, m5[3]), m5[4]);
   mx = cross_half_max(mx);
   const float ms = mx * c2;
   const bool need = ms > m_run + kLazy;
@@ -280,6 +315,84 @@ __device__ inline void softmax_p(const Slot<T>& sl, const f32x16& s, int flag, f
     m_run = m_new;
   }
   float ls[2] = {0.0f, 0.0f};   // two independent row-sum chains
+#pragma unroll
+  for (int h2 = 0; h2 < 2; ++h2) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const float p0 = fast_exp2(fmaf(x[8 * h2 + e], c2, -m_run));
+      const float p1 = fast_exp2(fmaf(x[8 * h2 + e + 1], c2, -m_run));
+      const v2 pp = cvt_pair<T>(p0, p1);
+      pf[h2][e] = pp[0];
+      pf[h2][e + 1] = pp[1];
+      ls[h2] = dot2_ones(pp, ls[h2]);
+    }
+  }
+  l_run += ls[0] + ls[1];
+}
+
+// Two-phase form of the same update for the band loop, where PV of the previous
+// block is still pending when the scores of this one arrive.
+// Phase 1: masking (only where `MASKED`) and the scaled row max of one sub-block.
+template <typename T, bool MASKED>
+__device__ __forceinline__ float masked_max(const Slot<T>& sl, const f32x16& s, int flag, bool band,
+                                            int band_c, int W, float c2, float x[16]) {
+  const int g = lane_id() >> 5;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) x[v] = s[v];
+  if (MASKED) {
+    if (flag) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const f32x4 bb = *(const f32x4*)&sl.bias2[8 * jj + 4 * g];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[4 * jj + i] += bb[i];
+      }
+    }
+    if (band) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int c = band_c + 8 * (v >> 2) + (v & 3);
+        x[v] = (unsigned)c <= (unsigned)W ? x[v] : -INFINITY;
+      }
+    }
+  }
+  float m5[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) m5[i] = vmax(vmax(x[3 * i], x[3 * i + 1]), x[3 * i + 2]);
+  float mx = vmax(vmax(m5[0], m5[1]), vmax(m5[2], x[15]));
+  mx = vmax(vmax(mx, m5[3]), m5[4]);
+  return cross_half_max(mx) * c2;
+}
+
+// Rare path: the max of some row grew by more than kLazy.  The pending PV of the
+// previous block (made with the old max) is added first, then the accumulators
+// are rescaled and the pending P cleared, so the unconditional PV that follows
+// adds zeros.
+template <typename T>
+__device__ __forceinline__ void rescale_pending(const VFrag<T>& vf, float ms,
+                                                typename Frag<T>::v8 pf[2], f32x16 o[2],
+                                                float& m_run, float& l_run) {
+  typedef typename Frag<T>::v8 v8;
+  pv_frag<T>(vf, pf, o);
+  pf[0] = v8{};
+  pf[1] = v8{};
+  const float m_new = ms > m_run + kLazy ? ms : m_run;
+  const float alpha = fast_exp2(m_run - m_new);
+  l_run *= alpha;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    o[0][v] *= alpha;
+    o[1][v] *= alpha;
+  }
+  m_run = m_new;
+}
+
+// Phase 2: P = exp2(c2 x - m), rounded to T, and its row sum.
+template <typename T>
+__device__ __forceinline__ void exp_p(const float x[16], float m_run, float c2, float& l_run,
+                                      typename Frag<T>::v8 pf[2]) {
+  typedef typename Frag<T>::v2 v2;
+  float ls[2] = {0.0f, 0.0f};
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
@@ -375,8 +488,8 @@ __device__ inline void store_entry(Slot<T>& sl, const Stage<T>& s, const Ctx<T>&
 // ------------------------------------------------------------------ global rows
 // Key split `sp` of the global rows of (b, h): partial states into the workspace,
 // then the ticket; the workgroup that completes the ticket writes the rows.  The
-// first round's four blocks are already in the ring (list entries n_list ..
-// n_list + 3); later rounds / query blocks load theirs here.
+// first n_sp / 4 rounds of four blocks are already in the ring (list entries
+// n_list ..); later rounds / query blocks load theirs here.
 template <typename T, bool RAW>
 __device__ void global_split(const AttnArgs& a, const Ctx<T>& c, int sp, Slot<T>* ring) {
   typedef typename Frag<T>::v8 v8;
@@ -398,9 +511,10 @@ __device__ void global_split(const AttnArgs& a, const Ctx<T>& c, int sp, Slot<T>
     load_q<T>(qf, qgh + (size_t)(r < nb ? r : 0) * 64, r < nb);
     f32x16 o[2] = {f32x16{}, f32x16{}};
     float m_run = kNegBig, l_run = 0.0f;
+    const int n_pref = c.n_sp / kWaves;   // rounds already in the ring
     for (int u = 0; u < n_rounds; ++u) {
-      int slot = (c.n_list + wave) % kRing;
-      if (qb > 0 || u > 0) {
+      int slot = (c.n_list + kWaves * u + wave) % kRing;
+      if (qb > 0 || u >= n_pref) {
         Stage<T> st[kWaves];
 #pragma unroll
         for (int w = 0; w < kWaves; ++w)
@@ -429,9 +543,9 @@ __device__ void global_split(const AttnArgs& a, const Ctx<T>& c, int sp, Slot<T>
       stp[n * kStPitch + 1] = l_tot;
     }
     __syncthreads();
-    // merge the four wave states: thread -> (query q, 8 dims); publish with
-    // agent-scope atomic stores (write-through, coherent across XCDs)
-    {
+    // merge the wave states: thread -> (query q, 8 dims); publish with
+    // write-through stores (coherent across XCDs)
+    if (t < 32 * 8) {
       const int q = t >> 3, d0 = (t & 7) * 8;
       const int rr = 32 * qb + q;
       float mw[kWaves], M = kNegBig;
@@ -539,10 +653,13 @@ __device__ void global_split(const AttnArgs& a, const Ctx<T>& c, int sp, Slot<T>
 }
 
 // ------------------------------------------------------------------ band work
-// Entry of wave `wave` at step t: global phase entry t, band phase entry t + wave.
+// Wave w owns the 32 rows r0 + 64 (w % 4) + 32 (w / 4) ..: row group w % 4, sub-block
+// w / 4.  Entry of row group rg at step t: global phase entry t, band phase entry
+// t + 2 rg (row group rg's first band block is 2rg: its 64 rows start 64 rg after the
+// tile's).
 template <typename T>
-__device__ inline int wave_entry(const Ctx<T>& c, int t, int wave) {
-  return t < c.ngb ? t : t + wave;
+__device__ inline int wave_entry(const Ctx<T>& c, int t, int rg) {
+  return t < c.ngb ? t : t + 2 * rg;
 }
 
 __device__ inline int xcd_remap(int i, int n) {
@@ -572,13 +689,80 @@ __device__ inline int count_globals(const AttnArgs& a, int b) {
   return s_cnt;
 }
 
+// Staging only: write entry t + kAhead into the ring, load entry t + kAhead + kDepth.
 template <typename T, bool RAW>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_mfma_kernel(AttnArgs a, int n_tiles) {
+__device__ __forceinline__ void stage_step(const Ctx<T>& c, Slot<T>* ring, int tt, Stage<T>& set) {
+  const int e = tt + kAhead;
+  store_entry<T, RAW>(ring[e % kRing], set, c, e);
+  __builtin_amdgcn_sched_barrier(0);
+  load_entry<T>(set, c, e + kDepth);
+}
+
+// One step t of a wave.  On entry the wave holds the scores of block t (dead keys
+// already at -inf), the K fragment and per-key term of block t + 1, and the V^T
+// fragment and P of block t - 1.  The matrix-core work of the step (PV of t - 1,
+// QK^T of t + 1) does not depend on the step's softmax, so the two overlap (and the
+// other wave of the SIMD fills the gaps); PV goes first so that the rare rescale
+// finds it in the accumulators.  Before the barrier the wave already reads what
+// the next step needs (K and per-key term of t + 2, V^T of t): those entries were
+// written a step earlier, so their LDS latency hides behind the barrier.  Entries
+// t .. t + 8 are read during the step and t + 9 is written: the ring has ten slots.
+template <typename T, bool RAW>
+__device__ __forceinline__ void band_step(const Ctx<T>& c, Slot<T>* ring, int tt, int rg, int sb,
+                                          int n, int g, float c2, Stage<T>& set,
+                                          const typename Frag<T>::v8 qf[4], f32x16 o[2],
+                                          float& m_run, float& l_run, f32x16& s_cur,
+                                          f32x16& s_nxt, f32x16& cb, KFrag<T>& kf,
+                                          VFrag<T>& vf, typename Frag<T>::v8 pf[2]) {
+  pv_frag<T>(vf, pf, o);
+  s_nxt = qk_frag_c<T>(kf, qf, cb);
+  const int tq = tt - c.ngb - sb;   // band block relative to this sub-block's first one
+  // blocks tq = 1 .. (W - 31) / 32 lie wholly inside the window of every row
+  if (tt >= c.ngb && !(tq >= 1 && kBlk * tq + kBlk - 1 <= c.W)) {
+    const int band_c = kBlk * tq + 4 * g - n;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int cc = band_c + 8 * (v >> 2) + (v & 3);
+      s_cur[v] = (unsigned)cc <= (unsigned)c.W ? s_cur[v] : -INFINITY;
+    }
+  }
+  float m5[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) m5[i] = vmax(vmax(s_cur[3 * i], s_cur[3 * i + 1]), s_cur[3 * i + 2]);
+  float mx = vmax(vmax(m5[0], m5[1]), vmax(m5[2], s_cur[15]));
+  mx = vmax(vmax(mx, m5[3]), m5[4]);
+  const float ms = cross_half_max(mx) * c2;
+  if (__builtin_expect(__ballot(ms > m_run + kLazy) != 0ull, 0)) {
+    // rare: the max of some row grew by more than kLazy
+    const float m_new = ms > m_run + kLazy ? ms : m_run;
+    const float alpha = fast_exp2(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      o[0][v] *= alpha;
+      o[1][v] *= alpha;
+    }
+    m_run = m_new;
+  }
+  float x[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) x[v] = s_cur[v];
+  exp_p<T>(x, m_run, c2, l_run, pf);
+  stage_step<T, RAW>(c, ring, tt, set);
+  const Slot<T>& k2 = ring[wave_entry(c, tt + 2, rg) % kRing];
+  read_k<T>(kf, k2);
+  cb = read_bias<T>(k2);
+  read_v<T>(vf, ring[wave_entry(c, tt, rg) % kRing]);
+  __syncthreads();
+}
+
+template <typename T, bool RAW>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_mfma_kernel(AttnArgs a, int n_tiles) {
   __shared__ __attribute__((aligned(16))) Slot<T> ring[kRing];
   typedef typename Frag<T>::v8 v8;
-  const int t = threadIdx.x;
   const int lane = lane_id();
   const int wave = wave_id();   // uniform: index math on the scalar unit
+  const int rg = wave & 3, sb = wave >> 2;
   const int n = lane & 31, g = lane >> 5;
   const int n_wg = a.B * a.H * n_tiles;
   // the integer divides below run on the vector ALU; readfirstlane keeps their
@@ -596,14 +780,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   c.ngb = (a.G + kBlk - 1) / kBlk;
   c.r0 = c.tile * kTile;
   c.kbase = c.r0 - (a.W >> 1);
+  // a row group needs nband + 1 band blocks (its second sub-block starts one block
+  // later); the steps run in pairs (the register sets alternate), so an odd count
+  // gets one more step, whose block is outside every window and adds nothing
   const int nband = (c.W + 2 * kBlk - 1) / kBlk;
-  const int n_steps = c.ngb + nband;
-  c.n_list = n_steps + kWaves - 1;
+  const int n_steps = (c.ngb + nband + 1 + 1) & ~1;
+  c.n_list = c.ngb + nband + 2 * 3 + 1;
   const size_t head = (size_t)c.bh * c.S * 64;
   c.mask = (const T*)(RAW ? a.local_mask : a.bias) + (size_t)c.b * c.S;
   const float c2 = a.scale * kLog2e;
   const bool split = a.G > 0 && c.tile < a.n_split;
-  c.n_sp = split ? kWaves : 0;
+  const int sp_blocks = a.split_len / kBlk;
+  c.n_sp = split ? (sp_blocks < kSpPref ? sp_blocks : kSpPref) : 0;
   c.sp_lo = split ? c.tile * a.split_len : 0;
   c.sp_hi = split ? min(c.S, c.sp_lo + a.split_len) : 0;
   c.kh = (const T*)a.k + head;
@@ -617,11 +805,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   for (int i = 0; i < kAhead; ++i) load_entry<T>(pro[i], c, i);
   // Q before the register sets: in the loop its wait count then never holds back
   // the sets in flight
-  const int srow = c.r0 + 32 * wave + n;
   v8 qf[4];
+  const int srow = c.r0 + 64 * rg + 32 * sb + n;
   load_q<T>(qf, (const T*)a.q + head + (size_t)(srow < c.S ? srow : 0) * 64, srow < c.S);
   __builtin_amdgcn_sched_barrier(0);
-  Stage<T> st[kDepth];   // entry e lives in set e % kDepth
+  static_assert(kDepth == 2, "steps run in pairs: entry e uses set e % 2");
+  Stage<T> st[kDepth];
 #pragma unroll
   for (int u = 0; u < kDepth; ++u) {
     load_entry<T>(st[(kAhead + u) % kDepth], c, kAhead + u);
@@ -635,94 +824,54 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
   f32x16 o[2] = {f32x16{}, f32x16{}};
   float m_run = kNegBig, l_run = 0.0f;
-
-  // Software pipeline over the wave's blocks: at step t the scores of the next
-  // block (entry e(t+1)) go on the matrix cores while the softmax of the current
-  // one (entry e(t), scores from the previous step) runs on the vector ALUs, then
-  // its PV product is queued.  Entries t .. t+4 are readable at step t; entry t+5
-  // is written into the slot entry t-1 used (read for the last time before the
-  // previous barrier) and the loads of entry t+5+kDepth are issued into the same
-  // register set.  Entries past the list are written and read too (zeros /
-  // discarded scores), which keeps the step free of branches around memory
-  // operations.  Full groups of kDepth steps run without guards (so the wait
-  // counts stay those of the steady state); the remaining steps run once, guarded.
-  // step order: every LDS read of the step first (V^T of the current block, K and
-  // flag of the next), then the staging, then the softmax on the vector ALUs
-  // (hiding the reads' latency), then the next block's QK^T and the current
-  // block's PV on the matrix cores, then the barrier.
-  f32x16 sc[2];
-  int fl[2];   // flag of the block whose scores sit in sc[] (a lane value until used)
+  f32x16 sc0, sc1;   // scores of the current / next block
+  f32x16 cb;         // per-key term of the next block
+  v8 pf[2] = {v8{}, v8{}};   // P of the previous block: none yet
+  KFrag<T> kf;
+  VFrag<T> vf;
   {
-    const Slot<T>& s0 = ring[wave_entry(c, 0, wave) % kRing];
-    fl[0] = s0.flag;
-    KFrag<T> kf;
+    const Slot<T>& s0 = ring[wave_entry(c, 0, rg) % kRing];
+    const Slot<T>& s1 = ring[wave_entry(c, 1, rg) % kRing];
     read_k<T>(kf, s0);
-    sc[0] = qk_frag<T>(kf, qf);
+    sc0 = qk_frag_c<T>(kf, qf, read_bias<T>(s0));
+    read_k<T>(kf, s1);
+    cb = read_bias<T>(s1);
+    read_v<T>(vf, s0);   // with P = 0: adds nothing
   }
-  auto step = [&](int tt, Stage<T>& set, f32x16& s_cur, int& f_cur, f32x16& s_nxt, int& f_nxt) {
-    typedef typename Frag<T>::v8 v8;
-    const Slot<T>& cs = ring[wave_entry(c, tt, wave) % kRing];
-    const Slot<T>& nx = ring[wave_entry(c, tt + 1, wave) % kRing];
-    VFrag<T> vf;
-    read_v<T>(vf, cs);
-    KFrag<T> kf;
-    read_k<T>(kf, nx);
-    f_nxt = nx.flag;
-    __builtin_amdgcn_sched_barrier(0);
-    const int e = tt + kAhead;
-    store_entry<T, RAW>(ring[e % kRing], set, c, e);
-    __builtin_amdgcn_sched_barrier(0);
-    load_entry<T>(set, c, e + kDepth);
-    __builtin_amdgcn_sched_barrier(0);
-    const bool glob = tt < c.ngb;
-    const int tb = tt - c.ngb;
-    const bool inner = tb >= 1 && kBlk * tb + kBlk - 1 <= c.W;
-    v8 pf[2];
-    softmax_p<T>(cs, s_cur, __builtin_amdgcn_readfirstlane(f_cur), o, m_run, l_run, c2,
-                 !glob && !inner, kBlk * tb + 4 * g - n, c.W, pf);
-    s_nxt = qk_frag<T>(kf, qf);
-    pv_frag<T>(vf, pf, o);
-    __syncthreads();
-  };
-  static_assert(kDepth % 2 == 0, "score buffers alternate within a group of steps");
-  int t0 = 0;
-  for (; t0 + kDepth <= n_steps; t0 += kDepth) {
-#pragma unroll
-    for (int u = 0; u < kDepth; ++u)
-      step(t0 + u, st[(u + kAhead) % kDepth], sc[u & 1], fl[u & 1], sc[(u + 1) & 1],
-           fl[(u + 1) & 1]);
+  constexpr int s0i = kAhead % kDepth, s1i = (kAhead + 1) % kDepth;
+  for (int t0 = 0; t0 < n_steps; t0 += 2) {
+    band_step<T, RAW>(c, ring, t0, rg, sb, n, g, c2, st[s0i], qf, o, m_run, l_run, sc0, sc1, cb,
+                      kf, vf, pf);
+    band_step<T, RAW>(c, ring, t0 + 1, rg, sb, n, g, c2, st[s1i], qf, o, m_run, l_run, sc1, sc0, cb,
+                      kf, vf, pf);
   }
-  // remaining steps, then two drain steps that only write the last two list
-  // entries (the split's blocks n_list + 2, n_list + 3, still in registers)
-#pragma unroll
-  for (int u = 0; u < kDepth + 1; ++u) {
-    const int tt = t0 + u;
-    if (tt < n_steps) {
-      step(tt, st[(u + kAhead) % kDepth], sc[u & 1], fl[u & 1], sc[(u + 1) & 1],
-           fl[(u + 1) & 1]);
-    } else if (tt < n_steps + 2) {
-      const int e = tt + kAhead;
-      store_entry<T, RAW>(ring[e % kRing], st[(u + kAhead) % kDepth], c, e);
-    }
+  pv_frag<T>(vf, pf, o);   // PV of the last block (its V^T was read by the last step)
+  // drain: stage the split's prefetched blocks still in registers (in pairs; at most
+  // one extra entry, out of range, lands in a slot nobody reads any more)
+  const int n_drain = c.n_list + c.n_sp - (n_steps + kAhead);
+  for (int t0 = n_steps; t0 < n_steps + n_drain; t0 += 2) {
+    stage_step<T, RAW>(c, ring, t0, st[s0i]);
+    stage_step<T, RAW>(c, ring, t0 + 1, st[s1i]);
   }
   __syncthreads();
 
   // epilogue: normalise and store the local rows
-  const float l_tot = cross_half_sum(l_run);
-  const bool write = srow < c.S && srow >= c.nb;
-  if (write) {
-    const bool live = mask_live<RAW>(Elem<T>::to_f(c.mask[srow]));
-    const float inv = live ? 1.0f / l_tot : 0.0f;
-    T* dst = (T*)a.out + (size_t)c.b * a.out_sb + (size_t)c.h * a.out_sh + (size_t)srow * a.out_ss;
+  {
     typedef typename Frag<T>::v4 v4;
+    const float l_tot = cross_half_sum(l_run);
+    if (srow < c.S && srow >= c.nb) {
+      const bool live = mask_live<RAW>(Elem<T>::to_f(c.mask[srow]));
+      const float inv = live ? 1.0f / l_tot : 0.0f;
+      T* dst = (T*)a.out + (size_t)c.b * a.out_sb + (size_t)c.h * a.out_sh + (size_t)srow * a.out_ss;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+      for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        v4 w;
+        for (int jj = 0; jj < 4; ++jj) {
+          v4 w;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = Elem<T>::from_f(live ? o[mb][4 * jj + i] * inv : 0.0f);
-        *(v4*)(dst + 32 * mb + 8 * jj + 4 * g) = w;
+          for (int i = 0; i < 4; ++i) w[i] = Elem<T>::from_f(live ? o[mb][4 * jj + i] * inv : 0.0f);
+          *(v4*)(dst + 32 * mb + 8 * jj + 4 * g) = w;
+        }
       }
     }
   }
