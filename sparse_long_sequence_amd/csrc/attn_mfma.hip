@@ -39,12 +39,12 @@
 //
 // Global rows (r < n_b) attend to all live keys through kg / vg.  The first
 // n_split tiles of each (b, h) also take one key split of those rows (split_len
-// keys, 32 per wave per round) after their band work: the eight wave states are
-// merged in LDS and one partial (m, l, o[64]) per row is published with
-// write-through stores (coherent across XCDs without cache maintenance); after
-// them the workgroup takes an atomic ticket, and the one that completes the (b, h)
-// reads all partials with coherent loads, writes the global rows and resets the
-// ticket.
+// keys, 32 per wave per round) before their band work (its first loads go out with
+// the band's): the eight wave states are merged in LDS and one partial
+// (m, l, o[64]) per row is published with write-through stores (coherent across
+// XCDs without cache maintenance).  After its band work the workgroup takes an
+// atomic ticket, and the one that completes the (b, h) reads all partials with
+// coherent loads, writes the global rows and resets the ticket.
 #include "lf_device.h"
 #include "lf_internal.h"
 
@@ -61,10 +61,8 @@ constexpr int kKld = 72;             // LDS row pitch of K (elements): 144 B, co
 constexpr int kVld = 40;             // LDS row pitch of V^T (elements): 80 B, 16-B aligned rows
 constexpr int kRing = 10;            // LDS block slots
 constexpr int kAhead = 9;            // entry t + kAhead is written at step t
-constexpr int kSpPref = 8;           // split blocks prefetched through the list
 constexpr int kDepth = 2;            // register sets of loads in flight
 constexpr int kStPitch = 67;         // floats per row of a wave state in LDS: m, l, o[64], pad
-constexpr int kCombinePairs = 4096;  // (row, split) pairs per combine chunk (2 x 16 KB of LDS)
 constexpr int kMaxSplit = 32;        // at most this many key splits per (b, h)
 constexpr int kSc1 = 16;             // cache-policy bit of coherent (write-through / bypass) access
 constexpr float kLog2e = 1.4426950408889634f;
@@ -81,7 +79,6 @@ struct Slot {
 };
 
 static_assert(32 * kStPitch * 4 <= sizeof(Slot<_Float16>), "a wave state fits in one slot");
-static_assert(2 * kCombinePairs * 4 <= kRing * sizeof(Slot<_Float16>), "combine buffers fit the ring");
 
 template <typename T>
 struct Frag {
@@ -437,7 +434,6 @@ __device__ inline void load_q(typename Frag<T>::v8 qf[4], const T* __restrict__ 
 template <typename T>
 struct Ctx {
   int b, h, bh, tile, S, W, G, nb, ngb, r0, kbase, n_list;
-  int n_sp;                  // split entries after the list (4 if this tile carries one)
   int sp_lo, sp_hi;          // key range of the split
   const T *kh, *vh;          // k, v of this head
   const T *kgh, *vgh;        // kg, vg of this head (split tiles; else k, v)
@@ -445,53 +441,40 @@ struct Ctx {
 };
 
 // List entry i: global-key block i (positions 32i.., live below n_b; under the
-// head-of-sequence precondition the global positions are 0 .. n_b - 1), band
-// block i - ngb (keys kbase + 32(i - ngb).., live in [n_b, S)), or, right after
-// the list, the first round of this tile's global-row split (kg / vg keys
-// sp_lo + 32(i - n_list).., live in [sp_lo, sp_hi)), which the pipeline thus
-// prefetches during the last band steps.  Further entries read out of range (no
-// memory traffic) and are never read back.
-// (Conditional expressions below pick copied values, never two fields of the
-// context: selecting between field addresses would keep the context in memory.)
+// head-of-sequence precondition the global positions are 0 .. n_b - 1) or band
+// block i - ngb (keys kbase + 32(i - ngb).., live in [n_b, S)).  Entries past the
+// list read out of range (no memory traffic) and are never used.
 template <typename T>
 __device__ inline int entry_base(const Ctx<T>& c, int i) {
   const int ngb = c.ngb, n_list = c.n_list, S = c.S;
   const int base = i < ngb ? kBlk * i : c.kbase + kBlk * (i - ngb);
-  const int sp = c.sp_lo + kBlk * (i - n_list);
-  return i < n_list ? base : (i < n_list + c.n_sp ? sp : S);
+  return i < n_list ? base : S;
 }
 
 template <typename T>
 __device__ inline void load_entry(Stage<T>& s, const Ctx<T>& c, int i) {
-  // the choice is uniform: select the (scalar) base pointers, then build the
-  // resources, so nothing about the load becomes per-lane
-  const bool band = i < c.n_list;
   const uint32_t bytes = (uint32_t)c.S * 128u;
-  // select values, not the fields' addresses (keeps the context in registers)
-  const T* kp = c.kh;
-  const T* vp = c.vh;
-  const T* kgp = c.kgh;
-  const T* vgp = c.vgh;
-  stage_load<T>(s, make_rsrc(band ? kp : kgp, bytes), make_rsrc(band ? vp : vgp, bytes),
+  stage_load<T>(s, make_rsrc(c.kh, bytes), make_rsrc(c.vh, bytes),
                 make_rsrc(c.mask, (uint32_t)c.S * 2u), entry_base(c, i));
 }
 
 template <typename T, bool RAW>
 __device__ inline void store_entry(Slot<T>& sl, const Stage<T>& s, const Ctx<T>& c, int i) {
-  const int nb = c.nb, S = c.S, sp_lo = c.sp_lo, sp_hi = c.sp_hi;
-  const bool glob = i < c.ngb, band = i < c.n_list;
-  const int lo = glob ? 0 : (band ? nb : sp_lo);
-  const int hi = glob ? nb : (band ? S : sp_hi);
-  stage_store<T, RAW>(sl, s, entry_base(c, i), lo, hi);
+  const int nb = c.nb, S = c.S;
+  const bool glob = i < c.ngb;
+  stage_store<T, RAW>(sl, s, entry_base(c, i), glob ? 0 : nb, glob ? nb : S);
 }
 
 // ------------------------------------------------------------------ global rows
-// Key split `sp` of the global rows of (b, h): partial states into the workspace,
-// then the ticket; the workgroup that completes the ticket writes the rows.  The
-// first n_sp / 4 rounds of four blocks are already in the ring (list entries
-// n_list ..); later rounds / query blocks load theirs here.
+// Key split `sp` of the global rows of (b, h), run before the band work: rounds of
+// kWaves blocks (one per wave), then the wave states are merged in LDS and one
+// partial (m, l, o[64]) per row is published with write-through stores.  The first
+// round of the first query block arrives already loaded (`first`, issued with the
+// workgroup's first loads); the stores are waited for only at the ticket, after
+// the band work.
 template <typename T, bool RAW>
-__device__ void global_split(const AttnArgs& a, const Ctx<T>& c, int sp, Slot<T>* ring) {
+__device__ void global_split_run(const AttnArgs& a, const Ctx<T>& c, int sp, Slot<T>* ring,
+                                 const Stage<T> first[kWaves]) {
   typedef typename Frag<T>::v8 v8;
   const int t = threadIdx.x;
   const int lane = lane_id();
@@ -511,10 +494,12 @@ __device__ void global_split(const AttnArgs& a, const Ctx<T>& c, int sp, Slot<T>
     load_q<T>(qf, qgh + (size_t)(r < nb ? r : 0) * 64, r < nb);
     f32x16 o[2] = {f32x16{}, f32x16{}};
     float m_run = kNegBig, l_run = 0.0f;
-    const int n_pref = c.n_sp / kWaves;   // rounds already in the ring
     for (int u = 0; u < n_rounds; ++u) {
-      int slot = (c.n_list + kWaves * u + wave) % kRing;
-      if (qb > 0 || u >= n_pref) {
+      if (qb == 0 && u == 0) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w)
+          stage_store<T, RAW>(ring[w], first[w], k_lo + kBlk * w, k_lo, k_hi);
+      } else {
         Stage<T> st[kWaves];
 #pragma unroll
         for (int w = 0; w < kWaves; ++w)
@@ -525,10 +510,9 @@ __device__ void global_split(const AttnArgs& a, const Ctx<T>& c, int sp, Slot<T>
 #pragma unroll
         for (int w = 0; w < kWaves; ++w)
           stage_store<T, RAW>(ring[w], st[w], k_lo + kBlk * (kWaves * u + w), k_lo, k_hi);
-        __syncthreads();
-        slot = wave;
       }
-      block_step<T>(ring[slot], qf, o, m_run, l_run, c2, false, 0, 0);
+      __syncthreads();
+      block_step<T>(ring[wave], qf, o, m_run, l_run, c2, false, 0, 0);
     }
     __syncthreads();   // every wave is done with its block before the states go in
     float* stp = (float*)&ring[wave];
@@ -580,9 +564,16 @@ __device__ void global_split(const AttnArgs& a, const Ctx<T>& c, int sp, Slot<T>
     }
     __syncthreads();   // slots free again
   }
+}
 
-  // ticket: every partial store of this workgroup has completed (write-through)
-  // before the ticket is taken
+// Ticket of a split workgroup, taken after its band work: by then its partial
+// stores (write-through) have long completed.  The workgroup that completes the
+// (b, h) merges every split's partial and writes the global rows: thread per (row,
+// 4 dims); the (m, l) and o of 16 splits per round are loaded together with
+// coherent (sc1) loads, splits past n_split read out of range and get weight 0.
+template <typename T, bool RAW>
+__device__ void global_combine(const AttnArgs& a, const Ctx<T>& c) {
+  const int t = threadIdx.x;
   __shared__ int s_last;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -593,62 +584,51 @@ __device__ void global_split(const AttnArgs& a, const Ctx<T>& c, int sp, Slot<T>
   }
   __syncthreads();
   if (!s_last) return;
-  // merge every split's partial: rows in chunks, (m, l) of all (row, split) pairs
-  // into LDS, per-row weights exp2(m - M) / L, then the output dims as weighted
-  // sums.  Partials are read with coherent (sc1) loads, all of a thread's loads in
-  // flight together; splits past n_split read out of range (zeros, weight 0).
-  const int ns = a.n_split;
+  const int G = c.G, nb = c.nb, ns = a.n_split;
   const float* pbase = a.partials + (size_t)c.bh * ns * (size_t)G * kPartPitch;
   const rsrc_t rall = make_rsrc(pbase, (uint32_t)ns * G * kPartPitch * 4u);
   const int sstride = G * kPartPitch * 4;   // bytes between splits
   T* outh = (T*)a.out + (size_t)c.b * a.out_sb + (size_t)c.h * a.out_sh;
-  float* mw = (float*)ring;                        // [rows][kMaxSplit]: m, then the weight
-  float* lw = mw + kCombinePairs;                  // [rows][kMaxSplit]: l
-  constexpr int rows_per_chunk = kCombinePairs / kMaxSplit;
-  for (int r0 = 0; r0 < nb; r0 += rows_per_chunk) {
-    const int nr = min(rows_per_chunk, nb - r0);
-    for (int i = t; i < nr * kMaxSplit; i += kThreads) {
-      const int rr = r0 + i / kMaxSplit, s2 = i % kMaxSplit;
-      const u32x2 ml = __builtin_amdgcn_raw_buffer_load_b64(
-          rall, s2 < ns ? s2 * sstride + rr * kPartPitch * 4 : -1, 0, kSc1);
-      mw[i] = s2 < ns ? __uint_as_float(ml[0]) : kNegBig;
-      lw[i] = __uint_as_float(ml[1]);
-    }
-    __syncthreads();
-    for (int rr = t; rr < nr; rr += kThreads) {
-      const float* m_r = mw + rr * kMaxSplit;
-      float M = kNegBig;
-      for (int s2 = 0; s2 < kMaxSplit; ++s2) M = fmaxf(M, m_r[s2]);
-      float L = 0.0f;
-      for (int s2 = 0; s2 < kMaxSplit; ++s2) L += lw[rr * kMaxSplit + s2] * fast_exp2(m_r[s2] - M);
-      const int pos = RAW ? r0 + rr : a.gidx[(size_t)c.b * c.S + r0 + rr];
-      const float inv = mask_live<RAW>(Elem<T>::to_f(c.mask[pos])) ? 1.0f / L : 0.0f;
-      for (int s2 = 0; s2 < kMaxSplit; ++s2)
-        mw[rr * kMaxSplit + s2] = s2 < ns ? fast_exp2(m_r[s2] - M) * inv : 0.0f;
-    }
-    __syncthreads();
-    for (int idx = t; idx < nr * 16; idx += kThreads) {
-      const int rl = idx >> 4, d4 = (idx & 15) * 4;
-      const int off0 = ((r0 + rl) * kPartPitch + 4 + d4) * 4;
-      f32x4 O = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int idx = t; idx < nb * 16; idx += kThreads) {
+    const int rl = idx >> 4, d4 = (idx & 15) * 4;
+    const int off_ml = rl * kPartPitch * 4, off_o = (rl * kPartPitch + 4 + d4) * 4;
+    float M = kNegBig, L = 0.0f;
+    f32x4 O = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int h = 0; h < ns; h += 16) {
+      u32x2 ml[16];
+      u32x4 pv[16];
 #pragma unroll
-      for (int h = 0; h < kMaxSplit; h += 16) {
-        u32x4 pv[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j)
-          pv[j] = __builtin_amdgcn_raw_buffer_load_b128(
-              rall, h + j < ns ? off0 + (h + j) * sstride : -1, 0, kSc1);
-#pragma unroll
-        for (int j = 0; j < 16; ++j) O += __builtin_bit_cast(f32x4, pv[j]) * mw[rl * kMaxSplit + h + j];
+      for (int j = 0; j < 16; ++j) {
+        const bool ok = h + j < ns;
+        ml[j] = __builtin_amdgcn_raw_buffer_load_b64(rall, ok ? (h + j) * sstride + off_ml : -1, 0, kSc1);
+        pv[j] = __builtin_amdgcn_raw_buffer_load_b128(rall, ok ? (h + j) * sstride + off_o : -1, 0, kSc1);
       }
-      typename Frag<T>::v4 w;
+      float m[16];
+      float mh = M;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = Elem<T>::from_f(O[i]);
-      const int pos = RAW ? r0 + rl : a.gidx[(size_t)c.b * c.S + r0 + rl];
-      *(typename Frag<T>::v4*)(outh + (size_t)pos * a.out_ss + d4) = w;
+      for (int j = 0; j < 16; ++j) {
+        m[j] = h + j < ns ? __uint_as_float(ml[j][0]) : kNegBig;
+        mh = fmaxf(mh, m[j]);
+      }
+      const float sc = fast_exp2(M - mh);
+      L *= sc;
+      O *= sc;
+      M = mh;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float w = h + j < ns ? fast_exp2(m[j] - M) : 0.0f;
+        L += __uint_as_float(ml[j][1]) * w;
+        O += __builtin_bit_cast(f32x4, pv[j]) * w;
+      }
     }
-    __syncthreads();
+    const int pos = RAW ? rl : a.gidx[(size_t)c.b * c.S + rl];
+    const float inv = mask_live<RAW>(Elem<T>::to_f(c.mask[pos])) ? 1.0f / L : 0.0f;
+    typename Frag<T>::v4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = Elem<T>::from_f(O[i] * inv);
+    *(typename Frag<T>::v4*)(outh + (size_t)pos * a.out_ss + d4) = w;
   }
+  __syncthreads();
   if (t == 0) __hip_atomic_store(a.counters + c.bh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -790,8 +770,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   c.mask = (const T*)(RAW ? a.local_mask : a.bias) + (size_t)c.b * c.S;
   const float c2 = a.scale * kLog2e;
   const bool split = a.G > 0 && c.tile < a.n_split;
-  const int sp_blocks = a.split_len / kBlk;
-  c.n_sp = split ? (sp_blocks < kSpPref ? sp_blocks : kSpPref) : 0;
+
   c.sp_lo = split ? c.tile * a.split_len : 0;
   c.sp_hi = split ? min(c.S, c.sp_lo + a.split_len) : 0;
   c.kh = (const T*)a.k + head;
@@ -799,7 +778,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   c.kgh = split ? (const T*)a.kg + head : c.kh;
   c.vgh = split ? (const T*)a.vg + head : c.vh;
 
-  // every load the prologue needs is issued before anything waits
+  // every load the prologue needs is issued before anything waits: the first round
+  // of the global-row split (split tiles), the first ring entries, Q, the register
+  // sets
+  Stage<T> spl[kWaves];
+  if (split) {
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+      stage_load<T>(spl[w], make_rsrc(c.kgh, (uint32_t)c.S * 128u),
+                    make_rsrc(c.vgh, (uint32_t)c.S * 128u), make_rsrc(c.mask, (uint32_t)c.S * 2u),
+                    c.sp_lo + kBlk * w);
+  }
   Stage<T> pro[kAhead];
 #pragma unroll
   for (int i = 0; i < kAhead; ++i) load_entry<T>(pro[i], c, i);
@@ -817,6 +806,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     __builtin_amdgcn_sched_barrier(0);
   }
   c.nb = count_globals<T, RAW>(a, c.b);
+  // the split of the global rows first: its loads were issued first, and its
+  // results are waited for only at the ticket, after the band work
+  if (split && c.nb > 0) global_split_run<T, RAW>(a, c, c.tile, ring, spl);
 
 #pragma unroll
   for (int i = 0; i < kAhead; ++i) store_entry<T, RAW>(ring[i], pro[i], c, i);
@@ -846,14 +838,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
                       kf, vf, pf);
   }
   pv_frag<T>(vf, pf, o);   // PV of the last block (its V^T was read by the last step)
-  // drain: stage the split's prefetched blocks still in registers (in pairs; at most
-  // one extra entry, out of range, lands in a slot nobody reads any more)
-  const int n_drain = c.n_list + c.n_sp - (n_steps + kAhead);
-  for (int t0 = n_steps; t0 < n_steps + n_drain; t0 += 2) {
-    stage_step<T, RAW>(c, ring, t0, st[s0i]);
-    stage_step<T, RAW>(c, ring, t0 + 1, st[s1i]);
-  }
-  __syncthreads();
 
   // epilogue: normalise and store the local rows
   {
@@ -876,7 +860,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   }
 
-  if (split && c.nb > 0) global_split<T, RAW>(a, c, c.tile, ring);
+  if (split && c.nb > 0) global_combine<T, RAW>(a, c);
 }
 
 template <typename T>
