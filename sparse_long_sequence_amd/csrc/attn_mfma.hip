@@ -19,23 +19,23 @@
 // Band workgroup: 8 waves = 256 query rows of one (b, h), two waves per SIMD (one
 // wave's vector work overlaps the other's matrix work).  Wave w owns the 32 rows
 // r0 + 64 (w % 4) + 32 (w / 4) ..: row group w % 4, sub-block w / 4.  Keys move in
-// blocks of 32 rows (K row-major, V transposed, plus a per-key 0 / -inf term)
-// through a 10-slot LDS ring.  The key list of a workgroup is
-//     [ceil(G/32) global-key blocks][band blocks 0 .. nband+6]
-// where band block j holds keys r0 - W/2 + 32j ..; row group rg needs band blocks
-// 2rg .. 2rg + nband (nband = (W + 63) / 32).  At step t every wave reads entry t
-// (global phase) or t + 2rg (band phase: the row groups walk the band on a
-// diagonal, so none of them idles); entry t + 9 is written into the ring from
-// registers and the loads of entry t + 11 are issued.  One barrier per step.
+// entries of 64 (two 32-key blocks; K row-major, V transposed, plus a per-key
+// 0 / -inf term) through an 8-slot LDS ring.  The entry list of a workgroup is
+//     [ceil(G/64) global-key entries][band entries 0 .. npb+2]
+// where band entry j holds keys r0 - W/2 + 64j ..; row group rg needs band blocks
+// 2rg .. 2rg + nband (nband = (W + 63) / 32), i.e. band entries rg .. rg + npb - 1.
+// At step t every wave reads entry t (global phase) or t + rg (band phase: the row
+// groups walk the band on a diagonal, so none of them idles); entry t + 7 is written
+// into the ring from registers and the loads of entry t + 9 are issued.  One
+// barrier per step, i.e. per 64 keys.
 //
-// Per block and wave: S^T = K Q^T (4 x v_mfma_f32_32x32x16, accumulator initialised
-// with the per-key term, so dead keys cost no vector work), so each lane holds 16
-// scores of ONE query (lanes n and n + 32 share a query); the running max is kept in
-// scaled log2 units and only moved when it grows by more than 8 (then p <= 2^8,
-// exact range for fp16 / bf16), so rescaling the accumulators is rare; P is rounded
-// to the input type, its row sum is taken from the rounded values (v_dot2), and
-// O^T += V^T P^T (4 more MFMAs) runs one step later, next to the QK^T of the
-// following block, while the vector ALUs work on the softmax.
+// Per 32-key block and wave: S^T = K Q^T (4 x v_mfma_f32_32x32x16, accumulator
+// initialised with the per-key term, so dead keys cost no vector work), so each
+// lane holds 16 scores of ONE query (lanes n and n + 32 share a query).  The
+// running max is kept in scaled log2 units, updated once per 64 keys and only moved
+// when it grows by more than 8 (then p <= 2^8, exact range for fp16 / bf16), so
+// rescaling the accumulators is rare; P is rounded to the input type, its row sum
+// is taken from the rounded values (v_dot2), then O^T += V^T P^T (4 more MFMAs).
 //
 // Global rows (r < n_b) attend to all live keys through kg / vg.  The first
 // n_split tiles of each (b, h) also take one key split of those rows (split_len
@@ -56,11 +56,12 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsW = 32;           // query rows per wave
 constexpr int kTile = kRowsW * kWaves;  // query rows per workgroup
-constexpr int kBlk = 32;             // keys per block
+constexpr int kBlk = 32;             // keys per MFMA block
+constexpr int kEnt = 64;             // keys per ring entry (two blocks)
 constexpr int kKld = 72;             // LDS row pitch of K (elements): 144 B, conflict-free reads
-constexpr int kVld = 40;             // LDS row pitch of V^T (elements): 80 B, 16-B aligned rows
-constexpr int kRing = 10;            // LDS block slots
-constexpr int kAhead = 9;            // entry t + kAhead is written at step t
+constexpr int kVld = 72;             // LDS row pitch of V^T (elements): 144 B, conflict-free reads
+constexpr int kRing = 8;             // LDS entry slots
+constexpr int kAhead = 7;            // entry t + kAhead is written at step t
 constexpr int kDepth = 2;            // register sets of loads in flight
 constexpr int kStPitch = 67;         // floats per row of a wave state in LDS: m, l, o[64], pad
 constexpr int kMaxSplit = 32;        // at most this many key splits per (b, h)
@@ -71,14 +72,13 @@ constexpr float kLazy = 8.0f;        // move the max only when it grows by more 
 
 template <typename T>
 struct Slot {
-  T k[kBlk * kKld];     // K rows of the block
-  T vt[64 * kVld];      // V^T: row d holds the 32 keys of the block
-  float bias2[kBlk];    // 0 for a live key, -inf for an empty / excluded / padded slot
-  int flag;             // 0: every key live, 1: some, 2: none
-  int pad[3];
+  T k[kEnt * kKld];     // K rows of the entry
+  T vt[64 * kVld];      // V^T: row d holds the 64 keys of the entry
+  float bias2[kEnt];    // 0 for a live key, -inf for an empty / excluded / padded slot
 };
 
 static_assert(32 * kStPitch * 4 <= sizeof(Slot<_Float16>), "a wave state fits in one slot");
+static_assert(kRing >= kWaves, "the split merges one wave state per slot");
 
 template <typename T>
 struct Frag {
@@ -104,17 +104,17 @@ __device__ inline bool mask_live(float x) {
   return RAW ? x == 1.0f : x == 0.0f;
 }
 
-// Thread t stages K row t/16 (8 B at column 4*(t%16)), dims 2*(t%32) .. +1 of the
-// key pair 2*(t/32), 2*(t/32)+1 of V (4 B each) and, for t < 32, the mask value of
-// key slot t.  Every thread does the same work; no branch.
+// Thread t stages 16 B of K row t/8 (column 8*(t%8)), dims 4*(t%16) .. +3 of the key
+// pair 2*(t/16), 2*(t/16)+1 of V (8 B each) and, for t < 64, the mask value of key
+// slot t.  Every thread does the same work; no branch.
 template <typename T>
 struct Stage {
-  u32x2 k;
-  uint32_t v0, v1;
+  u32x4 k;
+  u32x2 v0, v1;
   unsigned short mask_bits;
 };
 
-// Block of keys base .. base + 31.  Every thread issues the same four loads, so the
+// Entry of keys base .. base + 63.  Every thread issues the same four loads, so the
 // compiler can keep later entries in flight while it waits for this one.  K / V
 // rows are loaded for every in-range key (a dead key's score is masked to -inf, so
 // its data never matters).
@@ -122,39 +122,40 @@ template <typename T>
 __device__ inline void stage_load(Stage<T>& s, rsrc_t rk, rsrc_t rv, rsrc_t rm, int base) {
   const int t = threadIdx.x;
   const int b128 = base * 128;
-  const int voff = (t >> 5) * 256 + 4 * (t & 31);
-  s.k = __builtin_amdgcn_raw_buffer_load_b64(rk, b128 + (t >> 4) * 128 + 8 * (t & 15), 0, 0);
-  s.v0 = __builtin_amdgcn_raw_buffer_load_b32(rv, b128 + voff, 0, 0);
-  s.v1 = __builtin_amdgcn_raw_buffer_load_b32(rv, b128 + voff + 128, 0, 0);
-  s.mask_bits = __builtin_amdgcn_raw_buffer_load_b16(rm, t < kBlk ? 2 * (base + t) : -1, 0, 0);
+  const int voff = (t >> 4) * 256 + 8 * (t & 15);
+  s.k = __builtin_amdgcn_raw_buffer_load_b128(rk, b128 + (t >> 3) * 128 + 16 * (t & 7), 0, 0);
+  s.v0 = __builtin_amdgcn_raw_buffer_load_b64(rv, b128 + voff, 0, 0);
+  s.v1 = __builtin_amdgcn_raw_buffer_load_b64(rv, b128 + voff + 128, 0, 0);
+  s.mask_bits = __builtin_amdgcn_raw_buffer_load_b16(rm, t < kEnt ? 2 * (base + t) : -1, 0, 0);
 }
 
-// Position of key kk (0..31) inside a V^T row: within each 16-key half, lane group g
-// of the PV MFMA needs keys 4g .. 4g+3 and 8+4g .. 8+4g+3 (the row order of the
+// Position of key kk (0..63) inside a V^T row: within each 16-key group, lane group
+// g of the PV MFMA needs keys 4g .. 4g+3 and 8+4g .. 8+4g+3 (the row order of the
 // score fragment), so those eight are stored together and read as 16 bytes.
 __device__ inline int vt_pos(int kk) {
-  return (kk & 16) + (kk & 3) + 4 * ((kk >> 3) & 1) + 8 * ((kk >> 2) & 1);
+  return (kk & 48) + (kk & 3) + 4 * ((kk >> 3) & 1) + 8 * ((kk >> 2) & 1);
 }
 
-// Write a staged block; key base + j is live iff lo <= key < hi and its mask says so.
+// Write a staged entry; key base + j is live iff lo <= key < hi and its mask says so.
 template <typename T, bool RAW>
 __device__ inline void stage_store(Slot<T>& sl, const Stage<T>& s, int base, int lo, int hi) {
   const int t = threadIdx.x;
-  *(u32x2*)&sl.k[(t >> 4) * kKld + 4 * (t & 15)] = s.k;
-  // dims 2c, 2c+1 of keys 2vp, 2vp+1 -> V^T rows 2c, 2c+1, one dword (a key pair) each
-  const int vp = t >> 5, cc = t & 31;
+  *(u32x4*)&sl.k[(t >> 3) * kKld + 8 * (t & 7)] = s.k;
+  // dims 4c .. 4c+3 of keys 2vp, 2vp+1 -> V^T rows 4c .. 4c+3, one dword (a key pair)
+  // each
+  const int vp = t >> 4, cc = t & 15;
   uint32_t* vt = (uint32_t*)sl.vt + vt_pos(2 * vp) / 2;
   constexpr int P = kVld / 2;   // pitch in dwords
-  vt[(2 * cc) * P] = __builtin_amdgcn_perm(s.v1, s.v0, 0x05040100u);
-  vt[(2 * cc + 1) * P] = __builtin_amdgcn_perm(s.v1, s.v0, 0x07060302u);
+  vt[(4 * cc + 0) * P] = __builtin_amdgcn_perm(s.v1[0], s.v0[0], 0x05040100u);
+  vt[(4 * cc + 1) * P] = __builtin_amdgcn_perm(s.v1[0], s.v0[0], 0x07060302u);
+  vt[(4 * cc + 2) * P] = __builtin_amdgcn_perm(s.v1[1], s.v0[1], 0x05040100u);
+  vt[(4 * cc + 3) * P] = __builtin_amdgcn_perm(s.v1[1], s.v0[1], 0x07060302u);
   if (wave_id() == 0) {
     const int lane = lane_id();
     const int key = base + lane;
-    const bool live = lane < kBlk && key >= lo && key < hi &&
+    const bool live = key >= lo && key < hi &&
                       mask_live<RAW>(Elem<T>::to_f(__builtin_bit_cast(T, s.mask_bits)));
-    const uint64_t bal = __ballot(live);
-    if (lane < kBlk) sl.bias2[lane] = live ? 0.0f : -INFINITY;
-    if (lane == 0) sl.flag = bal == 0xffffffffull ? 0 : (bal == 0ull ? 2 : 1);
+    sl.bias2[lane] = live ? 0.0f : -INFINITY;
   }
 }
 
@@ -180,10 +181,10 @@ __device__ inline typename Frag<T>::v2 cvt_pair(float a, float b) {
   return __builtin_convertvector(x, typename Frag<T>::v2);
 }
 
-// Operand fragments of one 32-key block, read from LDS.  K: A operand of
-// S^T = K Q^T (lane (n, g) holds key n, dims 16t + 8g ..); V^T: A operand of
-// O^T += V^T P^T (lane holds dim 32mb + n, keys 16h + 4g .. +3 and 16h + 8 + 4g ..,
-// stored side by side).
+// Operand fragments of 32-key block j of an entry, read from LDS.  K: A operand of
+// S^T = K Q^T (lane (n, g) holds key 32j + n, dims 16t + 8g ..); V^T: A operand of
+// O^T += V^T P^T (lane holds dim 32mb + n, keys 32j + 16h + 4g .. +3 and
+// 32j + 16h + 8 + 4g .., stored side by side).
 template <typename T>
 struct KFrag {
   typename Frag<T>::v8 a[4];
@@ -194,16 +195,16 @@ struct VFrag {
 };
 
 template <typename T>
-__device__ inline void read_k(KFrag<T>& f, const Slot<T>& sl) {
+__device__ inline void read_k(KFrag<T>& f, const Slot<T>& sl, int j) {
   typedef typename Frag<T>::v8 v8;
   const int lane = lane_id();
   const int n = lane & 31, g = lane >> 5;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) f.a[t] = *(const v8*)&sl.k[n * kKld + 16 * t + 8 * g];
+  for (int t = 0; t < 4; ++t) f.a[t] = *(const v8*)&sl.k[(kBlk * j + n) * kKld + 16 * t + 8 * g];
 }
 
 template <typename T>
-__device__ inline void read_v(VFrag<T>& f, const Slot<T>& sl) {
+__device__ inline void read_v(VFrag<T>& f, const Slot<T>& sl, int j) {
   typedef typename Frag<T>::v8 v8;
   const int lane = lane_id();
   const int n = lane & 31, g = lane >> 5;
@@ -211,21 +212,27 @@ __device__ inline void read_v(VFrag<T>& f, const Slot<T>& sl) {
   for (int h = 0; h < 2; ++h) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
-      f.a[h][mb] = *(const v8*)(sl.vt + (32 * mb + n) * kVld + 16 * h + 8 * g);
+      f.a[h][mb] = *(const v8*)(sl.vt + (32 * mb + n) * kVld + kBlk * j + 16 * h + 8 * g);
   }
 }
 
-// S^T of one block for the wave's 32 queries (4 MFMAs).
+// Per-key term of block j in the accumulator layout (lane (n, g), v -> key
+// 32j + 8 (v / 4) + 4 g + v % 4).
 template <typename T>
-__device__ inline f32x16 qk_frag(const KFrag<T>& kf, const typename Frag<T>::v8 qf[4]) {
-  f32x16 s = f32x16{};
+__device__ inline f32x16 read_bias(const Slot<T>& sl, int j) {
+  const int g = lane_id() >> 5;
+  f32x16 c;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) s = mfma32(kf.a[t], qf[t], s);
-  return s;
+  for (int jj = 0; jj < 4; ++jj) {
+    const f32x4 bb = *(const f32x4*)&sl.bias2[kBlk * j + 8 * jj + 4 * g];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[4 * jj + i] = bb[i];
+  }
+  return c;
 }
 
 // S^T of one block plus the per-key term (0 / -inf) as accumulator init: dead keys
-// come out at -inf with no vector-ALU work.
+// come out at -inf with no vector-ALU work (4 MFMAs).
 template <typename T>
 __device__ inline f32x16 qk_frag_c(const KFrag<T>& kf, const typename Frag<T>::v8 qf[4],
                                    const f32x16& c) {
@@ -233,21 +240,6 @@ __device__ inline f32x16 qk_frag_c(const KFrag<T>& kf, const typename Frag<T>::v
 #pragma unroll
   for (int t = 0; t < 4; ++t) s = mfma32(kf.a[t], qf[t], s);
   return s;
-}
-
-// Per-key term of a block in the accumulator layout (lane (n, g), v -> key
-// 8 (v / 4) + 4 g + v % 4).
-template <typename T>
-__device__ inline f32x16 read_bias(const Slot<T>& sl) {
-  const int g = lane_id() >> 5;
-  f32x16 c;
-#pragma unroll
-  for (int jj = 0; jj < 4; ++jj) {
-    const f32x4 bb = *(const f32x4*)&sl.bias2[8 * jj + 4 * g];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) c[4 * jj + i] = bb[i];
-  }
-  return c;
 }
 
 // O^T += V^T P^T (4 MFMAs).
@@ -260,119 +252,31 @@ __device__ inline void pv_frag(const VFrag<T>& vf, const typename Frag<T>::v8 pf
   }
 }
 
-// Online-softmax update with the scores s of one block; returns the P^T operand.
-// flag (uniform): 0 every key live, else add the per-key 0 / -inf term of `sl`.
-// band (uniform): apply |j - s| <= W/2 with c = band_c + 8*(v/4) + (v%4) in 0..W.
-// Every block runs the same code on the accumulators (a block without a live key
-// adds exact zeros), so the only branch that touches them is the rare rescale.
-template <typename T>
-__device__ inline void softmax_p(const Slot<T>& sl, const f32x16& s, int flag, f32x16 o[2],
-                                 float& m_run, float& l_run, float c2, bool band, int band_c,
-                                 int W, typename Frag<T>::v8 pf[2]) {
-  typedef typename Frag<T>::v2 v2;
+// Row max of 16 scores (NaN-propagating maximum: no operand canonicalisation; the
+// scores are never NaN).
+__device__ inline float max16(const f32x16& s) {
+  float m5[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) m5[i] = vmax(vmax(s[3 * i], s[3 * i + 1]), s[3 * i + 2]);
+  const float mx = vmax(vmax(m5[0], m5[1]), vmax(m5[2], s[15]));
+  return vmax(vmax(mx, m5[3]), m5[4]);
+}
+
+// Band mask of block tq of a sub-block: key kk of the block and query n are within
+// the window iff c = 32 tq + kk - n lies in 0 .. W (lane (n, g), v -> kk =
+// 8 (v / 4) + 4 g + v % 4).
+__device__ inline void band_mask(f32x16& s, int tq, int W) {
   const int lane = lane_id();
-  const int g = lane >> 5;
-  float x[16];
+  const int band_c = kBlk * tq + 4 * (lane >> 5) - (lane & 31);
 #pragma unroll
-  for (int v = 0; v < 16; ++v) x[v] = s[v];
-  if (flag) {
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const f32x4 bb = *(const f32x4*)&sl.bias2[8 * jj + 4 * g];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[4 * jj + i] += bb[i];
-    }
+  for (int v = 0; v < 16; ++v) {
+    const int cc = band_c + 8 * (v >> 2) + (v & 3);
+    s[v] = (unsigned)cc <= (unsigned)W ? s[v] : -INFINITY;
   }
-  if (band) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int c = band_c + 8 * (v >> 2) + (v & 3);
-      x[v] = (unsigned)c <= (unsigned)W ? x[v] : -INFINITY;
-    }
-  }
-  // max as a tree of three-input maxima (NaN-propagating maximum: no operand
-  // canonicalisation, the scores are never NaN)
-  float m5[5];
-#pragma unroll
-  for (int i = 0; i < 5; ++i) m5[i] = vmax(vmax(x[3 * i], x[3 * i + 1]), x[3 * i + 2]);
-  float mx = vmax(vmax(m5[0], m5[1]), vmax(m5[2], x[15]));
-  mx = vmax(vmax(mx, m5[3]), m5[4]);
-  mx = cross_half_max(mx);
-  const float ms = mx * c2;
-  const bool need = ms > m_run + kLazy;
-  if (__builtin_expect(__ballot(need) != 0ull, 0)) {
-    const float m_new = need ? ms : m_run;
-    const float alpha = fast_exp2(m_run - m_new);
-    l_run *= alpha;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      o[0][v] *= alpha;
-      o[1][v] *= alpha;
-    }
-    m_run = m_new;
-  }
-  float ls[2] = {0.0f, 0.0f};   // two independent row-sum chains
-#pragma unroll
-  for (int h2 = 0; h2 < 2; ++h2) {
-#pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      const float p0 = fast_exp2(fmaf(x[8 * h2 + e], c2, -m_run));
-      const float p1 = fast_exp2(fmaf(x[8 * h2 + e + 1], c2, -m_run));
-      const v2 pp = cvt_pair<T>(p0, p1);
-      pf[h2][e] = pp[0];
-      pf[h2][e + 1] = pp[1];
-      ls[h2] = dot2_ones(pp, ls[h2]);
-    }
-  }
-  l_run += ls[0] + ls[1];
 }
 
-// Two-phase form of the same update for the band loop, where PV of the previous
-// block is still pending when the scores of this one arrive.
-// Phase 1: masking (only where `MASKED`) and the scaled row max of one sub-block.
-template <typename T, bool MASKED>
-__device__ __forceinline__ float masked_max(const Slot<T>& sl, const f32x16& s, int flag, bool band,
-                                            int band_c, int W, float c2, float x[16]) {
-  const int g = lane_id() >> 5;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) x[v] = s[v];
-  if (MASKED) {
-    if (flag) {
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const f32x4 bb = *(const f32x4*)&sl.bias2[8 * jj + 4 * g];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[4 * jj + i] += bb[i];
-      }
-    }
-    if (band) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int c = band_c + 8 * (v >> 2) + (v & 3);
-        x[v] = (unsigned)c <= (unsigned)W ? x[v] : -INFINITY;
-      }
-    }
-  }
-  float m5[5];
-#pragma unroll
-  for (int i = 0; i < 5; ++i) m5[i] = vmax(vmax(x[3 * i], x[3 * i + 1]), x[3 * i + 2]);
-  float mx = vmax(vmax(m5[0], m5[1]), vmax(m5[2], x[15]));
-  mx = vmax(vmax(mx, m5[3]), m5[4]);
-  return cross_half_max(mx) * c2;
-}
-
-// Rare path: the max of some row grew by more than kLazy.  The pending PV of the
-// previous block (made with the old max) is added first, then the accumulators
-// are rescaled and the pending P cleared, so the unconditional PV that follows
-// adds zeros.
-template <typename T>
-__device__ __forceinline__ void rescale_pending(const VFrag<T>& vf, float ms,
-                                                typename Frag<T>::v8 pf[2], f32x16 o[2],
-                                                float& m_run, float& l_run) {
-  typedef typename Frag<T>::v8 v8;
-  pv_frag<T>(vf, pf, o);
-  pf[0] = v8{};
-  pf[1] = v8{};
+// Rare path: the scaled row max ms grew by more than kLazy over m_run.
+__device__ inline void rescale(float ms, f32x16 o[2], float& m_run, float& l_run) {
   const float m_new = ms > m_run + kLazy ? ms : m_run;
   const float alpha = fast_exp2(m_run - m_new);
   l_run *= alpha;
@@ -384,18 +288,18 @@ __device__ __forceinline__ void rescale_pending(const VFrag<T>& vf, float ms,
   m_run = m_new;
 }
 
-// Phase 2: P = exp2(c2 x - m), rounded to T, and its row sum.
+// P = exp2(c2 s - m), rounded to T, and its row sum.
 template <typename T>
-__device__ __forceinline__ void exp_p(const float x[16], float m_run, float c2, float& l_run,
-                                      typename Frag<T>::v8 pf[2]) {
+__device__ inline void exp_p(const f32x16& s, float m_run, float c2, float& l_run,
+                             typename Frag<T>::v8 pf[2]) {
   typedef typename Frag<T>::v2 v2;
   float ls[2] = {0.0f, 0.0f};
 #pragma unroll
   for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      const float p0 = fast_exp2(fmaf(x[8 * h2 + e], c2, -m_run));
-      const float p1 = fast_exp2(fmaf(x[8 * h2 + e + 1], c2, -m_run));
+      const float p0 = fast_exp2(fmaf(s[8 * h2 + e], c2, -m_run));
+      const float p1 = fast_exp2(fmaf(s[8 * h2 + e + 1], c2, -m_run));
       const v2 pp = cvt_pair<T>(p0, p1);
       pf[h2][e] = pp[0];
       pf[h2][e + 1] = pp[1];
@@ -405,20 +309,20 @@ __device__ __forceinline__ void exp_p(const float x[16], float m_run, float c2, 
   l_run += ls[0] + ls[1];
 }
 
-// One whole block (used where there is nothing to overlap it with).
+// One whole 32-key block (the global-row split: nothing to overlap it with).
 template <typename T>
-__device__ inline void block_step(const Slot<T>& sl, const typename Frag<T>::v8 qf[4],
-                                  f32x16 o[2], float& m_run, float& l_run, float c2, bool band,
-                                  int band_c, int W) {
+__device__ inline void block_step(const Slot<T>& sl, int j, const typename Frag<T>::v8 qf[4],
+                                  f32x16 o[2], float& m_run, float& l_run, float c2) {
   typedef typename Frag<T>::v8 v8;
-  const int flag = __builtin_amdgcn_readfirstlane(sl.flag);
   KFrag<T> kf;
-  read_k<T>(kf, sl);
-  const f32x16 s = qk_frag<T>(kf, qf);
+  read_k<T>(kf, sl, j);
+  const f32x16 s = qk_frag_c<T>(kf, qf, read_bias<T>(sl, j));
   VFrag<T> vf;
-  read_v<T>(vf, sl);
+  read_v<T>(vf, sl, j);
+  const float ms = cross_half_max(max16(s)) * c2;
+  if (__builtin_expect(__ballot(ms > m_run + kLazy) != 0ull, 0)) rescale(ms, o, m_run, l_run);
   v8 pf[2];
-  softmax_p<T>(sl, s, flag, o, m_run, l_run, c2, band, band_c, W, pf);
+  exp_p<T>(s, m_run, c2, l_run, pf);
   pv_frag<T>(vf, pf, o);
 }
 
@@ -433,21 +337,21 @@ __device__ inline void load_q(typename Frag<T>::v8 qf[4], const T* __restrict__ 
 // ------------------------------------------------------------------ workgroup context
 template <typename T>
 struct Ctx {
-  int b, h, bh, tile, S, W, G, nb, ngb, r0, kbase, n_list;
+  int b, h, bh, tile, S, W, G, nb, ngp, r0, kbase, n_list;
   int sp_lo, sp_hi;          // key range of the split
   const T *kh, *vh;          // k, v of this head
   const T *kgh, *vgh;        // kg, vg of this head (split tiles; else k, v)
   const T* mask;             // that mask row (raw local mask, or the shifted one)
 };
 
-// List entry i: global-key block i (positions 32i.., live below n_b; under the
+// List entry i: global-key entry i (positions 64i.., live below n_b; under the
 // head-of-sequence precondition the global positions are 0 .. n_b - 1) or band
-// block i - ngb (keys kbase + 32(i - ngb).., live in [n_b, S)).  Entries past the
+// entry i - ngp (keys kbase + 64(i - ngp).., live in [n_b, S)).  Entries past the
 // list read out of range (no memory traffic) and are never used.
 template <typename T>
 __device__ inline int entry_base(const Ctx<T>& c, int i) {
-  const int ngb = c.ngb, n_list = c.n_list, S = c.S;
-  const int base = i < ngb ? kBlk * i : c.kbase + kBlk * (i - ngb);
+  const int ngp = c.ngp, n_list = c.n_list, S = c.S;
+  const int base = i < ngp ? kEnt * i : c.kbase + kEnt * (i - ngp);
   return i < n_list ? base : S;
 }
 
@@ -461,20 +365,22 @@ __device__ inline void load_entry(Stage<T>& s, const Ctx<T>& c, int i) {
 template <typename T, bool RAW>
 __device__ inline void store_entry(Slot<T>& sl, const Stage<T>& s, const Ctx<T>& c, int i) {
   const int nb = c.nb, S = c.S;
-  const bool glob = i < c.ngb;
+  const bool glob = i < c.ngp;
   stage_store<T, RAW>(sl, s, entry_base(c, i), glob ? 0 : nb, glob ? nb : S);
 }
 
 // ------------------------------------------------------------------ global rows
 // Key split `sp` of the global rows of (b, h), run before the band work: rounds of
-// kWaves blocks (one per wave), then the wave states are merged in LDS and one
-// partial (m, l, o[64]) per row is published with write-through stores.  The first
-// round of the first query block arrives already loaded (`first`, issued with the
-// workgroup's first loads); the stores are waited for only at the ticket, after
-// the band work.
+// kWaves blocks (one per wave, four entries), then the wave states are merged in
+// LDS and one partial (m, l, o[64]) per row is published with write-through
+// stores.  The first round of the first query block arrives already loaded
+// (`first`, issued with the workgroup's first loads); the stores are waited for
+// only at the ticket, after the band work.
+constexpr int kSplitEnt = kWaves * kBlk / kEnt;   // entries per round
+
 template <typename T, bool RAW>
 __device__ void global_split_run(const AttnArgs& a, const Ctx<T>& c, int sp, Slot<T>* ring,
-                                 const Stage<T> first[kWaves]) {
+                                 const Stage<T> first[kSplitEnt]) {
   typedef typename Frag<T>::v8 v8;
   const int t = threadIdx.x;
   const int lane = lane_id();
@@ -495,24 +401,25 @@ __device__ void global_split_run(const AttnArgs& a, const Ctx<T>& c, int sp, Slo
     f32x16 o[2] = {f32x16{}, f32x16{}};
     float m_run = kNegBig, l_run = 0.0f;
     for (int u = 0; u < n_rounds; ++u) {
+      const int base = k_lo + kBlk * kWaves * u;
       if (qb == 0 && u == 0) {
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w)
-          stage_store<T, RAW>(ring[w], first[w], k_lo + kBlk * w, k_lo, k_hi);
+        for (int e = 0; e < kSplitEnt; ++e)
+          stage_store<T, RAW>(ring[e], first[e], base + kEnt * e, k_lo, k_hi);
       } else {
-        Stage<T> st[kWaves];
+        Stage<T> st[kSplitEnt];
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w)
-          stage_load<T>(st[w], make_rsrc(c.kgh, (uint32_t)c.S * 128u),
+        for (int e = 0; e < kSplitEnt; ++e)
+          stage_load<T>(st[e], make_rsrc(c.kgh, (uint32_t)c.S * 128u),
                         make_rsrc(c.vgh, (uint32_t)c.S * 128u), make_rsrc(c.mask, (uint32_t)c.S * 2u),
-                        k_lo + kBlk * (kWaves * u + w));
+                        base + kEnt * e);
         __syncthreads();   // earlier readers of the slots are done
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w)
-          stage_store<T, RAW>(ring[w], st[w], k_lo + kBlk * (kWaves * u + w), k_lo, k_hi);
+        for (int e = 0; e < kSplitEnt; ++e)
+          stage_store<T, RAW>(ring[e], st[e], base + kEnt * e, k_lo, k_hi);
       }
       __syncthreads();
-      block_step<T>(ring[wave], qf, o, m_run, l_run, c2, false, 0, 0);
+      block_step<T>(ring[wave >> 1], wave & 1, qf, o, m_run, l_run, c2);
     }
     __syncthreads();   // every wave is done with its block before the states go in
     float* stp = (float*)&ring[wave];
@@ -633,13 +540,12 @@ __device__ void global_combine(const AttnArgs& a, const Ctx<T>& c) {
 }
 
 // ------------------------------------------------------------------ band work
-// Wave w owns the 32 rows r0 + 64 (w % 4) + 32 (w / 4) ..: row group w % 4, sub-block
-// w / 4.  Entry of row group rg at step t: global phase entry t, band phase entry
-// t + 2 rg (row group rg's first band block is 2rg: its 64 rows start 64 rg after the
+// Entry of row group rg at step t: global phase entry t, band phase entry t + rg
+// (row group rg's first band block is 2rg: its 64 rows start 64 rg after the
 // tile's).
 template <typename T>
 __device__ inline int wave_entry(const Ctx<T>& c, int t, int rg) {
-  return t < c.ngb ? t : t + 2 * rg;
+  return t < c.ngp ? t : t + rg;
 }
 
 __device__ inline int xcd_remap(int i, int n) {
@@ -669,70 +575,48 @@ __device__ inline int count_globals(const AttnArgs& a, int b) {
   return s_cnt;
 }
 
-// Staging only: write entry t + kAhead into the ring, load entry t + kAhead + kDepth.
+// One step t of a wave: the two 32-key blocks of its entry.  LDS reads first
+// (K, V^T and per-key terms of both blocks), then QK^T, the band mask on edge
+// steps only, one running-max update for the 64 keys, P, PV, then the staging of
+// entry t + kAhead and the loads of entry t + kAhead + kDepth, then the barrier.
+// Entries t .. t + 3 are read during the step and t + 7 is written, into the slot
+// of entry t - 1.
 template <typename T, bool RAW>
-__device__ __forceinline__ void stage_step(const Ctx<T>& c, Slot<T>* ring, int tt, Stage<T>& set) {
+__device__ __forceinline__ void band_step(const Ctx<T>& c, Slot<T>* ring, int tt, int rg, int sb,
+                                          float c2, Stage<T>& set,
+                                          const typename Frag<T>::v8 qf[4], f32x16 o[2],
+                                          float& m_run, float& l_run) {
+  typedef typename Frag<T>::v8 v8;
+  const Slot<T>& cs = ring[wave_entry(c, tt, rg) % kRing];
+  KFrag<T> kf0, kf1;
+  read_k<T>(kf0, cs, 0);
+  read_k<T>(kf1, cs, 1);
+  const f32x16 c0 = read_bias<T>(cs, 0), c1 = read_bias<T>(cs, 1);
+  VFrag<T> vf0, vf1;
+  read_v<T>(vf0, cs, 0);
+  read_v<T>(vf1, cs, 1);
+  f32x16 s0 = qk_frag_c<T>(kf0, qf, c0);
+  f32x16 s1 = qk_frag_c<T>(kf1, qf, c1);
+  // blocks tq = 1 .. (W - 31) / 32 of a sub-block lie wholly inside the window of
+  // every row; the others get the band mask
+  const int tq0 = 2 * (tt - c.ngp) - sb;
+  const bool inner0 = tq0 >= 1 && kBlk * tq0 + kBlk - 1 <= c.W;
+  const bool inner1 = tq0 + 1 >= 1 && kBlk * (tq0 + 1) + kBlk - 1 <= c.W;
+  if (tt >= c.ngp && !(inner0 && inner1)) {
+    band_mask(s0, tq0, c.W);
+    band_mask(s1, tq0 + 1, c.W);
+  }
+  const float ms = cross_half_max(vmax(max16(s0), max16(s1))) * c2;
+  if (__builtin_expect(__ballot(ms > m_run + kLazy) != 0ull, 0)) rescale(ms, o, m_run, l_run);
+  v8 p0[2], p1[2];
+  exp_p<T>(s0, m_run, c2, l_run, p0);
+  exp_p<T>(s1, m_run, c2, l_run, p1);
+  pv_frag<T>(vf0, p0, o);
+  pv_frag<T>(vf1, p1, o);
   const int e = tt + kAhead;
   store_entry<T, RAW>(ring[e % kRing], set, c, e);
   __builtin_amdgcn_sched_barrier(0);
   load_entry<T>(set, c, e + kDepth);
-}
-
-// One step t of a wave.  On entry the wave holds the scores of block t (dead keys
-// already at -inf), the K fragment and per-key term of block t + 1, and the V^T
-// fragment and P of block t - 1.  The matrix-core work of the step (PV of t - 1,
-// QK^T of t + 1) does not depend on the step's softmax, so the two overlap (and the
-// other wave of the SIMD fills the gaps); PV goes first so that the rare rescale
-// finds it in the accumulators.  Before the barrier the wave already reads what
-// the next step needs (K and per-key term of t + 2, V^T of t): those entries were
-// written a step earlier, so their LDS latency hides behind the barrier.  Entries
-// t .. t + 8 are read during the step and t + 9 is written: the ring has ten slots.
-template <typename T, bool RAW>
-__device__ __forceinline__ void band_step(const Ctx<T>& c, Slot<T>* ring, int tt, int rg, int sb,
-                                          int n, int g, float c2, Stage<T>& set,
-                                          const typename Frag<T>::v8 qf[4], f32x16 o[2],
-                                          float& m_run, float& l_run, f32x16& s_cur,
-                                          f32x16& s_nxt, f32x16& cb, KFrag<T>& kf,
-                                          VFrag<T>& vf, typename Frag<T>::v8 pf[2]) {
-  pv_frag<T>(vf, pf, o);
-  s_nxt = qk_frag_c<T>(kf, qf, cb);
-  const int tq = tt - c.ngb - sb;   // band block relative to this sub-block's first one
-  // blocks tq = 1 .. (W - 31) / 32 lie wholly inside the window of every row
-  if (tt >= c.ngb && !(tq >= 1 && kBlk * tq + kBlk - 1 <= c.W)) {
-    const int band_c = kBlk * tq + 4 * g - n;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int cc = band_c + 8 * (v >> 2) + (v & 3);
-      s_cur[v] = (unsigned)cc <= (unsigned)c.W ? s_cur[v] : -INFINITY;
-    }
-  }
-  float m5[5];
-#pragma unroll
-  for (int i = 0; i < 5; ++i) m5[i] = vmax(vmax(s_cur[3 * i], s_cur[3 * i + 1]), s_cur[3 * i + 2]);
-  float mx = vmax(vmax(m5[0], m5[1]), vmax(m5[2], s_cur[15]));
-  mx = vmax(vmax(mx, m5[3]), m5[4]);
-  const float ms = cross_half_max(mx) * c2;
-  if (__builtin_expect(__ballot(ms > m_run + kLazy) != 0ull, 0)) {
-    // rare: the max of some row grew by more than kLazy
-    const float m_new = ms > m_run + kLazy ? ms : m_run;
-    const float alpha = fast_exp2(m_run - m_new);
-    l_run *= alpha;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      o[0][v] *= alpha;
-      o[1][v] *= alpha;
-    }
-    m_run = m_new;
-  }
-  float x[16];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) x[v] = s_cur[v];
-  exp_p<T>(x, m_run, c2, l_run, pf);
-  stage_step<T, RAW>(c, ring, tt, set);
-  const Slot<T>& k2 = ring[wave_entry(c, tt + 2, rg) % kRing];
-  read_k<T>(kf, k2);
-  cb = read_bias<T>(k2);
-  read_v<T>(vf, ring[wave_entry(c, tt, rg) % kRing]);
   __syncthreads();
 }
 
@@ -757,20 +641,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   c.S = a.S;
   c.W = a.W;
   c.G = a.G;
-  c.ngb = (a.G + kBlk - 1) / kBlk;
+  c.ngp = (a.G + kEnt - 1) / kEnt;
   c.r0 = c.tile * kTile;
   c.kbase = c.r0 - (a.W >> 1);
   // a row group needs nband + 1 band blocks (its second sub-block starts one block
-  // later); the steps run in pairs (the register sets alternate), so an odd count
-  // gets one more step, whose block is outside every window and adds nothing
+  // later): npb entries
   const int nband = (c.W + 2 * kBlk - 1) / kBlk;
-  const int n_steps = (c.ngb + nband + 1 + 1) & ~1;
-  c.n_list = c.ngb + nband + 2 * 3 + 1;
+  const int npb = (nband + 2) / 2;
+  const int n_steps = c.ngp + npb;
+  c.n_list = c.ngp + npb + 3;
   const size_t head = (size_t)c.bh * c.S * 64;
   c.mask = (const T*)(RAW ? a.local_mask : a.bias) + (size_t)c.b * c.S;
   const float c2 = a.scale * kLog2e;
   const bool split = a.G > 0 && c.tile < a.n_split;
-
   c.sp_lo = split ? c.tile * a.split_len : 0;
   c.sp_hi = split ? min(c.S, c.sp_lo + a.split_len) : 0;
   c.kh = (const T*)a.k + head;
@@ -781,13 +664,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // every load the prologue needs is issued before anything waits: the first round
   // of the global-row split (split tiles), the first ring entries, Q, the register
   // sets
-  Stage<T> spl[kWaves];
+  Stage<T> spl[kSplitEnt];
   if (split) {
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w)
-      stage_load<T>(spl[w], make_rsrc(c.kgh, (uint32_t)c.S * 128u),
+    for (int e = 0; e < kSplitEnt; ++e)
+      stage_load<T>(spl[e], make_rsrc(c.kgh, (uint32_t)c.S * 128u),
                     make_rsrc(c.vgh, (uint32_t)c.S * 128u), make_rsrc(c.mask, (uint32_t)c.S * 2u),
-                    c.sp_lo + kBlk * w);
+                    c.sp_lo + kEnt * e);
   }
   Stage<T> pro[kAhead];
 #pragma unroll
@@ -816,28 +699,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 
   f32x16 o[2] = {f32x16{}, f32x16{}};
   float m_run = kNegBig, l_run = 0.0f;
-  f32x16 sc0, sc1;   // scores of the current / next block
-  f32x16 cb;         // per-key term of the next block
-  v8 pf[2] = {v8{}, v8{}};   // P of the previous block: none yet
-  KFrag<T> kf;
-  VFrag<T> vf;
-  {
-    const Slot<T>& s0 = ring[wave_entry(c, 0, rg) % kRing];
-    const Slot<T>& s1 = ring[wave_entry(c, 1, rg) % kRing];
-    read_k<T>(kf, s0);
-    sc0 = qk_frag_c<T>(kf, qf, read_bias<T>(s0));
-    read_k<T>(kf, s1);
-    cb = read_bias<T>(s1);
-    read_v<T>(vf, s0);   // with P = 0: adds nothing
-  }
   constexpr int s0i = kAhead % kDepth, s1i = (kAhead + 1) % kDepth;
-  for (int t0 = 0; t0 < n_steps; t0 += 2) {
-    band_step<T, RAW>(c, ring, t0, rg, sb, n, g, c2, st[s0i], qf, o, m_run, l_run, sc0, sc1, cb,
-                      kf, vf, pf);
-    band_step<T, RAW>(c, ring, t0 + 1, rg, sb, n, g, c2, st[s1i], qf, o, m_run, l_run, sc1, sc0, cb,
-                      kf, vf, pf);
+  int t0 = 0;
+  for (; t0 + 2 <= n_steps; t0 += 2) {
+    band_step<T, RAW>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
+    band_step<T, RAW>(c, ring, t0 + 1, rg, sb, c2, st[s1i], qf, o, m_run, l_run);
   }
-  pv_frag<T>(vf, pf, o);   // PV of the last block (its V^T was read by the last step)
+  if (t0 < n_steps) band_step<T, RAW>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
 
   // epilogue: normalise and store the local rows
   {
@@ -888,8 +756,8 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
 }  // namespace
 
 void attn_split_plan(int S, int* n_split, int* split_len) {
-  // one split per 128-row tile, at most 32 splits per (b, h); splits are whole
-  // rounds of 4 x 32 keys
+  // one split per 256-row tile, at most 32 splits per (b, h); splits are whole
+  // rounds of 8 x 32 keys
   const int n_tiles = (S + kTile - 1) / kTile;
   const int want = n_tiles < kMaxSplit ? n_tiles : kMaxSplit;
   const int unit = kBlk * kWaves;
