@@ -9,8 +9,12 @@ index extraction, mask shift, band + global attention (every step of the path).
 Prints ONE JSON line on stdout.  `value` is effective TFLOP/s = algorithmic flops
 (256 per allowed (query, key) pair) / wall time per step.  `roofline` reports the
 dominant kernel (the band + global-row launch) timed by HIP events recorded on its
-own stream around each launch inside the timed region.  `cpu_baseline` times the
-float64 oracle on a bounded sample of the same workload on this host.
+own stream around each launch inside the timed region, against the roofline that
+binds at its algorithmic intensity (flops / algorithmic bytes vs the ridge point
+2516.6 TFLOP/s / 8 TB/s); the MFMA fraction is reported beside it.  `traffic` is
+the counter-measured HBM bytes per launch from the committed summary, when it was
+taken on the current kernel sources.  `cpu_baseline` times the float64 oracle on a
+bounded sample of the same workload on this host.
 """
 from __future__ import annotations
 
@@ -105,6 +109,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the oracle CPU baseline (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="after the timed loop, run one plain elementwise copy of this many MiB "
+                         "(fp32 in, fp32 out) so HBM counters can be scaled by a known size")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
@@ -141,6 +148,14 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     n_k, k_ms = lf.kernel_timing_stop()
+    if args.calibrate_copy_mb > 0:
+        n = args.calibrate_copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)   # reads and writes calibrate_copy_mb MiB each
+        torch.cuda.synchronize()
+        log(f"calibration copy: {args.calibrate_copy_mb} MiB read + {args.calibrate_copy_mb} MiB written")
     ms = e0.elapsed_time(e1) / args.steps
     k_avg_ms = k_ms / max(n_k, 1)
 
@@ -153,6 +168,27 @@ def main():
         f"{alg_bytes / (k_avg_ms * 1e-3) / 1e9:.0f} GB/s algorithmic")
 
     traffic = stored_traffic()
+    # which roofline binds: algorithmic intensity against the ridge point
+    ridge = PEAK_FP16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    intensity = flops / alg_bytes
+    hbm_gbs = alg_bytes / (k_avg_ms * 1e-3) / 1e9
+    if intensity < ridge:
+        roof = {"bound": "hbm", "achieved": round(hbm_gbs, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(hbm_gbs / PEAK_HBM_GBS, 5)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(k_tflops, 3), "peak": PEAK_FP16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(k_tflops / PEAK_FP16_TFLOPS, 5)}
+    roof.update({
+        "traffic": traffic,
+        "kernel": "attn_mfma_kernel (band tiles + global-row splits)",
+        "kernel_avg_us": round(k_avg_ms * 1e3, 3),
+        "algorithmic_flops_per_launch": flops,
+        "algorithmic_bytes_per_launch": alg_bytes,
+        "intensity_flop_per_byte": round(intensity, 1),
+        "ridge_flop_per_byte": round(ridge, 1),
+        "mfma_achieved_tflops": round(k_tflops, 3),
+        "mfma_frac": round(k_tflops / PEAK_FP16_TFLOPS, 5),
+    })
     res = {
         "metric": METRIC,
         "value": round(tflops, 3),
@@ -169,18 +205,7 @@ def main():
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "S": wl.S, "W": wl.W, "G": wl.G,
                    "head_dim": 64},
         "pct_mfma_peak": round(100.0 * tflops / PEAK_FP16_TFLOPS, 3),
-        "roofline": {
-            "bound": "mfma",
-            "achieved": round(k_tflops, 3),
-            "peak": PEAK_FP16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(k_tflops / PEAK_FP16_TFLOPS, 5),
-            "traffic": traffic,
-            "kernel": "attn_mfma_kernel (band tiles + global-row splits)",
-            "kernel_avg_us": round(k_avg_ms * 1e3, 3),
-            "algorithmic_flops_per_launch": flops,
-            "algorithmic_bytes_per_launch": alg_bytes,
-        },
+        "roofline": roof,
     }
     if not args.no_cpu_baseline and args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_seconds)
