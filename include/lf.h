@@ -146,15 +146,24 @@ size_t lf_encoder_layer_workspace_bytes(int dtype, int B, int S, int hidden, int
                                         int W, int G);
 
 /*
- * One post-LayerNorm Longformer encoder layer ([FT-LF] per-layer steps 1-6):
+ * One post-LayerNorm Longformer encoder layer ([FT-LF] computation flow, per-layer
+ * steps 1-6):
  *   [q|k|v|kg|vg] = x W_proj^T + b_proj, split into heads; qg = x[:, :G] W_qg^T + b_qg;
  *   a  = band + global attention (as lf_attn_forward, scale attn_scale), heads joined;
  *   h1 = LayerNorm(x + a W_o^T + b_o; ln1)    (biased variance, eps ln_eps)
  *   y  = LayerNorm(h1 + GELU(h1 W_1^T + b_1) W_2^T + b_2; ln2)   (exact erf GELU)
- * x, y: [B, S, hidden].  Requires hidden == 64*H and hidden % 64 == 0, ffn % 64 == 0,
- * plus the attention shape rules.  `workspace` (device, ws_bytes >=
- * lf_encoder_layer_workspace_bytes) holds the intermediates; the residual stream
- * is kept in fp32 there.  Currently implemented for LF_F16 and LF_BF16.
+ * x, y: [B, S, hidden] in `dtype`, which must be LF_F16 or LF_BF16 (LF_F32 returns
+ * LF_ERR_UNSUPPORTED).  Shape rules: the attention rules of lf_attn_forward, plus
+ * hidden == 64*H, hidden and ffn multiples of 128, hidden one of 256, 512, 768,
+ * 1024, 2048, 4096 (LayerNorm row widths), B*S*ffn*2 < 2^31.  w_qg / b_qg may be
+ * NULL when G == 0.  `workspace` (device, 256-byte aligned, ws_bytes >=
+ * lf_encoder_layer_workspace_bytes) holds every intermediate: attention tickets
+ * first, then q, k, v, kg, vg, qg, the attention output, the fp32 pre-LayerNorm
+ * rows, h1 in fp32 and in `dtype`, the FFN intermediate.  Its first bytes (the
+ * tickets) must be zero before the first call that uses it (zero-fill it once after
+ * allocating); every call leaves them zero.  The residual stream (x + projection,
+ * h1) is kept in fp32; GEMM inputs are rounded to `dtype`.  Calls sharing a
+ * workspace must not overlap in time.  Enqueues 8 launches on `stream`, no sync.
  */
 int lf_encoder_layer(int dtype, const lf_layer_weights* w, const void* x,
                      const void* local_mask, const void* global_mask, int B, int S,

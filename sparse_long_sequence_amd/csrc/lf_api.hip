@@ -146,6 +146,59 @@ lf::AttnArgs make_args(int dtype, const void* q, const void* k, const void* v, c
   return a;
 }
 
+// Shape rules of the encoder layer: the attention rules plus hidden == 64 * H, hidden
+// and ffn multiples of 128 (GEMM tiles) and LayerNorm widths the row kernel takes.
+int validate_layer(int dtype, int B, int S, int hidden, int H, int ffn, int W, int G) {
+  if (dtype != LF_F16 && dtype != LF_BF16) {
+    if (!known_dtype(dtype)) return fail(LF_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+    return fail(LF_ERR_UNSUPPORTED, "lf_encoder_layer runs in fp16 or bf16");
+  }
+  if (int e = validate_attn(dtype, B, H, S, W, G)) return e;
+  if (hidden != 64 * H)
+    return fail(LF_ERR_INVALID_ARGUMENT, "hidden must be 64*H (hidden=%d, H=%d)", hidden, H);
+  if (hidden % 128 != 0 || ffn % 128 != 0 || ffn < 128)
+    return fail(LF_ERR_INVALID_ARGUMENT, "hidden and ffn must be multiples of 128 (got %d, %d)",
+                hidden, ffn);
+  if (!lf::layernorm_width_ok(hidden))
+    return fail(LF_ERR_INVALID_ARGUMENT, "hidden must be 256, 512, 768, 1024, 2048 or 4096");
+  if (G > S) return fail(LF_ERR_INVALID_ARGUMENT, "G must be <= S");
+  const int64_t M = (int64_t)B * S;
+  if (M * ffn * 2 > INT_MAX || M * hidden * 4 > (int64_t)1 << 40)
+    return fail(LF_ERR_INVALID_ARGUMENT, "B*S*ffn too large for 32-bit GEMM offsets");
+  return LF_OK;
+}
+
+// Encoder-layer workspace: the attention tickets and partials first (so the
+// tickets sit at offset 0), then q, k, v, kg, vg, qg, the attention output, the
+// fp32 pre-LayerNorm buffer, h1 in fp32 and in the layer dtype, and the FFN
+// intermediate (which reuses the q..vg area when it fits: they are dead by then).
+struct LayerWs {
+  size_t act_bytes, qkv_off, qg_off, attn_off, z_off, h1f_off, h1t_off, u_off, total;
+};
+
+LayerWs layer_ws(int dtype, int B, int S, int hidden, int H, int ffn, int G) {
+  LayerWs L;
+  const size_t es = dtype_size(dtype), M = (size_t)B * S;
+  const AttnWs aw = attn_ws(B, H, S, G);
+  size_t off = align256(aw.total);
+  L.act_bytes = align256(M * hidden * es);
+  L.qkv_off = off; off += 5 * L.act_bytes;
+  L.qg_off = off; off += align256((size_t)B * (G > 0 ? G : 1) * hidden * es);
+  L.attn_off = off; off += L.act_bytes;
+  L.z_off = off; off += align256(M * hidden * 4);
+  L.h1f_off = off; off += align256(M * hidden * 4);
+  L.h1t_off = off; off += L.act_bytes;
+  const size_t u_bytes = align256(M * (size_t)ffn * es);
+  if (u_bytes <= 5 * L.act_bytes) {
+    L.u_off = L.qkv_off;
+  } else {
+    L.u_off = off;
+    off += u_bytes;
+  }
+  L.total = off;
+  return L;
+}
+
 // Workspace of lf_attn_forward (fp16 / bf16), cached per (device, stream): the
 // split tickets [ticket_cap ints, zeroed when allocated and left zero by every
 // call] followed by the partial states.  Calls on one stream are ordered, so they
@@ -402,18 +455,104 @@ int lf_kernel_timing_stop(int* launches, double* total_ms) {
 
 size_t lf_encoder_layer_workspace_bytes(int dtype, int B, int S, int hidden, int H, int ffn,
                                         int W, int G) {
-  (void)dtype; (void)B; (void)S; (void)hidden; (void)H; (void)ffn; (void)W; (void)G;
-  return 0;
+  if (validate_layer(dtype, B, S, hidden, H, ffn, W, G) != LF_OK) return 0;
+  return layer_ws(dtype, B, S, hidden, H, ffn, G).total;
 }
 
 int lf_encoder_layer(int dtype, const lf_layer_weights* w, const void* x, const void* local_mask,
                      const void* global_mask, int B, int S, int hidden, int H, int ffn, int W,
                      int G, float attn_scale, float ln_eps, void* y, void* workspace,
                      size_t ws_bytes, void* stream) {
-  (void)dtype; (void)w; (void)x; (void)local_mask; (void)global_mask; (void)B; (void)S;
-  (void)hidden; (void)H; (void)ffn; (void)W; (void)G; (void)attn_scale; (void)ln_eps; (void)y;
-  (void)workspace; (void)ws_bytes; (void)stream;
-  return fail(LF_ERR_UNSUPPORTED, "lf_encoder_layer: not built yet");
+  if (int e = validate_layer(dtype, B, S, hidden, H, ffn, W, G)) return e;
+  if (!w) return fail(LF_ERR_INVALID_ARGUMENT, "null pointer: weights");
+  if (int e = null_check("x,local_mask,global_mask,y,workspace,w_proj,b_proj,w_o,b_o,ln1_g,"
+                         "ln1_b,w_ffn1,b_ffn1,w_ffn2,b_ffn2,ln2_g,ln2_b",
+                         {x, local_mask, global_mask, y, workspace, w->w_proj, w->b_proj, w->w_o,
+                          w->b_o, w->ln1_g, w->ln1_b, w->w_ffn1, w->b_ffn1, w->w_ffn2, w->b_ffn2,
+                          w->ln2_g, w->ln2_b}))
+    return e;
+  if (G > 0 && (!w->w_qg || !w->b_qg))
+    return fail(LF_ERR_INVALID_ARGUMENT, "null pointer: w_qg / b_qg (G > 0)");
+  const LayerWs L = layer_ws(dtype, B, S, hidden, H, ffn, G);
+  if (ws_bytes < L.total)
+    return fail(LF_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu bytes", ws_bytes, L.total);
+  if ((uintptr_t)workspace % 256 != 0)
+    return fail(LF_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if (!(attn_scale > 0.0f) || !(ln_eps > 0.0f))
+    return fail(LF_ERR_INVALID_ARGUMENT, "attn_scale and ln_eps must be > 0");
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const int M = B * S, D = hidden;
+  void* qkv[5];
+  for (int i = 0; i < 5; ++i) qkv[i] = ws + L.qkv_off + (size_t)i * L.act_bytes;
+  void* qg = ws + L.qg_off;
+  void* attn = ws + L.attn_off;
+  float* z = (float*)(ws + L.z_off);
+  float* h1f = (float*)(ws + L.h1f_off);
+  void* h1t = ws + L.h1t_off;
+  void* u = ws + L.u_off;
+
+  auto gemm = [&](int epi, const void* A, int lda, int a_group, int a_group_stride,
+                  const void* Wt, int ldw, const void* bias, int Mr, int N, int K) {
+    lf::GemmArgs g;
+    memset(&g, 0, sizeof g);
+    g.dtype = dtype; g.epi = epi;
+    g.a = A; g.lda = lda; g.a_group = a_group; g.a_group_stride = a_group_stride;
+    g.w = Wt; g.ldw = ldw; g.bias = bias;
+    g.M = Mr; g.N = N; g.K = K;
+    g.D = D; g.H = H; g.rows = S;
+    return g;
+  };
+  hipError_t he;
+  // step 1: packed projections, split into heads ([B, H, S, 64] each)
+  {
+    lf::GemmArgs g = gemm(lf::kEpiHeads, x, D, 0, 0, w->w_proj, D, w->b_proj, M, 5 * D, D);
+    for (int i = 0; i < 5; ++i) g.heads[i] = qkv[i];
+    if ((he = lf::launch_gemm(g, st)) != hipSuccess) return hip_fail(he, "projection GEMM");
+  }
+  // the global queries: rows 0 .. G-1 of every sequence
+  if (G > 0) {
+    lf::GemmArgs g = gemm(lf::kEpiHeads, x, D, G, S, w->w_qg, D, w->b_qg, B * G, D, D);
+    g.heads[0] = qg;
+    g.rows = G;
+    if ((he = lf::launch_gemm(g, st)) != hipSuccess) return hip_fail(he, "global-query GEMM");
+  }
+  // steps 3-4: attention, heads joined ([B, S, H * 64])
+  {
+    AttnWs aw = attn_ws(B, H, S, G);
+    lf::AttnArgs a = make_args(dtype, qkv[0], qkv[1], qkv[2], qg, qkv[3], qkv[4], nullptr, nullptr,
+                               nullptr, B, H, S, W, G, attn, ws, aw, aw.partials_off);
+    a.raw = 1;
+    a.local_mask = local_mask;
+    a.global_mask = global_mask;
+    a.out_ss = D;
+    a.out_sh = 64;
+    a.out_sb = (int64_t)S * D;
+    a.scale = attn_scale;
+    if ((he = lf::launch_attention(a, st)) != hipSuccess) return hip_fail(he, "attention");
+  }
+  // step 5: output projection + bias + residual (fp32), LayerNorm
+  {
+    lf::GemmArgs g = gemm(lf::kEpiResidT, attn, D, 0, 0, w->w_o, D, w->b_o, M, D, D);
+    g.out = z; g.ldo = D; g.resid = x; g.ldr = D;
+    if ((he = lf::launch_gemm(g, st)) != hipSuccess) return hip_fail(he, "output GEMM");
+    if ((he = lf::launch_layernorm(dtype, z, w->ln1_g, w->ln1_b, ln_eps, M, D, h1f, h1t, st)) !=
+        hipSuccess)
+      return hip_fail(he, "LayerNorm 1");
+  }
+  // step 6: FFN with GELU, second GEMM + bias + residual (fp32), LayerNorm
+  {
+    lf::GemmArgs g = gemm(lf::kEpiGelu, h1t, D, 0, 0, w->w_ffn1, D, w->b_ffn1, M, ffn, D);
+    g.out = u; g.ldo = ffn;
+    if ((he = lf::launch_gemm(g, st)) != hipSuccess) return hip_fail(he, "FFN GEMM 1");
+    lf::GemmArgs g2 = gemm(lf::kEpiResidF32, u, ffn, 0, 0, w->w_ffn2, ffn, w->b_ffn2, M, D, ffn);
+    g2.out = z; g2.ldo = D; g2.resid = h1f; g2.ldr = D;
+    if ((he = lf::launch_gemm(g2, st)) != hipSuccess) return hip_fail(he, "FFN GEMM 2");
+    if ((he = lf::launch_layernorm(dtype, z, w->ln2_g, w->ln2_b, ln_eps, M, D, nullptr, y, st)) !=
+        hipSuccess)
+      return hip_fail(he, "LayerNorm 2");
+  }
+  return ok();
 }
 
 }  // extern "C"

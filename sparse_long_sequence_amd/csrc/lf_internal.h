@@ -54,12 +54,38 @@ hipError_t launch_attention_fp32(const AttnArgs& a, hipStream_t st);
 hipError_t launch_check_masks(int dtype, const void* local_mask, const void* global_mask, int B,
                               int S, int G, int* flags, hipStream_t st);
 
-// Layer pieces.
-hipError_t launch_gemm(int dtype, int epilogue, const void* A, int lda, const void* Bw, int ldb,
-                       const void* bias, const void* resid_f32, void* C, int ldc, int M, int N,
-                       int K, int a_rows_per_batch, int a_batch_stride_rows, void* aux0,
-                       void* aux1, void* aux2, void* aux3, void* aux4, int S, int H,
-                       hipStream_t st);
+// Layer pieces (gemm.hip).  C[m, n] = sum_k A[arow(m), k] * W[n, k] + bias[n], with
+// arow(m) = (m / a_group) * a_group_stride + m % a_group when a_group > 0, else m;
+// then the epilogue.  A, W, bias, outputs and the T residual are in the layer dtype.
+enum GemmEpi {
+  kEpiHeads = 0,     // n -> tensor n / D, head (n % D) / 64, dim n % 64; m -> (m / rows,
+                     // m % rows): heads[tensor][((b * H + h) * rows + r) * 64 + d]
+  kEpiGelu = 1,      // out[m * ldo + n] = gelu(acc + bias), dtype
+  kEpiResidT = 2,    // out[m * ldo + n] = acc + bias + resid[m * ldr + n] (resid dtype), fp32
+  kEpiResidF32 = 3,  // same with an fp32 residual
+};
+
+struct GemmArgs {
+  int dtype, epi;
+  const void* a;
+  int lda, a_group, a_group_stride;
+  const void* w;
+  int ldw;
+  const void* bias;
+  int M, N, K;
+  void* heads[5];
+  int D, H, rows;
+  void* out;
+  int ldo;
+  const void* resid;
+  int ldr;
+};
+
+// N a positive multiple of 128, K of 64, M >= 1.
+bool gemm_shape_ok(int M, int N, int K);
+// Row widths the LayerNorm kernel takes (multiples of 256 up to 4096).
+bool layernorm_width_ok(int N);
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
 hipError_t launch_layernorm(int dtype, const float* z, const void* gamma, const void* beta,
                             float eps, int M, int N, float* out_f32, void* out_t,
                             hipStream_t st);

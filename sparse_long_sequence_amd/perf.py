@@ -1,0 +1,108 @@
+"""Timing driver for the library's entry points on seeded synthetic inputs.
+
+    python sparse_long_sequence_amd/perf.py attn  [--iters N]   # longformer-large attention
+    python sparse_long_sequence_amd/perf.py prep  [--iters N]   # index compaction + mask shift
+    python sparse_long_sequence_amd/perf.py layer [--iters N]   # one fp16 encoder layer
+
+Prints one JSON line per run: time per call (HIP events on the current stream around
+N back-to-back calls after a warm-up) and the algorithmic throughput.  This is the
+command profiles are taken with (rocprofv3 -- python3 <repo>/sparse_long_sequence_amd/perf.py
+...); the headline benchmark is bench.py at the repository root.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import sparse_long_sequence_amd as lf  # noqa: E402
+import workloads  # noqa: E402
+
+
+def _time(fn, iters: int, warmup: int) -> float:
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def run_attn(iters: int, warmup: int) -> dict:
+    wl = workloads.LARGE_FP16
+    g = {n: t.cuda() for n, t in workloads.make_attention_inputs(wl).items()}
+    out = torch.empty_like(g["q"])
+    ms = _time(lambda: lf.attn_forward(g["q"], g["k"], g["v"], g["qg"], g["kg"], g["vg"],
+                                       g["local_mask"], g["global_mask"], wl.W, wl.G, out=out),
+               iters, warmup)
+    S, W, G = wl.S, wl.W, wl.G
+    pairs = G * S + (S - G) * (W + 1 + G) - (W // 2) * (W // 2 + 1)
+    flops = 256.0 * pairs * wl.B * wl.H
+    return {"op": "attn_forward", "workload": wl.name, "ms": ms,
+            "tflops": flops / (ms * 1e-3) / 1e12}
+
+
+def run_prep(iters: int, warmup: int) -> dict:
+    wl = workloads.LONG_BF16
+    inp = workloads.make_attention_inputs(wl)
+    gm, lm = inp["global_mask"].cuda(), inp["local_mask"].cuda()
+    B, S = gm.shape
+    idx = torch.empty(B, S, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(B, dtype=torch.int32, device="cuda")
+    bias = torch.empty_like(lm)
+    ms_idx = _time(lambda: lf.init_global_idx(gm, idx, cnt), iters, warmup)
+    ms_shift = _time(lambda: lf.mask_shift(lm, bias), iters, warmup)
+    es = gm.element_size()
+    idx_bytes = B * S * (es + 4) + B * 4
+    shift_bytes = 2 * B * S * es
+    return {"op": "prep", "workload": f"masks of {wl.name}", "ms_init_global_idx": ms_idx,
+            "gbs_init_global_idx": idx_bytes / (ms_idx * 1e-3) / 1e9, "ms_mask_shift": ms_shift,
+            "gbs_mask_shift": shift_bytes / (ms_shift * 1e-3) / 1e9}
+
+
+def run_layer(iters: int, warmup: int) -> dict:
+    wl = workloads.LAYER_FP16
+    t = workloads.make_layer_inputs(wl)
+    x = t["x"].cuda()
+    w = {n: t[n].cuda() for n in lf.LAYER_WEIGHT_FIELDS}
+    lm, gm = t["local_mask"].cuda(), t["global_mask"].cuda()
+    y = torch.empty_like(x)
+    nbytes = lf.encoder_layer_workspace_bytes(x.dtype, wl.B, wl.S, wl.hidden, wl.H, wl.ffn,
+                                              wl.W, wl.G)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    ms = _time(lambda: lf.encoder_layer(x, w, lm, gm, wl.H, wl.W, wl.G, out=y, workspace=ws),
+               iters, warmup)
+    M, D, F, G, S, W = wl.B * wl.S, wl.hidden, wl.ffn, wl.G, wl.S, wl.W
+    gemm = 2.0 * M * D * (5 * D + D + 2 * F) + 2.0 * wl.B * G * D * D
+    pairs = G * S + (S - G) * (W + 1 + G) - (W // 2) * (W // 2 + 1)
+    attn = 256.0 * pairs * wl.B * wl.H
+    return {"op": "encoder_layer", "workload": wl.name, "ms": ms,
+            "gemm_gflop": gemm / 1e9, "attn_gflop": attn / 1e9,
+            "tflops": (gemm + attn) / (ms * 1e-3) / 1e12}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("op", choices=["attn", "prep", "layer"])
+    ap.add_argument("--iters", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    a = ap.parse_args()
+    fn = {"attn": run_attn, "prep": run_prep, "layer": run_layer}[a.op]
+    print(json.dumps(fn(a.iters, a.warmup)), flush=True)
+
+
+if __name__ == "__main__":
+    main()

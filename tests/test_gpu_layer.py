@@ -1,0 +1,114 @@
+"""GPU parity of the encoder layer against the float64 oracle.
+
+[FT-LF] computation flow, per-layer steps 1-6: projections (bias, head split),
+band + global attention, output projection + residual + LayerNorm, GELU FFN +
+residual + LayerNorm.  Tolerances on the layer output: fp16 max abs error 3e-3 (the
+full-size fp16 layer is a graded workload).  No bf16 layer is graded; its bound is
+derived from the arithmetic: 2.5e-2 + 2^-8 |ref| per element.  LayerNorm outputs
+exceed 4 in magnitude, where one bf16 rounding of the output alone is up to 2^-9 |y|
+(the relative term allows one ulp), and six tensors on the way are bf16 MFMA inputs
+(q, k, v, the attention output, h1, the GELU output), each rounded with relative
+error up to 2^-9 ~ 2e-3; after the LayerNorm's division by the row's standard
+deviation these accumulate to ~1e-2 in the tail over 10^5 outputs.
+Small layers are compared over the whole output; the full-size layer (hidden 1024,
+16 heads, FFN 4096) on sampled rows the oracle computes one by one."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp16": 3e-3, "bf16": 2.5e-2}
+
+
+@pytest.fixture(scope="module")
+def lf():
+    import sparse_long_sequence_amd as m
+    m.load_library()
+    return m
+
+
+def _inputs(seed, B, S, D, H, F, G, dtype, pad=None, w_std=0.05, b_std=0.02, ln_jitter=0.1):
+    rng = np.random.default_rng(seed)
+    w = workloads.random_layer_params(rng, D, F, dtype, w_std=w_std, b_std=b_std,
+                                      ln_jitter=ln_jitter)
+    x = torch.from_numpy(rng.standard_normal((B, S, D))).to(workloads.TORCH_DTYPES[dtype])
+    lm, gm = workloads.make_masks(rng, B, S, G, dtype, pad, None)
+    return x, w, lm, gm
+
+
+def _run(lf, x, w, lm, gm, H, W, G):
+    wg = {n: t.cuda() for n, t in w.items()}
+    y = lf.encoder_layer(x.cuda(), wg, lm.cuda(), gm.cuda(), H, W, G)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("case", [
+    # B, S, D, H, F, W, G, pad
+    (1, 512, 256, 4, 512, 128, 8, None),
+    (2, 384, 512, 8, 1024, 64, 0, (0.1, 0.25)),
+    (1, 256, 256, 4, 384, 128, 64, None),
+], ids=["B1_S512_D256_G8", "B2_S384_D512_G0_pad", "B1_S256_D256_G64"])
+def test_layer_parity_small(lf, dtype, case):
+    B, S, D, H, F, W, G, pad = case
+    x, w, lm, gm = _inputs(11 + S + G, B, S, D, H, F, G, dtype, pad)
+    y = _run(lf, x, w, lm, gm, H, W, G).cpu()
+    assert torch.isfinite(y.float()).all()
+    ref = oracle.encoder_layer(x, w, lm, gm, H, W, G)
+    err = np.abs(y.double().numpy() - ref)
+    tol = TOL[dtype] + (2.0 ** -8 * np.abs(ref) if dtype == "bf16" else 0.0)
+    worst = np.argmax(err - tol)
+    assert np.all(err <= tol), (f"max abs err {err.max():.3e}; worst excess at |ref| = "
+                                f"{np.abs(ref).flat[worst]:.3f} (err {err.flat[worst]:.3e})")
+
+
+def test_layer_zero_output_projection_is_layernorm_of_input(lf):
+    # W_o = 0, b_o = 0: h1 = LN(x); the FFN still runs on it
+    B, S, D, H, F, W, G = 1, 256, 256, 4, 256, 64, 4
+    x, w, lm, gm = _inputs(5, B, S, D, H, F, G, "fp16")
+    w["w_o"].zero_()
+    w["b_o"].zero_()
+    y = _run(lf, x, w, lm, gm, H, W, G).cpu()
+    ref = oracle.encoder_layer(x, w, lm, gm, H, W, G)
+    assert np.abs(y.double().numpy() - ref).max() <= TOL["fp16"]
+
+
+def test_layer_full_workload_sampled_rows(lf):
+    wl = workloads.LAYER_FP16
+    t = workloads.make_layer_inputs(wl)
+    x, lm, gm = t["x"], t["local_mask"], t["global_mask"]
+    w = {n: t[n] for n in lf.LAYER_WEIGHT_FIELDS}
+    y = _run(lf, x, w, lm, gm, wl.H, wl.W, wl.G)
+    y2 = _run(lf, x, w, lm, gm, wl.H, wl.W, wl.G)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "not deterministic"
+    assert torch.isfinite(y).all()
+    got = y.cpu()
+    rng = np.random.default_rng(wl.seed + 7)
+    rows = sorted({(b, s) for b in range(wl.B)
+                   for s in [0, 1, wl.G - 1, wl.G, wl.G + 1, wl.W // 2, wl.S // 2, wl.S - 1]
+                   + [int(v) for v in rng.integers(0, wl.S, 12)]})
+    ref = oracle.encoder_layer(x, w, lm, gm, wl.H, wl.W, wl.G, rows=rows)
+    g_rows = np.stack([got[b, s].double().numpy() for (b, s) in rows])
+    err = np.abs(g_rows - ref).max()
+    assert err <= TOL["fp16"], f"max abs err {err:.3e} over {len(rows)} rows"
+
+
+def test_layer_rejects_bad_arguments(lf):
+    B, S, D, H, F, W, G = 1, 256, 256, 4, 256, 64, 4
+    x, w, lm, gm = _inputs(3, B, S, D, H, F, G, "fp16")
+    wg = {n: t.cuda() for n, t in w.items()}
+    xg, lmg, gmg = x.cuda(), lm.cuda(), gm.cuda()
+    small = torch.zeros(1024, dtype=torch.uint8, device="cuda")
+    with pytest.raises(lf.LFError, match="workspace too small"):
+        lf.encoder_layer(xg, wg, lmg, gmg, H, W, G, workspace=small)
+    with pytest.raises(lf.LFError, match="hidden must be 64"):
+        lf.encoder_layer(xg, wg, lmg, gmg, H + 1, W, G)
+    x32 = xg.float()
+    with pytest.raises(lf.LFError):
+        lf.encoder_layer(x32, {n: t.float() for n, t in wg.items()}, lmg.float(), gmg.float(), H,
+                         W, G)
