@@ -170,6 +170,26 @@ int lf_encoder_layer(int dtype, const lf_layer_weights* w, const void* x,
                      int hidden, int H, int ffn, int W, int G, float attn_scale,
                      float ln_eps, void* y, void* workspace, size_t ws_bytes, void* stream);
 
+/* Workspace bytes lf_encoder_forward needs (0 on bad arguments). */
+size_t lf_encoder_forward_workspace_bytes(int dtype, int B, int S, int hidden, int H, int ffn,
+                                          int W, int G);
+
+/*
+ * A stack of n_layers encoder layers ([FT-LF] computation flow: the preprocessing
+ * list runs once — global-token index extraction and the local-mask shift — then the
+ * per-layer steps 1-6 run for every layer).  w points to n_layers weight sets, layer
+ * l using w[l]; each layer is lf_encoder_layer's computation, with the attention
+ * reading the preprocessed masks.  x is never written; the layer outputs alternate
+ * between y and an activation buffer in the workspace so that the last layer writes
+ * y.  Same shape rules, dtype, precision and workspace convention as
+ * lf_encoder_layer (ws_bytes >= lf_encoder_forward_workspace_bytes; its first bytes
+ * zero before the first use, left zero).  Enqueues 1 + 8 * n_layers launches.
+ */
+int lf_encoder_forward(int dtype, const lf_layer_weights* w, int n_layers, const void* x,
+                       const void* local_mask, const void* global_mask, int B, int S,
+                       int hidden, int H, int ffn, int W, int G, float attn_scale,
+                       float ln_eps, void* y, void* workspace, size_t ws_bytes, void* stream);
+
 /*
  * Measurement hook.  After lf_kernel_timing_start(capacity), each of the next
  * `capacity` lf_attn_forward / lf_attn_forward_pre calls made on this thread

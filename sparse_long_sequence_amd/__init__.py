@@ -16,7 +16,8 @@ import torch
 
 __all__ = ["LFError", "library_path", "load_library", "init_global_idx", "mask_shift",
            "attn_forward", "attn_forward_pre", "attn_workspace_bytes", "check_masks",
-           "encoder_layer", "encoder_layer_workspace_bytes", "LAYER_WEIGHT_FIELDS",
+           "encoder_layer", "encoder_layer_workspace_bytes", "encoder_forward",
+           "encoder_forward_workspace_bytes", "LAYER_WEIGHT_FIELDS",
            "kernel_timing_start", "kernel_timing_stop",
            "EXPORTED_SYMBOLS", "dtype_code"]
 
@@ -33,6 +34,7 @@ LAYER_WEIGHT_FIELDS = ["w_proj", "b_proj", "w_qg", "b_qg", "w_o", "b_o", "ln1_g"
 EXPORTED_SYMBOLS = ["lf_init_global_idx", "lf_mask_shift", "lf_attn_forward",
                     "lf_attn_workspace_bytes", "lf_attn_forward_pre", "lf_check_masks",
                     "lf_encoder_layer_workspace_bytes", "lf_encoder_layer",
+                    "lf_encoder_forward_workspace_bytes", "lf_encoder_forward",
                     "lf_kernel_timing_start", "lf_kernel_timing_stop",
                     "lf_status_string", "lf_last_error"]
 
@@ -72,6 +74,10 @@ def load_library():
     lib.lf_encoder_layer_workspace_bytes.restype = S
     lib.lf_encoder_layer.argtypes = [I, ctypes.POINTER(_LayerWeights), P, P, P, I, I, I, I, I,
                                      I, I, ctypes.c_float, ctypes.c_float, P, P, S, P]
+    lib.lf_encoder_forward_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
+    lib.lf_encoder_forward_workspace_bytes.restype = S
+    lib.lf_encoder_forward.argtypes = [I, ctypes.POINTER(_LayerWeights), I, P, P, P, I, I, I, I,
+                                       I, I, I, ctypes.c_float, ctypes.c_float, P, P, S, P]
     lib.lf_kernel_timing_start.argtypes = [I]
     lib.lf_kernel_timing_stop.argtypes = [ctypes.POINTER(ctypes.c_int),
                                           ctypes.POINTER(ctypes.c_double)]
@@ -81,6 +87,7 @@ def load_library():
     lib.lf_last_error.restype = ctypes.c_char_p
     for name in ("lf_init_global_idx", "lf_mask_shift", "lf_attn_forward",
                  "lf_attn_forward_pre", "lf_check_masks", "lf_encoder_layer",
+                 "lf_encoder_forward",
                  "lf_kernel_timing_start", "lf_kernel_timing_stop"):
         getattr(lib, name).restype = I
     _lib = lib
@@ -248,4 +255,34 @@ def encoder_layer(x, weights: dict, local_mask, global_mask, H: int, W: int, G: 
                                 _ptr(global_mask), B, S, D, H, F, W, G, attn_scale, ln_eps,
                                 _ptr(out), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(dev)))
+    return out
+
+
+def encoder_forward_workspace_bytes(dtype, B, S, hidden, H, ffn, W, G) -> int:
+    return int(load_library().lf_encoder_forward_workspace_bytes(dtype_code(dtype), B, S, hidden,
+                                                                 H, ffn, W, G))
+
+
+def encoder_forward(x, layers: list, local_mask, global_mask, H: int, W: int, G: int,
+                    attn_scale: float = 0.125, ln_eps: float = 1e-5, out=None, workspace=None):
+    """[FT-LF computation flow] preprocessing once, then len(layers) encoder layers -> y."""
+    lib = load_library()
+    if not layers:
+        raise ValueError("at least one layer")
+    ws = [[lw[n] for n in LAYER_WEIGHT_FIELDS] for lw in layers]
+    dev = _dev(x, local_mask, global_mask, *[t for w in ws for t in w])
+    B, S, D = x.shape
+    F = layers[0]["w_ffn1"].shape[0]
+    if out is None:
+        out = torch.empty_like(x)
+    nbytes = encoder_forward_workspace_bytes(x.dtype, B, S, D, H, F, W, G)
+    if workspace is None:
+        # the leading split tickets must start at zero; the library leaves them zero
+        workspace = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    _dev(out, workspace)
+    arr = (_LayerWeights * len(layers))(*[_LayerWeights(*[t.data_ptr() for t in w]) for w in ws])
+    _check(lib.lf_encoder_forward(dtype_code(x.dtype), arr, len(layers), _ptr(x),
+                                  _ptr(local_mask), _ptr(global_mask), B, S, D, H, F, W, G,
+                                  attn_scale, ln_eps, _ptr(out), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(dev)))
     return out

@@ -199,6 +199,138 @@ LayerWs layer_ws(int dtype, int B, int S, int hidden, int H, int ffn, int G) {
   return L;
 }
 
+// Masks of one layer call: raw (read by the attention kernel) or preprocessed.
+struct LayerMasks {
+  bool raw = true;
+  const void* local_mask = nullptr;
+  const void* global_mask = nullptr;
+  const int32_t* gidx = nullptr;
+  const int32_t* gcnt = nullptr;
+  const void* bias = nullptr;
+};
+
+int check_layer_call(const lf_layer_weights* w, int G, const void* x, const void* local_mask,
+                     const void* global_mask, const void* y, const void* workspace) {
+  if (!w) return fail(LF_ERR_INVALID_ARGUMENT, "null pointer: weights");
+  if (int e = null_check("x,local_mask,global_mask,y,workspace,w_proj,b_proj,w_o,b_o,ln1_g,"
+                         "ln1_b,w_ffn1,b_ffn1,w_ffn2,b_ffn2,ln2_g,ln2_b",
+                         {x, local_mask, global_mask, y, workspace, w->w_proj, w->b_proj, w->w_o,
+                          w->b_o, w->ln1_g, w->ln1_b, w->w_ffn1, w->b_ffn1, w->w_ffn2, w->b_ffn2,
+                          w->ln2_g, w->ln2_b}))
+    return e;
+  if (G > 0 && (!w->w_qg || !w->b_qg))
+    return fail(LF_ERR_INVALID_ARGUMENT, "null pointer: w_qg / b_qg (G > 0)");
+  return LF_OK;
+}
+
+int check_layer_ws(const void* workspace, size_t ws_bytes, size_t need, float attn_scale,
+                   float ln_eps) {
+  if (ws_bytes < need)
+    return fail(LF_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+  if ((uintptr_t)workspace % 256 != 0)
+    return fail(LF_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if (!(attn_scale > 0.0f) || !(ln_eps > 0.0f))
+    return fail(LF_ERR_INVALID_ARGUMENT, "attn_scale and ln_eps must be > 0");
+  return LF_OK;
+}
+
+// Stack workspace: one layer's workspace (tickets first), then the preprocessed
+// masks and one activation buffer for the layer outputs.
+struct StackWs {
+  LayerWs layer;
+  size_t gidx_off, gcnt_off, bias_off, act_off, total;
+};
+
+StackWs stack_ws(int dtype, int B, int S, int hidden, int H, int ffn, int G) {
+  StackWs W;
+  W.layer = layer_ws(dtype, B, S, hidden, H, ffn, G);
+  size_t off = W.layer.total;
+  W.gidx_off = off; off += align256((size_t)B * S * 4);
+  W.gcnt_off = off; off += align256((size_t)B * 4);
+  W.bias_off = off; off += align256((size_t)B * S * dtype_size(dtype));
+  W.act_off = off; off += W.layer.act_bytes;
+  W.total = off;
+  return W;
+}
+
+// One encoder layer ([FT-LF] per-layer steps 1-6) as 8 launches on `st`; arguments
+// already validated.
+int run_layer(int dtype, const lf_layer_weights* w, const void* x, const LayerMasks& mk, int B,
+              int S, int hidden, int H, int ffn, int W, int G, float attn_scale, float ln_eps,
+              void* y, char* ws, const LayerWs& L, hipStream_t st) {
+  const int M = B * S, D = hidden;
+  void* qkv[5];
+  for (int i = 0; i < 5; ++i) qkv[i] = ws + L.qkv_off + (size_t)i * L.act_bytes;
+  void* qg = ws + L.qg_off;
+  void* attn = ws + L.attn_off;
+  float* z = (float*)(ws + L.z_off);
+  float* h1f = (float*)(ws + L.h1f_off);
+  void* h1t = ws + L.h1t_off;
+  void* u = ws + L.u_off;
+
+  auto gemm = [&](int epi, const void* A, int lda, int a_group, int a_group_stride,
+                  const void* Wt, int ldw, const void* bias, int Mr, int N, int K) {
+    lf::GemmArgs g;
+    memset(&g, 0, sizeof g);
+    g.dtype = dtype; g.epi = epi;
+    g.a = A; g.lda = lda; g.a_group = a_group; g.a_group_stride = a_group_stride;
+    g.w = Wt; g.ldw = ldw; g.bias = bias;
+    g.M = Mr; g.N = N; g.K = K;
+    g.D = D; g.H = H; g.rows = S;
+    return g;
+  };
+  hipError_t he;
+  // step 1: packed projections, split into heads ([B, H, S, 64] each)
+  {
+    lf::GemmArgs g = gemm(lf::kEpiHeads, x, D, 0, 0, w->w_proj, D, w->b_proj, M, 5 * D, D);
+    for (int i = 0; i < 5; ++i) g.heads[i] = qkv[i];
+    if ((he = lf::launch_gemm(g, st)) != hipSuccess) return hip_fail(he, "projection GEMM");
+  }
+  // the global queries: rows 0 .. G-1 of every sequence
+  if (G > 0) {
+    lf::GemmArgs g = gemm(lf::kEpiHeads, x, D, G, S, w->w_qg, D, w->b_qg, B * G, D, D);
+    g.heads[0] = qg;
+    g.rows = G;
+    if ((he = lf::launch_gemm(g, st)) != hipSuccess) return hip_fail(he, "global-query GEMM");
+  }
+  // steps 3-4: attention, heads joined ([B, S, H * 64])
+  {
+    AttnWs aw = attn_ws(B, H, S, G);
+    lf::AttnArgs a = make_args(dtype, qkv[0], qkv[1], qkv[2], qg, qkv[3], qkv[4], mk.gidx,
+                               mk.gcnt, mk.bias, B, H, S, W, G, attn, ws, aw, aw.partials_off);
+    a.raw = mk.raw ? 1 : 0;
+    a.local_mask = mk.local_mask;
+    a.global_mask = mk.global_mask;
+    a.out_ss = D;
+    a.out_sh = 64;
+    a.out_sb = (int64_t)S * D;
+    a.scale = attn_scale;
+    if ((he = lf::launch_attention(a, st)) != hipSuccess) return hip_fail(he, "attention");
+  }
+  // step 5: output projection + bias + residual (fp32), LayerNorm
+  {
+    lf::GemmArgs g = gemm(lf::kEpiResidT, attn, D, 0, 0, w->w_o, D, w->b_o, M, D, D);
+    g.out = z; g.ldo = D; g.resid = x; g.ldr = D;
+    if ((he = lf::launch_gemm(g, st)) != hipSuccess) return hip_fail(he, "output GEMM");
+    if ((he = lf::launch_layernorm(dtype, z, w->ln1_g, w->ln1_b, ln_eps, M, D, h1f, h1t, st)) !=
+        hipSuccess)
+      return hip_fail(he, "LayerNorm 1");
+  }
+  // step 6: FFN with GELU, second GEMM + bias + residual (fp32), LayerNorm
+  {
+    lf::GemmArgs g = gemm(lf::kEpiGelu, h1t, D, 0, 0, w->w_ffn1, D, w->b_ffn1, M, ffn, D);
+    g.out = u; g.ldo = ffn;
+    if ((he = lf::launch_gemm(g, st)) != hipSuccess) return hip_fail(he, "FFN GEMM 1");
+    lf::GemmArgs g2 = gemm(lf::kEpiResidF32, u, ffn, 0, 0, w->w_ffn2, ffn, w->b_ffn2, M, D, ffn);
+    g2.out = z; g2.ldo = D; g2.resid = h1f; g2.ldr = D;
+    if ((he = lf::launch_gemm(g2, st)) != hipSuccess) return hip_fail(he, "FFN GEMM 2");
+    if ((he = lf::launch_layernorm(dtype, z, w->ln2_g, w->ln2_b, ln_eps, M, D, nullptr, y, st)) !=
+        hipSuccess)
+      return hip_fail(he, "LayerNorm 2");
+  }
+  return LF_OK;
+}
+
 // Workspace of lf_attn_forward (fp16 / bf16), cached per (device, stream): the
 // split tickets [ticket_cap ints, zeroed when allocated and left zero by every
 // call] followed by the partial states.  Calls on one stream are ordered, so they
@@ -464,93 +596,58 @@ int lf_encoder_layer(int dtype, const lf_layer_weights* w, const void* x, const 
                      int G, float attn_scale, float ln_eps, void* y, void* workspace,
                      size_t ws_bytes, void* stream) {
   if (int e = validate_layer(dtype, B, S, hidden, H, ffn, W, G)) return e;
-  if (!w) return fail(LF_ERR_INVALID_ARGUMENT, "null pointer: weights");
-  if (int e = null_check("x,local_mask,global_mask,y,workspace,w_proj,b_proj,w_o,b_o,ln1_g,"
-                         "ln1_b,w_ffn1,b_ffn1,w_ffn2,b_ffn2,ln2_g,ln2_b",
-                         {x, local_mask, global_mask, y, workspace, w->w_proj, w->b_proj, w->w_o,
-                          w->b_o, w->ln1_g, w->ln1_b, w->w_ffn1, w->b_ffn1, w->w_ffn2, w->b_ffn2,
-                          w->ln2_g, w->ln2_b}))
-    return e;
-  if (G > 0 && (!w->w_qg || !w->b_qg))
-    return fail(LF_ERR_INVALID_ARGUMENT, "null pointer: w_qg / b_qg (G > 0)");
+  if (int e = check_layer_call(w, G, x, local_mask, global_mask, y, workspace)) return e;
   const LayerWs L = layer_ws(dtype, B, S, hidden, H, ffn, G);
-  if (ws_bytes < L.total)
-    return fail(LF_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu bytes", ws_bytes, L.total);
-  if ((uintptr_t)workspace % 256 != 0)
-    return fail(LF_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
-  if (!(attn_scale > 0.0f) || !(ln_eps > 0.0f))
-    return fail(LF_ERR_INVALID_ARGUMENT, "attn_scale and ln_eps must be > 0");
+  if (int e = check_layer_ws(workspace, ws_bytes, L.total, attn_scale, ln_eps)) return e;
+  LayerMasks mk;
+  mk.raw = true;
+  mk.local_mask = local_mask;
+  mk.global_mask = global_mask;
+  return run_layer(dtype, w, x, mk, B, S, hidden, H, ffn, W, G, attn_scale, ln_eps, y,
+                   (char*)workspace, L, (hipStream_t)stream);
+}
+
+size_t lf_encoder_forward_workspace_bytes(int dtype, int B, int S, int hidden, int H, int ffn,
+                                          int W, int G) {
+  if (validate_layer(dtype, B, S, hidden, H, ffn, W, G) != LF_OK) return 0;
+  return stack_ws(dtype, B, S, hidden, H, ffn, G).total;
+}
+
+int lf_encoder_forward(int dtype, const lf_layer_weights* w, int n_layers, const void* x,
+                       const void* local_mask, const void* global_mask, int B, int S, int hidden,
+                       int H, int ffn, int W, int G, float attn_scale, float ln_eps, void* y,
+                       void* workspace, size_t ws_bytes, void* stream) {
+  if (int e = validate_layer(dtype, B, S, hidden, H, ffn, W, G)) return e;
+  if (n_layers < 1) return fail(LF_ERR_INVALID_ARGUMENT, "n_layers must be >= 1 (got %d)", n_layers);
+  if (!w) return fail(LF_ERR_INVALID_ARGUMENT, "null pointer: weights");
+  for (int l = 0; l < n_layers; ++l)
+    if (int e = check_layer_call(&w[l], G, x, local_mask, global_mask, y, workspace)) return e;
+  const StackWs SW = stack_ws(dtype, B, S, hidden, H, ffn, G);
+  if (int e = check_layer_ws(workspace, ws_bytes, SW.total, attn_scale, ln_eps)) return e;
   hipStream_t st = (hipStream_t)stream;
   char* ws = (char*)workspace;
-  const int M = B * S, D = hidden;
-  void* qkv[5];
-  for (int i = 0; i < 5; ++i) qkv[i] = ws + L.qkv_off + (size_t)i * L.act_bytes;
-  void* qg = ws + L.qg_off;
-  void* attn = ws + L.attn_off;
-  float* z = (float*)(ws + L.z_off);
-  float* h1f = (float*)(ws + L.h1f_off);
-  void* h1t = ws + L.h1t_off;
-  void* u = ws + L.u_off;
-
-  auto gemm = [&](int epi, const void* A, int lda, int a_group, int a_group_stride,
-                  const void* Wt, int ldw, const void* bias, int Mr, int N, int K) {
-    lf::GemmArgs g;
-    memset(&g, 0, sizeof g);
-    g.dtype = dtype; g.epi = epi;
-    g.a = A; g.lda = lda; g.a_group = a_group; g.a_group_stride = a_group_stride;
-    g.w = Wt; g.ldw = ldw; g.bias = bias;
-    g.M = Mr; g.N = N; g.K = K;
-    g.D = D; g.H = H; g.rows = S;
-    return g;
-  };
-  hipError_t he;
-  // step 1: packed projections, split into heads ([B, H, S, 64] each)
-  {
-    lf::GemmArgs g = gemm(lf::kEpiHeads, x, D, 0, 0, w->w_proj, D, w->b_proj, M, 5 * D, D);
-    for (int i = 0; i < 5; ++i) g.heads[i] = qkv[i];
-    if ((he = lf::launch_gemm(g, st)) != hipSuccess) return hip_fail(he, "projection GEMM");
-  }
-  // the global queries: rows 0 .. G-1 of every sequence
-  if (G > 0) {
-    lf::GemmArgs g = gemm(lf::kEpiHeads, x, D, G, S, w->w_qg, D, w->b_qg, B * G, D, D);
-    g.heads[0] = qg;
-    g.rows = G;
-    if ((he = lf::launch_gemm(g, st)) != hipSuccess) return hip_fail(he, "global-query GEMM");
-  }
-  // steps 3-4: attention, heads joined ([B, S, H * 64])
-  {
-    AttnWs aw = attn_ws(B, H, S, G);
-    lf::AttnArgs a = make_args(dtype, qkv[0], qkv[1], qkv[2], qg, qkv[3], qkv[4], nullptr, nullptr,
-                               nullptr, B, H, S, W, G, attn, ws, aw, aw.partials_off);
-    a.raw = 1;
-    a.local_mask = local_mask;
-    a.global_mask = global_mask;
-    a.out_ss = D;
-    a.out_sh = 64;
-    a.out_sb = (int64_t)S * D;
-    a.scale = attn_scale;
-    if ((he = lf::launch_attention(a, st)) != hipSuccess) return hip_fail(he, "attention");
-  }
-  // step 5: output projection + bias + residual (fp32), LayerNorm
-  {
-    lf::GemmArgs g = gemm(lf::kEpiResidT, attn, D, 0, 0, w->w_o, D, w->b_o, M, D, D);
-    g.out = z; g.ldo = D; g.resid = x; g.ldr = D;
-    if ((he = lf::launch_gemm(g, st)) != hipSuccess) return hip_fail(he, "output GEMM");
-    if ((he = lf::launch_layernorm(dtype, z, w->ln1_g, w->ln1_b, ln_eps, M, D, h1f, h1t, st)) !=
-        hipSuccess)
-      return hip_fail(he, "LayerNorm 1");
-  }
-  // step 6: FFN with GELU, second GEMM + bias + residual (fp32), LayerNorm
-  {
-    lf::GemmArgs g = gemm(lf::kEpiGelu, h1t, D, 0, 0, w->w_ffn1, D, w->b_ffn1, M, ffn, D);
-    g.out = u; g.ldo = ffn;
-    if ((he = lf::launch_gemm(g, st)) != hipSuccess) return hip_fail(he, "FFN GEMM 1");
-    lf::GemmArgs g2 = gemm(lf::kEpiResidF32, u, ffn, 0, 0, w->w_ffn2, ffn, w->b_ffn2, M, D, ffn);
-    g2.out = z; g2.ldo = D; g2.resid = h1f; g2.ldr = D;
-    if ((he = lf::launch_gemm(g2, st)) != hipSuccess) return hip_fail(he, "FFN GEMM 2");
-    if ((he = lf::launch_layernorm(dtype, z, w->ln2_g, w->ln2_b, ln_eps, M, D, nullptr, y, st)) !=
-        hipSuccess)
-      return hip_fail(he, "LayerNorm 2");
+  // preprocessing once for every layer ([FT-LF] computation flow: the global-token
+  // index and the local-mask shift are computed before the layer loop)
+  int32_t* gidx = (int32_t*)(ws + SW.gidx_off);
+  int32_t* gcnt = (int32_t*)(ws + SW.gcnt_off);
+  LayerMasks mk;
+  mk.raw = false;
+  mk.gidx = gidx;
+  mk.gcnt = gcnt;
+  mk.bias = ws + SW.bias_off;
+  hipError_t he = lf::launch_prep(dtype, global_mask, local_mask, B, S, gidx, gcnt,
+                                  ws + SW.bias_off, nullptr, 0, st);
+  if (he != hipSuccess) return hip_fail(he, "preprocessing");
+  // the layer outputs alternate between y and one activation buffer, so that the
+  // last layer writes y and x is never written
+  void* act = ws + SW.act_off;
+  const void* in = x;
+  for (int l = 0; l < n_layers; ++l) {
+    void* out = ((n_layers - 1 - l) % 2 == 0) ? y : act;
+    if (int e = run_layer(dtype, &w[l], in, mk, B, S, hidden, H, ffn, W, G, attn_scale, ln_eps,
+                          out, ws, SW.layer, st))
+      return e;
+    in = out;
   }
   return ok();
 }

@@ -3,6 +3,7 @@
     python sparse_long_sequence_amd/perf.py attn  [--iters N]   # longformer-large attention
     python sparse_long_sequence_amd/perf.py prep  [--iters N]   # index compaction + mask shift
     python sparse_long_sequence_amd/perf.py layer [--iters N]   # one fp16 encoder layer
+    python sparse_long_sequence_amd/perf.py stack [--iters N]   # 24-layer fp16 encoder, B1 S1024
 
 Prints one JSON line per run: time per call (HIP events on the current stream around
 N back-to-back calls after a warm-up) and the algorithmic throughput.  This is the
@@ -93,14 +94,53 @@ def run_layer(iters: int, warmup: int) -> dict:
             "tflops": (gemm + attn) / (ms * 1e-3) / 1e12}
 
 
+def run_stack(iters: int, warmup: int, n_layers: int = 24) -> dict:
+    # the pages' benchmark model: 16 heads x 64, FFN 4096, window 512, 24 layers, at
+    # batch 1 and sequence 1024; 16 leading global tokens (the count is not stated)
+    B, S, D, H, F, W, G = 1, 1024, 1024, 16, 4096, 512, 16
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20260006)
+    dt = torch.float16
+
+    def rnd(*shape, std=0.02):
+        return (torch.randn(*shape, generator=gen, device="cuda") * std).to(dt)
+
+    layers = []
+    for _ in range(n_layers):
+        w = {"w_proj": rnd(5 * D, D), "w_qg": rnd(D, D), "w_o": rnd(D, D),
+             "w_ffn1": rnd(F, D), "w_ffn2": rnd(D, F)}
+        for n, size in (("b_proj", 5 * D), ("b_qg", D), ("b_o", D), ("b_ffn1", F), ("b_ffn2", D)):
+            w[n] = torch.zeros(size, dtype=dt, device="cuda")
+        for n in ("ln1", "ln2"):
+            w[n + "_g"] = torch.ones(D, dtype=dt, device="cuda")
+            w[n + "_b"] = torch.zeros(D, dtype=dt, device="cuda")
+        layers.append(w)
+    x = torch.randn(B, S, D, generator=gen, device="cuda").to(dt)
+    lm = torch.ones(B, S, dtype=dt, device="cuda")
+    gm = torch.full((B, S), -10000.0, dtype=dt, device="cuda")
+    gm[:, :G] = 0.0
+    y = torch.empty_like(x)
+    nbytes = lf.encoder_forward_workspace_bytes(dt, B, S, D, H, F, W, G)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    ms = _time(lambda: lf.encoder_forward(x, layers, lm, gm, H, W, G, out=y, workspace=ws),
+               iters, warmup)
+    M = B * S
+    gemm = 2.0 * M * D * (5 * D + D + 2 * F) + 2.0 * B * G * D * D
+    pairs = G * S + (S - G) * (W + 1 + G) - (W // 2) * (W // 2 + 1)
+    attn = 256.0 * pairs * B * H
+    return {"op": "encoder_forward", "workload": f"longformer_large_24L_fp16_B{B}_S{S}_W{W}_G{G}",
+            "layers": n_layers, "ms": ms, "ms_per_layer": ms / n_layers,
+            "tflops": n_layers * (gemm + attn) / (ms * 1e-3) / 1e12}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("op", choices=["attn", "prep", "layer"])
+    ap.add_argument("op", choices=["attn", "prep", "layer", "stack"])
     ap.add_argument("--iters", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     a = ap.parse_args()
-    fn = {"attn": run_attn, "prep": run_prep, "layer": run_layer}[a.op]
+    fn = {"attn": run_attn, "prep": run_prep, "layer": run_layer, "stack": run_stack}[a.op]
     print(json.dumps(fn(a.iters, a.warmup)), flush=True)
 
 
