@@ -560,15 +560,25 @@ __device__ inline int xcd_remap(int i, int n) {
 
 // Number of global tokens of batch row b: raw mode counts the zeros among the first
 // G global-mask values (the tokens are leading, so this is their number); pre mode
-// reads global_count.
+// reads global_count.  In raw mode the first kThreads mask values are loaded by
+// count_load before any other load of the workgroup (vector loads complete in order,
+// so a later wait on it does not wait for the staging loads); count_globals adds the
+// rest, if any, and reduces.
 template <typename T, bool RAW>
-__device__ inline int count_globals(const AttnArgs& a, int b) {
+__device__ inline T count_load(const AttnArgs& a, int b) {
+  const T* gm = (const T*)a.global_mask + (size_t)b * a.S;
+  const int t = threadIdx.x;
+  return RAW && t < a.G ? gm[t] : Elem<T>::from_f(1.0f);
+}
+
+template <typename T, bool RAW>
+__device__ inline int count_globals(const AttnArgs& a, int b, T first) {
   if (!RAW) return min(a.gcnt[b], a.G);
   __shared__ int s_cnt;
   if (threadIdx.x == 0) s_cnt = 0;
   const T* gm = (const T*)a.global_mask + (size_t)b * a.S;
-  int cnt = 0;
-  for (int s = threadIdx.x; s < a.G; s += kThreads) cnt += Elem<T>::to_f(gm[s]) == 0.0f;
+  int cnt = Elem<T>::to_f(first) == 0.0f;
+  for (int s = threadIdx.x + kThreads; s < a.G; s += kThreads) cnt += Elem<T>::to_f(gm[s]) == 0.0f;
   __syncthreads();
   if (cnt) atomicAdd(&s_cnt, cnt);
   __syncthreads();
@@ -661,9 +671,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   c.kgh = split ? (const T*)a.kg + head : c.kh;
   c.vgh = split ? (const T*)a.vg + head : c.vh;
 
-  // every load the prologue needs is issued before anything waits: the first round
-  // of the global-row split (split tiles), the first ring entries, Q, the register
-  // sets
+  // every load the prologue needs is issued before anything waits: the global-mask
+  // values, the first round of the global-row split (split tiles), the first ring
+  // entries, Q, the register sets
+  const T gfirst = count_load<T, RAW>(a, c.b);
+  __builtin_amdgcn_sched_barrier(0);
   Stage<T> spl[kSplitEnt];
   if (split) {
 #pragma unroll
@@ -688,7 +700,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     load_entry<T>(st[(kAhead + u) % kDepth], c, kAhead + u);
     __builtin_amdgcn_sched_barrier(0);
   }
-  c.nb = count_globals<T, RAW>(a, c.b);
+  c.nb = count_globals<T, RAW>(a, c.b, gfirst);
   // the split of the global rows first: its loads were issued first, and its
   // results are waited for only at the ticket, after the band work
   if (split && c.nb > 0) global_split_run<T, RAW>(a, c, c.tile, ring, spl);
