@@ -25,9 +25,11 @@
 // where band entry j holds keys r0 - W/2 + 64j ..; row group rg needs band blocks
 // 2rg .. 2rg + nband (nband = (W + 63) / 32), i.e. band entries rg .. rg + npb - 1.
 // At step t every wave reads entry t (global phase) or t + rg (band phase: the row
-// groups walk the band on a diagonal, so none of them idles); entry t + 7 is written
-// into the ring from registers and the loads of entry t + 9 are issued.  One
-// barrier per step, i.e. per 64 keys.
+// groups walk the band on a diagonal, so none of them idles); entry t + 4 is written
+// into the ring from registers and the loads of entry t + 6 are issued.  One
+// barrier per step, i.e. per 64 keys.  Writing only one entry ahead of the read
+// window keeps the workgroups' first loads small (entries 0..3 and Q), so the HBM
+// traffic spreads over the loop instead of arriving as one burst at the start.
 //
 // Per 32-key block and wave: S^T = K Q^T (4 x v_mfma_f32_32x32x16, accumulator
 // initialised with the per-key term, so dead keys cost no vector work), so each
@@ -60,8 +62,8 @@ constexpr int kBlk = 32;             // keys per MFMA block
 constexpr int kEnt = 64;             // keys per ring entry (two blocks)
 constexpr int kKld = 72;             // LDS row pitch of K (elements): 144 B, conflict-free reads
 constexpr int kVld = 72;             // LDS row pitch of V^T (elements): 144 B, conflict-free reads
-constexpr int kRing = 8;             // LDS entry slots
-constexpr int kAhead = 7;            // entry t + kAhead is written at step t
+constexpr int kRing = 8;             // LDS entry slots (the global-row split merges 8 wave states)
+constexpr int kAhead = 4;            // entry t + kAhead is written at step t
 constexpr int kDepth = 2;            // register sets of loads in flight
 constexpr int kStPitch = 67;         // floats per row of a wave state in LDS: m, l, o[64], pad
 constexpr int kMaxSplit = 32;        // at most this many key splits per (b, h)
@@ -589,8 +591,8 @@ __device__ inline int count_globals(const AttnArgs& a, int b, T first) {
 // (K, V^T and per-key terms of both blocks), then QK^T, the band mask on edge
 // steps only, one running-max update for the 64 keys, P, PV, then the staging of
 // entry t + kAhead and the loads of entry t + kAhead + kDepth, then the barrier.
-// Entries t .. t + 3 are read during the step and t + 7 is written, into the slot
-// of entry t - 1.
+// Entries t .. t + 3 are read during the step and t + 4 is written (its slot was last
+// read at step t - 4).
 template <typename T, bool RAW>
 __device__ __forceinline__ void band_step(const Ctx<T>& c, Slot<T>* ring, int tt, int rg, int sb,
                                           float c2, Stage<T>& set,
