@@ -44,8 +44,8 @@
 // keys, 32 per wave per round) before their band work (its first loads go out with
 // the band's): the eight wave states are merged in LDS and one partial
 // (m, l, o[64]) per row is published with write-through stores (coherent across
-// XCDs without cache maintenance).  After its band work the workgroup takes an
-// atomic ticket, and the one that completes the (b, h) reads all partials with
+// XCDs without cache maintenance).  Then the workgroup takes an atomic ticket; after
+// its band work, the one whose ticket completed the (b, h) reads all partials with
 // coherent loads, writes the global rows and resets the ticket.
 #include "lf_device.h"
 #include "lf_internal.h"
@@ -376,13 +376,14 @@ __device__ inline void store_entry(Slot<T>& sl, const Stage<T>& s, const Ctx<T>&
 // kWaves blocks (one per wave, four entries), then the wave states are merged in
 // LDS and one partial (m, l, o[64]) per row is published with write-through
 // stores.  The first round of the first query block arrives already loaded
-// (`first`, issued with the workgroup's first loads); the stores are waited for
-// only at the ticket, after the band work.
+// (`first` and `qf0`, issued with the workgroup's first loads; `qf0` holds rows
+// 0 .. 31 below G, and rows from n_b on are computed but not published).
 constexpr int kSplitEnt = kWaves * kBlk / kEnt;   // entries per round
 
 template <typename T, bool RAW>
 __device__ void global_split_run(const AttnArgs& a, const Ctx<T>& c, int sp, Slot<T>* ring,
-                                 const Stage<T> first[kSplitEnt]) {
+                                 const Stage<T> first[kSplitEnt],
+                                 const typename Frag<T>::v8 qf0[4]) {
   typedef typename Frag<T>::v8 v8;
   const int t = threadIdx.x;
   const int lane = lane_id();
@@ -399,7 +400,12 @@ __device__ void global_split_run(const AttnArgs& a, const Ctx<T>& c, int sp, Slo
   for (int qb = 0; qb * 32 < nb; ++qb) {
     v8 qf[4];
     const int r = 32 * qb + n;
-    load_q<T>(qf, qgh + (size_t)(r < nb ? r : 0) * 64, r < nb);
+    if (qb == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) qf[i] = qf0[i];
+    } else {
+      load_q<T>(qf, qgh + (size_t)(r < nb ? r : 0) * 64, r < nb);
+    }
     f32x16 o[2] = {f32x16{}, f32x16{}};
     float m_run = kNegBig, l_run = 0.0f;
     for (int u = 0; u < n_rounds; ++u) {
@@ -475,24 +481,27 @@ __device__ void global_split_run(const AttnArgs& a, const Ctx<T>& c, int sp, Slo
   }
 }
 
-// Ticket of a split workgroup, taken after its band work: by then its partial
-// stores (write-through) have long completed.  The workgroup that completes the
-// (b, h) merges every split's partial and writes the global rows: thread per (row,
-// 4 dims); the (m, l) and o of 16 splits per round are loaded together with
-// coherent (sc1) loads, splits past n_split read out of range and get weight 0.
+// Ticket of a split workgroup, taken right after its partial is published: every
+// wave waits for its write-through stores, then one atomic increment.  The old
+// value (thread 0) is first looked at after the band work, so the atomic's round
+// trip is hidden behind it.
+template <typename T>
+__device__ inline int take_ticket(const AttnArgs& a, const Ctx<T>& c) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  int old = 0;
+  if (threadIdx.x == 0)
+    old = __hip_atomic_fetch_add(a.counters + c.bh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return old;
+}
+
+// Run by the workgroup whose ticket completed the (b, h): merges every split's
+// partial and writes the global rows, thread per (row, 4 dims); the (m, l) and o of
+// 16 splits per round are loaded together with coherent (sc1) loads, splits past
+// n_split read out of range and get weight 0.
 template <typename T, bool RAW>
 __device__ void global_combine(const AttnArgs& a, const Ctx<T>& c) {
   const int t = threadIdx.x;
-  __shared__ int s_last;
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (t == 0) {
-    const int old = __hip_atomic_fetch_add(a.counters + c.bh, 1, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-    s_last = old == a.n_split - 1;
-  }
-  __syncthreads();
-  if (!s_last) return;
   const int G = c.G, nb = c.nb, ns = a.n_split;
   const float* pbase = a.partials + (size_t)c.bh * ns * (size_t)G * kPartPitch;
   const rsrc_t rall = make_rsrc(pbase, (uint32_t)ns * G * kPartPitch * 4u);
@@ -560,31 +569,32 @@ __device__ inline int xcd_remap(int i, int n) {
   return (i % 8) * per + i / 8;
 }
 
-// Number of global tokens of batch row b: raw mode counts the zeros among the first
-// G global-mask values (the tokens are leading, so this is their number); pre mode
-// reads global_count.  In raw mode the first kThreads mask values are loaded by
-// count_load before any other load of the workgroup (vector loads complete in order,
-// so a later wait on it does not wait for the staging loads); count_globals adds the
-// rest, if any, and reduces.
+// Number of global tokens of batch row b: raw mode counts the zeros (+0 or -0: the
+// bits other than the sign are clear, in fp16 and bf16 alike) among the first G
+// global-mask values (the tokens are leading, so this is their number); pre mode reads
+// global_count.  Every wave counts for itself with ballots, so no barrier is needed:
+// count_load issues the first load (the first 64 mask values, one per lane) before
+// any other load of the workgroup, and since vector loads complete in order, the wait
+// in count_globals does not wait for the staging loads issued after it.
 template <typename T, bool RAW>
-__device__ inline T count_load(const AttnArgs& a, int b) {
-  const T* gm = (const T*)a.global_mask + (size_t)b * a.S;
-  const int t = threadIdx.x;
-  return RAW && t < a.G ? gm[t] : Elem<T>::from_f(1.0f);
+__device__ inline int count_load(const AttnArgs& a, int b) {
+  if (!RAW) return a.gcnt[b];
+  const unsigned short* gm = (const unsigned short*)a.global_mask + (size_t)b * a.S;
+  const int lane = lane_id();
+  return lane < a.G ? gm[lane] : 0x3c00;   // 0x3c00: not a zero
 }
 
 template <typename T, bool RAW>
-__device__ inline int count_globals(const AttnArgs& a, int b, T first) {
-  if (!RAW) return min(a.gcnt[b], a.G);
-  __shared__ int s_cnt;
-  if (threadIdx.x == 0) s_cnt = 0;
-  const T* gm = (const T*)a.global_mask + (size_t)b * a.S;
-  int cnt = Elem<T>::to_f(first) == 0.0f;
-  for (int s = threadIdx.x + kThreads; s < a.G; s += kThreads) cnt += Elem<T>::to_f(gm[s]) == 0.0f;
-  __syncthreads();
-  if (cnt) atomicAdd(&s_cnt, cnt);
-  __syncthreads();
-  return s_cnt;
+__device__ inline int count_globals(const AttnArgs& a, int b, int first) {
+  if (!RAW) return min(first, a.G);
+  const unsigned short* gm = (const unsigned short*)a.global_mask + (size_t)b * a.S;
+  int cnt = __builtin_popcountll(__ballot((first & 0x7fff) == 0));
+  for (int s0 = 64; s0 < a.G; s0 += 64) {
+    const int s = s0 + lane_id();
+    const int x = s < a.G ? gm[s] : 0x3c00;
+    cnt += __builtin_popcountll(__ballot((x & 0x7fff) == 0));
+  }
+  return __builtin_amdgcn_readfirstlane(cnt);
 }
 
 // One step t of a wave: the two 32-key blocks of its entry.  LDS reads first
@@ -676,10 +686,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // every load the prologue needs is issued before anything waits: the global-mask
   // values, the first round of the global-row split (split tiles), the first ring
   // entries, Q, the register sets
-  const T gfirst = count_load<T, RAW>(a, c.b);
+  const int gfirst = count_load<T, RAW>(a, c.b);
   __builtin_amdgcn_sched_barrier(0);
   Stage<T> spl[kSplitEnt];
+  v8 qg0[4];
   if (split) {
+    const int r = n;   // split rows 0 .. 31 below G (rows from n_b on are not published)
+    load_q<T>(qg0, (const T*)a.qg + ((size_t)c.bh * a.G + (r < a.G ? r : 0)) * 64, r < a.G);
 #pragma unroll
     for (int e = 0; e < kSplitEnt; ++e)
       stage_load<T>(spl[e], make_rsrc(c.kgh, (uint32_t)c.S * 128u),
@@ -703,9 +716,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     __builtin_amdgcn_sched_barrier(0);
   }
   c.nb = count_globals<T, RAW>(a, c.b, gfirst);
-  // the split of the global rows first: its loads were issued first, and its
-  // results are waited for only at the ticket, after the band work
-  if (split && c.nb > 0) global_split_run<T, RAW>(a, c, c.tile, ring, spl);
+  // the split of the global rows first (its loads were issued first), then the
+  // ticket, whose value is looked at after the band work
+  int ticket = 0;
+  if (split && c.nb > 0) {
+    global_split_run<T, RAW>(a, c, c.tile, ring, spl, qg0);
+    ticket = take_ticket<T>(a, c);
+  }
 
 #pragma unroll
   for (int i = 0; i < kAhead; ++i) store_entry<T, RAW>(ring[i], pro[i], c, i);
@@ -742,7 +759,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   }
 
-  if (split && c.nb > 0) global_combine<T, RAW>(a, c);
+  if (split && c.nb > 0) {
+    __shared__ int s_last;
+    if (threadIdx.x == 0) s_last = ticket == a.n_split - 1;
+    __syncthreads();
+    if (s_last) global_combine<T, RAW>(a, c);
+  }
 }
 
 template <typename T>
