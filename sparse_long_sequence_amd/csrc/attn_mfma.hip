@@ -25,11 +25,14 @@
 // where band entry j holds keys r0 - W/2 + 64j ..; row group rg needs band blocks
 // 2rg .. 2rg + nband (nband = (W + 63) / 32), i.e. band entries rg .. rg + npb - 1.
 // At step t every wave reads entry t (global phase) or t + rg (band phase: the row
-// groups walk the band on a diagonal, so none of them idles); entry t + 4 is written
-// into the ring from registers and the loads of entry t + 6 are issued.  One
-// barrier per step, i.e. per 64 keys.  Writing only one entry ahead of the read
-// window keeps the workgroups' first loads small (entries 0..3 and Q), so the HBM
-// traffic spreads over the loop instead of arriving as one burst at the start.
+// groups walk the band on a diagonal, so none of them idles); entry t + 5 is written
+// into the ring from registers and the loads of entry t + 7 are issued.  Steps run
+// in pairs with one barrier per pair: an entry written at step t is first read at
+// step t + 2, after the barrier that ends the pair, and the slot it overwrites (that
+// of entry t - 3) was last read before the previous barrier.  Writing only two
+// entries ahead of the read window keeps the workgroups' first loads small (entries
+// 0..4 and Q), so the HBM traffic spreads over the loop instead of arriving as one
+// burst at the start.
 //
 // Per 32-key block and wave: S^T = K Q^T (4 x v_mfma_f32_32x32x16, accumulator
 // initialised with the per-key term, so dead keys cost no vector work), so each
@@ -63,7 +66,7 @@ constexpr int kEnt = 64;             // keys per ring entry (two blocks)
 constexpr int kKld = 72;             // LDS row pitch of K (elements): 144 B, conflict-free reads
 constexpr int kVld = 72;             // LDS row pitch of V^T (elements): 144 B, conflict-free reads
 constexpr int kRing = 8;             // LDS entry slots (the global-row split merges 8 wave states)
-constexpr int kAhead = 4;            // entry t + kAhead is written at step t
+constexpr int kAhead = 5;            // entry t + kAhead is written at step t
 constexpr int kDepth = 2;            // register sets of loads in flight
 constexpr int kStPitch = 67;         // floats per row of a wave state in LDS: m, l, o[64], pad
 constexpr int kMaxSplit = 32;        // at most this many key splits per (b, h)
@@ -600,10 +603,10 @@ __device__ inline int count_globals(const AttnArgs& a, int b, int first) {
 // One step t of a wave: the two 32-key blocks of its entry.  LDS reads first
 // (K, V^T and per-key terms of both blocks), then QK^T, the band mask on edge
 // steps only, one running-max update for the 64 keys, P, PV, then the staging of
-// entry t + kAhead and the loads of entry t + kAhead + kDepth, then the barrier.
-// Entries t .. t + 3 are read during the step and t + 4 is written (its slot was last
-// read at step t - 4).
-template <typename T, bool RAW>
+// entry t + kAhead and the loads of entry t + kAhead + kDepth, then (BAR: second
+// step of a pair) the barrier.  Entries t .. t + 3 are read during the step and
+// t + 5 is written.
+template <typename T, bool RAW, bool BAR>
 __device__ __forceinline__ void band_step(const Ctx<T>& c, Slot<T>* ring, int tt, int rg, int sb,
                                           float c2, Stage<T>& set,
                                           const typename Frag<T>::v8 qf[4], f32x16 o[2],
@@ -639,7 +642,7 @@ __device__ __forceinline__ void band_step(const Ctx<T>& c, Slot<T>* ring, int tt
   store_entry<T, RAW>(ring[e % kRing], set, c, e);
   __builtin_amdgcn_sched_barrier(0);
   load_entry<T>(set, c, e + kDepth);
-  __syncthreads();
+  if (BAR) __syncthreads();
 }
 
 template <typename T, bool RAW>
@@ -733,10 +736,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   constexpr int s0i = kAhead % kDepth, s1i = (kAhead + 1) % kDepth;
   int t0 = 0;
   for (; t0 + 2 <= n_steps; t0 += 2) {
-    band_step<T, RAW>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
-    band_step<T, RAW>(c, ring, t0 + 1, rg, sb, c2, st[s1i], qf, o, m_run, l_run);
+    band_step<T, RAW, false>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
+    band_step<T, RAW, true>(c, ring, t0 + 1, rg, sb, c2, st[s1i], qf, o, m_run, l_run);
   }
-  if (t0 < n_steps) band_step<T, RAW>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
+  if (t0 < n_steps) band_step<T, RAW, false>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
 
   // epilogue: normalise and store the local rows
   {
