@@ -9,11 +9,9 @@ index extraction, mask shift, band + global attention (every step of the path).
 Prints ONE JSON line on stdout.  After W warm-up steps and `--warmup-seconds` of
 further untimed steps (the GPU clocks ramp up over the first second of work), K
 steps are timed between two events: `value` is effective TFLOP/s = algorithmic
-flops (256 per allowed (query, key) pair) / time per step.  The same K steps are then
-run again with HIP events recorded by the library on its launch stream around each
-launch of the dominant kernel (the band + global-row launch); those events slow the
-loop down, so they are kept out of the first pass.  `roofline` reports that kernel
-against the roofline that
+flops (256 per allowed (query, key) pair) / time per step.  A step is one launch of
+the band + global-row kernel, so the same events give that kernel's average launch
+duration.  `roofline` reports that kernel against the roofline that
 binds at its algorithmic intensity (flops / algorithmic bytes vs the ridge point
 2516.6 TFLOP/s / 8 TB/s); the MFMA fraction is reported beside it.  `traffic` is
 the counter-measured HBM bytes per launch from the committed summary, when it was
@@ -36,6 +34,7 @@ sys.path.insert(0, ROOT)
 METRIC = "band+global attention ms and TFLOP/s (% MFMA peak), B=1 H=16 S=4096 W=512 fp16"
 PEAK_FP16_TFLOPS = 2516.6        # MI355X dense fp16 MFMA: 256 CU x 4 SIMD x 1024 flop/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
+LAUNCHES_PER_STEP = 1            # lf_attn_forward on fp16 / bf16 inputs: one kernel launch
 KERNEL_SOURCES = ["sparse_long_sequence_amd/csrc/attn_mfma.hip",
                   "sparse_long_sequence_amd/csrc/lf_device.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_mfma_longformer_large_fp16_traffic.txt")
@@ -151,10 +150,13 @@ def main():
         for _ in range(100):
             step()
         torch.cuda.synchronize()
+    # K steps between two events recorded on the stream the kernel is launched on
+    # (torch's current stream, which the binding passes to the library).  A step is
+    # exactly one kernel launch, so (end - start) / K is also the kernel's average
+    # launch duration (gaps between back-to-back launches included).  Events around
+    # every launch would add several microseconds per launch, so there are none.
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    # pass 1 (the value): K steps with only the two bracketing events, on the stream
-    # the kernel runs on (torch's current stream)
     torch.cuda.synchronize()
     e0.record()
     for _ in range(args.steps):
@@ -162,14 +164,7 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
-    # pass 2 (the roofline): the same K steps with an event pair around every launch
-    # of the attention kernel, recorded by the library on its launch stream; those
-    # events add a few microseconds per step, which is why they stay out of pass 1
-    lf.kernel_timing_start(args.steps)
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    n_k, k_ms = lf.kernel_timing_stop()
+    n_k, k_ms = args.steps * LAUNCHES_PER_STEP, e0.elapsed_time(e1)
     if args.calibrate_copy_mb > 0:
         n = args.calibrate_copy_mb * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -178,7 +173,7 @@ def main():
         torch.mul(src, 1.0, out=dst)   # reads and writes calibrate_copy_mb MiB each
         torch.cuda.synchronize()
         log(f"calibration copy: {args.calibrate_copy_mb} MiB read + {args.calibrate_copy_mb} MiB written")
-    k_avg_ms = k_ms / max(n_k, 1)
+    k_avg_ms = k_ms / n_k
 
     flops = 256.0 * pairs_per_head(wl.S, wl.W, wl.G) * wl.B * wl.H
     tflops = flops / (ms * 1e-3) / 1e12
