@@ -87,15 +87,44 @@ int lf_mask_shift(int dtype, const void* local_mask, int B, int S, void* local_b
  *   - any other row s is softmax over the live keys j with |j - s| <= W/2,
  *     j >= n_b, plus the live global keys j < n_b, of c <q[s], k[j]>, weighting
  *     v[j].  Global keys are therefore counted once.
- * Padding enters as the additive -10000 score bias of the mask shift.  Runs the
- * index extraction and the mask shift itself; needs temporary device memory,
- * taken with hipMallocAsync on `stream` and returned with hipFreeAsync.
- * fp16 / bf16 run on MFMA with fp32 accumulation; fp32 runs on fp32 FMA.
+ * Padding enters as the additive -10000 score bias of the mask shift.  fp16 / bf16:
+ * one launch on MFMA with fp32 accumulation, reading both masks itself; its
+ * global-row partials and split tickets live in one library-owned workspace per
+ * (device, stream), allocated on first use and grown (after a stream
+ * synchronisation) when a larger shape needs it, so concurrent calls must use
+ * distinct streams.  fp32: the index extraction and mask shift into temporary
+ * device memory (hipMallocAsync / hipFreeAsync on `stream`), then fp32 FMA.
  */
 int lf_attn_forward(int dtype, const void* q, const void* k, const void* v,
                     const void* qg, const void* kg, const void* vg,
                     const void* local_mask, const void* global_mask,
                     int B, int H, int S, int W, int G, void* out, void* stream);
+
+/*
+ * Band + global attention with the global tokens at any positions (the global
+ * attention pattern of the Longformer model itself, which the [FT-LF] page names as
+ * the case its head-of-sequence constraint excludes, section "使用前提：四条硬性约束").
+ * Same arguments, layouts, precision and errors as lf_attn_forward, with positions
+ * P_b = the flagged positions of batch row b in ascending order (flag: global_mask
+ * == 0.0), n_b = |P_b| <= G:
+ *   - a row with local_mask 0 is written as +0.0;
+ *   - the global row s = P_b[r] is softmax_j(c <qg[r], kg[j]>) . vg[j] over every
+ *     live key j (qg row r belongs to the r-th global position);
+ *   - any other row s is softmax over the live keys j with |j - s| <= W/2 and j not
+ *     in P_b, plus the live keys of P_b, of c <q[s], k[j]>, weighting v[j].
+ * With leading global tokens this equals lf_attn_forward.  Two launches on `stream`:
+ * the index extraction (as lf_init_global_idx) into library-owned device memory,
+ * then the attention, which gathers the global keys through that index.  The
+ * library keeps one workspace per (device, stream), allocated on first use and
+ * grown when a larger shape needs it (that growth synchronises the stream), so
+ * concurrent calls must use distinct streams.  Data-dependent preconditions (masks
+ * 0/1 and 0/-10000, n_b <= G) are checked only by lf_check_masks or under
+ * LF_DEBUG_CHECK=1, which here skips the head-of-sequence test.
+ */
+int lf_attn_forward_any_globals(int dtype, const void* q, const void* k, const void* v,
+                                const void* qg, const void* kg, const void* vg,
+                                const void* local_mask, const void* global_mask,
+                                int B, int H, int S, int W, int G, void* out, void* stream);
 
 /* Bytes of workspace lf_attn_forward_pre needs for this shape (0 on bad arguments). */
 size_t lf_attn_workspace_bytes(int dtype, int B, int H, int S, int W, int G);

@@ -15,7 +15,8 @@ import os
 import torch
 
 __all__ = ["LFError", "library_path", "load_library", "init_global_idx", "mask_shift",
-           "attn_forward", "attn_forward_pre", "attn_workspace_bytes", "check_masks",
+           "attn_forward", "attn_forward_any_globals", "attn_forward_pre", "attn_workspace_bytes",
+           "check_masks",
            "encoder_layer", "encoder_layer_workspace_bytes", "encoder_forward",
            "encoder_forward_workspace_bytes", "LAYER_WEIGHT_FIELDS",
            "kernel_timing_start", "kernel_timing_stop",
@@ -32,6 +33,7 @@ LAYER_WEIGHT_FIELDS = ["w_proj", "b_proj", "w_qg", "b_qg", "w_o", "b_o", "ln1_g"
                        "w_ffn1", "b_ffn1", "w_ffn2", "b_ffn2", "ln2_g", "ln2_b"]
 
 EXPORTED_SYMBOLS = ["lf_init_global_idx", "lf_mask_shift", "lf_attn_forward",
+                    "lf_attn_forward_any_globals",
                     "lf_attn_workspace_bytes", "lf_attn_forward_pre", "lf_check_masks",
                     "lf_encoder_layer_workspace_bytes", "lf_encoder_layer",
                     "lf_encoder_forward_workspace_bytes", "lf_encoder_forward",
@@ -66,6 +68,7 @@ def load_library():
     lib.lf_init_global_idx.argtypes = [I, P, I, I, P, P, P]
     lib.lf_mask_shift.argtypes = [I, P, I, I, P, P]
     lib.lf_attn_forward.argtypes = [I, P, P, P, P, P, P, P, P, I, I, I, I, I, P, P]
+    lib.lf_attn_forward_any_globals.argtypes = [I, P, P, P, P, P, P, P, P, I, I, I, I, I, P, P]
     lib.lf_attn_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.lf_attn_workspace_bytes.restype = S
     lib.lf_attn_forward_pre.argtypes = [I, P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, P, S, P]
@@ -86,6 +89,7 @@ def load_library():
     lib.lf_last_error.argtypes = []
     lib.lf_last_error.restype = ctypes.c_char_p
     for name in ("lf_init_global_idx", "lf_mask_shift", "lf_attn_forward",
+                 "lf_attn_forward_any_globals",
                  "lf_attn_forward_pre", "lf_check_masks", "lf_encoder_layer",
                  "lf_encoder_forward",
                  "lf_kernel_timing_start", "lf_kernel_timing_stop"):
@@ -181,6 +185,25 @@ def attn_forward(q, k, v, qg, kg, vg, local_mask, global_mask, W: int, G: int, o
     _check(lib.lf_attn_forward(dtype_code(q.dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(qg),
                                _ptr(kg), _ptr(vg), _ptr(local_mask), _ptr(global_mask),
                                B, H, S, W, G, _ptr(out), _stream(dev)))
+    return out
+
+
+def attn_forward_any_globals(q, k, v, qg, kg, vg, local_mask, global_mask, W: int, G: int,
+                             out=None):
+    """Band + global attention with the global tokens at any positions -> out [B,H,S,64]."""
+    lib = load_library()
+    dev = _dev(q, k, v, qg, kg, vg, local_mask, global_mask)
+    B, H, S = _attn_shapes(q, qg, W, G)
+    for t in (k, v, kg, vg):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v, kg, vg must share shape and dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out)
+    _check(lib.lf_attn_forward_any_globals(dtype_code(q.dtype), _ptr(q), _ptr(k), _ptr(v),
+                                           _ptr(qg), _ptr(kg), _ptr(vg), _ptr(local_mask),
+                                           _ptr(global_mask), B, H, S, W, G, _ptr(out),
+                                           _stream(dev)))
     return out
 
 

@@ -117,6 +117,7 @@ struct Stage {
   u32x4 k;
   u32x2 v0, v1;
   unsigned short mask_bits;
+  unsigned short gflag_bits;   // globals-anywhere mode, band entries: global-mask value
 };
 
 // Entry of keys base .. base + 63.  Every thread issues the same four loads, so the
@@ -134,6 +135,26 @@ __device__ inline void stage_load(Stage<T>& s, rsrc_t rk, rsrc_t rv, rsrc_t rm, 
   s.mask_bits = __builtin_amdgcn_raw_buffer_load_b16(rm, t < kEnt ? 2 * (base + t) : -1, 0, 0);
 }
 
+// Globals-anywhere mode: global-key entry of slots slot0 .. slot0 + 63, slot r holding
+// position gi[r].  Slots below G load (the index holds S positions per row, G <= S);
+// slots from n_b on hold ordinary positions and are marked dead when the entry is
+// stored (the loads are issued before n_b is known), slots from G on read position
+// S, out of range, so their loads return zeros.  Same thread mapping as stage_load.
+template <typename T>
+__device__ inline void stage_gather(Stage<T>& s, rsrc_t rk, rsrc_t rv, rsrc_t rm,
+                                   const int32_t* __restrict__ gi, int slot0, int G, int S) {
+  const int t = threadIdx.x;
+  const int sk = slot0 + (t >> 3), sv = slot0 + 2 * (t >> 4), sm = slot0 + (t & 63);
+  const int pk = sk < G ? gi[sk] : S;
+  const int pv0 = sv < G ? gi[sv] : S;
+  const int pv1 = sv + 1 < G ? gi[sv + 1] : S;
+  const int pm = sm < G ? gi[sm] : S;
+  s.k = __builtin_amdgcn_raw_buffer_load_b128(rk, pk * 128 + 16 * (t & 7), 0, 0);
+  s.v0 = __builtin_amdgcn_raw_buffer_load_b64(rv, pv0 * 128 + 8 * (t & 15), 0, 0);
+  s.v1 = __builtin_amdgcn_raw_buffer_load_b64(rv, pv1 * 128 + 8 * (t & 15), 0, 0);
+  s.mask_bits = __builtin_amdgcn_raw_buffer_load_b16(rm, t < kEnt ? 2 * pm : -1, 0, 0);
+}
+
 // Position of key kk (0..63) inside a V^T row: within each 16-key group, lane group
 // g of the PV MFMA needs keys 4g .. 4g+3 and 8+4g .. 8+4g+3 (the row order of the
 // score fragment), so those eight are stored together and read as 16 bytes.
@@ -141,9 +162,12 @@ __device__ inline int vt_pos(int kk) {
   return (kk & 48) + (kk & 3) + 4 * ((kk >> 3) & 1) + 8 * ((kk >> 2) & 1);
 }
 
-// Write a staged entry; key base + j is live iff lo <= key < hi and its mask says so.
+// Write a staged entry; key base + j is live iff lo <= key < hi and its mask says so
+// (and, with excl_glob, its global-mask value is not zero: a global position is not
+// a band key).
 template <typename T, bool RAW>
-__device__ inline void stage_store(Slot<T>& sl, const Stage<T>& s, int base, int lo, int hi) {
+__device__ inline void stage_store(Slot<T>& sl, const Stage<T>& s, int base, int lo, int hi,
+                                   bool excl_glob = false) {
   const int t = threadIdx.x;
   *(u32x4*)&sl.k[(t >> 3) * kKld + 8 * (t & 7)] = s.k;
   // dims 4c .. 4c+3 of keys 2vp, 2vp+1 -> V^T rows 4c .. 4c+3, one dword (a key pair)
@@ -159,7 +183,8 @@ __device__ inline void stage_store(Slot<T>& sl, const Stage<T>& s, int base, int
     const int lane = lane_id();
     const int key = base + lane;
     const bool live = key >= lo && key < hi &&
-                      mask_live<RAW>(Elem<T>::to_f(__builtin_bit_cast(T, s.mask_bits)));
+                      mask_live<RAW>(Elem<T>::to_f(__builtin_bit_cast(T, s.mask_bits))) &&
+                      !(excl_glob && (s.gflag_bits & 0x7fff) == 0);
     sl.bias2[lane] = live ? 0.0f : -INFINITY;
   }
 }
@@ -347,6 +372,8 @@ struct Ctx {
   const T *kh, *vh;          // k, v of this head
   const T *kgh, *vgh;        // kg, vg of this head (split tiles; else k, v)
   const T* mask;             // that mask row (raw local mask, or the shifted one)
+  const int32_t* gi;         // globals-anywhere mode: global positions of batch row b
+  const unsigned short* gm;  // globals-anywhere mode: global-mask row b (raw bits)
 };
 
 // List entry i: global-key entry i (positions 64i.., live below n_b; under the
@@ -360,18 +387,33 @@ __device__ inline int entry_base(const Ctx<T>& c, int i) {
   return i < n_list ? base : S;
 }
 
-template <typename T>
+// ANY (globals-anywhere mode): global-key entries gather the global positions
+// through the index, band entries also load the global-mask values of their keys.
+template <typename T, bool ANY>
 __device__ inline void load_entry(Stage<T>& s, const Ctx<T>& c, int i) {
   const uint32_t bytes = (uint32_t)c.S * 128u;
-  stage_load<T>(s, make_rsrc(c.kh, bytes), make_rsrc(c.vh, bytes),
-                make_rsrc(c.mask, (uint32_t)c.S * 2u), entry_base(c, i));
+  const rsrc_t rk = make_rsrc(c.kh, bytes), rv = make_rsrc(c.vh, bytes);
+  const rsrc_t rm = make_rsrc(c.mask, (uint32_t)c.S * 2u);
+  if (ANY && i < c.ngp) {
+    stage_gather<T>(s, rk, rv, rm, c.gi, kEnt * i, c.G, c.S);
+    return;
+  }
+  const int base = entry_base(c, i);
+  stage_load<T>(s, rk, rv, rm, base);
+  if (ANY) {
+    const int t = threadIdx.x;
+    s.gflag_bits = __builtin_amdgcn_raw_buffer_load_b16(make_rsrc(c.gm, (uint32_t)c.S * 2u),
+                                                        t < kEnt ? 2 * (base + t) : -1, 0, 0);
+  }
 }
 
-template <typename T, bool RAW>
+template <typename T, bool RAW, bool ANY>
 __device__ inline void store_entry(Slot<T>& sl, const Stage<T>& s, const Ctx<T>& c, int i) {
   const int nb = c.nb, S = c.S;
   const bool glob = i < c.ngp;
-  stage_store<T, RAW>(sl, s, entry_base(c, i), glob ? 0 : nb, glob ? nb : S);
+  // band keys: from n_b on when the globals lead, anywhere but the global positions
+  // otherwise
+  stage_store<T, RAW>(sl, s, entry_base(c, i), glob || ANY ? 0 : nb, glob ? nb : S, ANY && !glob);
 }
 
 // ------------------------------------------------------------------ global rows
@@ -383,7 +425,10 @@ __device__ inline void store_entry(Slot<T>& sl, const Stage<T>& s, const Ctx<T>&
 // 0 .. 31 below G, and rows from n_b on are computed but not published).
 constexpr int kSplitEnt = kWaves * kBlk / kEnt;   // entries per round
 
-template <typename T, bool RAW>
+// ANY is unused in the body: it gives each kernel instantiation a copy of its own
+// (with one copy shared by the two raw-mask kernels, the compiler allocated the
+// leading-globals kernel's prologue registers worse: 14 spilled VGPRs instead of 1).
+template <typename T, bool RAW, bool ANY>
 __device__ void global_split_run(const AttnArgs& a, const Ctx<T>& c, int sp, Slot<T>* ring,
                                  const Stage<T> first[kSplitEnt],
                                  const typename Frag<T>::v8 qf0[4]) {
@@ -502,7 +547,7 @@ __device__ inline int take_ticket(const AttnArgs& a, const Ctx<T>& c) {
 // partial and writes the global rows, thread per (row, 4 dims); the (m, l) and o of
 // 16 splits per round are loaded together with coherent (sc1) loads, splits past
 // n_split read out of range and get weight 0.
-template <typename T, bool RAW>
+template <typename T, bool RAW, bool ANY>
 __device__ void global_combine(const AttnArgs& a, const Ctx<T>& c) {
   const int t = threadIdx.x;
   const int G = c.G, nb = c.nb, ns = a.n_split;
@@ -542,7 +587,7 @@ __device__ void global_combine(const AttnArgs& a, const Ctx<T>& c) {
         O += __builtin_bit_cast(f32x4, pv[j]) * w;
       }
     }
-    const int pos = RAW ? rl : a.gidx[(size_t)c.b * c.S + rl];
+    const int pos = RAW && !ANY ? rl : a.gidx[(size_t)c.b * c.S + rl];
     const float inv = mask_live<RAW>(Elem<T>::to_f(c.mask[pos])) ? 1.0f / L : 0.0f;
     typename Frag<T>::v4 w;
 #pragma unroll
@@ -574,22 +619,22 @@ __device__ inline int xcd_remap(int i, int n) {
 
 // Number of global tokens of batch row b: raw mode counts the zeros (+0 or -0: the
 // bits other than the sign are clear, in fp16 and bf16 alike) among the first G
-// global-mask values (the tokens are leading, so this is their number); pre mode reads
-// global_count.  Every wave counts for itself with ballots, so no barrier is needed:
+// global-mask values (the tokens are leading, so this is their number); pre mode and
+// the globals-anywhere mode read global_count.  Every wave counts for itself with ballots, so no barrier is needed:
 // count_load issues the first load (the first 64 mask values, one per lane) before
 // any other load of the workgroup, and since vector loads complete in order, the wait
 // in count_globals does not wait for the staging loads issued after it.
-template <typename T, bool RAW>
+template <typename T, bool RAW, bool ANY>
 __device__ inline int count_load(const AttnArgs& a, int b) {
-  if (!RAW) return a.gcnt[b];
+  if (!RAW || ANY) return a.gcnt[b];
   const unsigned short* gm = (const unsigned short*)a.global_mask + (size_t)b * a.S;
   const int lane = lane_id();
   return lane < a.G ? gm[lane] : 0x3c00;   // 0x3c00: not a zero
 }
 
-template <typename T, bool RAW>
+template <typename T, bool RAW, bool ANY>
 __device__ inline int count_globals(const AttnArgs& a, int b, int first) {
-  if (!RAW) return min(first, a.G);
+  if (!RAW || ANY) return min(first, a.G);
   const unsigned short* gm = (const unsigned short*)a.global_mask + (size_t)b * a.S;
   int cnt = __builtin_popcountll(__ballot((first & 0x7fff) == 0));
   for (int s0 = 64; s0 < a.G; s0 += 64) {
@@ -606,7 +651,7 @@ __device__ inline int count_globals(const AttnArgs& a, int b, int first) {
 // entry t + kAhead and the loads of entry t + kAhead + kDepth, then (BAR: second
 // step of a pair) the barrier.  Entries t .. t + 3 are read during the step and
 // t + 5 is written.
-template <typename T, bool RAW, bool BAR>
+template <typename T, bool RAW, bool ANY, bool BAR>
 __device__ __forceinline__ void band_step(const Ctx<T>& c, Slot<T>* ring, int tt, int rg, int sb,
                                           float c2, Stage<T>& set,
                                           const typename Frag<T>::v8 qf[4], f32x16 o[2],
@@ -639,13 +684,15 @@ __device__ __forceinline__ void band_step(const Ctx<T>& c, Slot<T>* ring, int tt
   pv_frag<T>(vf0, p0, o);
   pv_frag<T>(vf1, p1, o);
   const int e = tt + kAhead;
-  store_entry<T, RAW>(ring[e % kRing], set, c, e);
+  store_entry<T, RAW, ANY>(ring[e % kRing], set, c, e);
   __builtin_amdgcn_sched_barrier(0);
-  load_entry<T>(set, c, e + kDepth);
+  load_entry<T, ANY>(set, c, e + kDepth);
   if (BAR) __syncthreads();
 }
 
-template <typename T, bool RAW>
+// RAW: read the raw masks (else global_count and the shifted mask); ANY (with RAW):
+// global tokens at any positions, through global_idx / global_count.
+template <typename T, bool RAW, bool ANY>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_mfma_kernel(AttnArgs a, int n_tiles) {
   __shared__ __attribute__((aligned(16))) Slot<T> ring[kRing];
   typedef typename Frag<T>::v8 v8;
@@ -677,6 +724,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   c.n_list = c.ngp + npb + 3;
   const size_t head = (size_t)c.bh * c.S * 64;
   c.mask = (const T*)(RAW ? a.local_mask : a.bias) + (size_t)c.b * c.S;
+  c.gi = ANY ? a.gidx + (size_t)c.b * c.S : nullptr;
+  c.gm = ANY ? (const unsigned short*)a.global_mask + (size_t)c.b * c.S : nullptr;
   const float c2 = a.scale * kLog2e;
   const bool split = a.G > 0 && c.tile < a.n_split;
   c.sp_lo = split ? c.tile * a.split_len : 0;
@@ -689,7 +738,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   // every load the prologue needs is issued before anything waits: the global-mask
   // values, the first round of the global-row split (split tiles), the first ring
   // entries, Q, the register sets
-  const int gfirst = count_load<T, RAW>(a, c.b);
+  const int gfirst = count_load<T, RAW, ANY>(a, c.b);
   __builtin_amdgcn_sched_barrier(0);
   Stage<T> spl[kSplitEnt];
   v8 qg0[4];
@@ -704,7 +753,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
   Stage<T> pro[kAhead];
 #pragma unroll
-  for (int i = 0; i < kAhead; ++i) load_entry<T>(pro[i], c, i);
+  for (int i = 0; i < kAhead; ++i) load_entry<T, ANY>(pro[i], c, i);
   // Q before the register sets: in the loop its wait count then never holds back
   // the sets in flight
   v8 qf[4];
@@ -715,20 +764,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   Stage<T> st[kDepth];
 #pragma unroll
   for (int u = 0; u < kDepth; ++u) {
-    load_entry<T>(st[(kAhead + u) % kDepth], c, kAhead + u);
+    load_entry<T, ANY>(st[(kAhead + u) % kDepth], c, kAhead + u);
     __builtin_amdgcn_sched_barrier(0);
   }
-  c.nb = count_globals<T, RAW>(a, c.b, gfirst);
+  c.nb = count_globals<T, RAW, ANY>(a, c.b, gfirst);
   // the split of the global rows first (its loads were issued first), then the
   // ticket, whose value is looked at after the band work
   int ticket = 0;
   if (split && c.nb > 0) {
-    global_split_run<T, RAW>(a, c, c.tile, ring, spl, qg0);
+    global_split_run<T, RAW, ANY>(a, c, c.tile, ring, spl, qg0);
     ticket = take_ticket<T>(a, c);
   }
 
 #pragma unroll
-  for (int i = 0; i < kAhead; ++i) store_entry<T, RAW>(ring[i], pro[i], c, i);
+  for (int i = 0; i < kAhead; ++i) store_entry<T, RAW, ANY>(ring[i], pro[i], c, i);
   __syncthreads();
 
   f32x16 o[2] = {f32x16{}, f32x16{}};
@@ -736,16 +785,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   constexpr int s0i = kAhead % kDepth, s1i = (kAhead + 1) % kDepth;
   int t0 = 0;
   for (; t0 + 2 <= n_steps; t0 += 2) {
-    band_step<T, RAW, false>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
-    band_step<T, RAW, true>(c, ring, t0 + 1, rg, sb, c2, st[s1i], qf, o, m_run, l_run);
+    band_step<T, RAW, ANY, false>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
+    band_step<T, RAW, ANY, true>(c, ring, t0 + 1, rg, sb, c2, st[s1i], qf, o, m_run, l_run);
   }
-  if (t0 < n_steps) band_step<T, RAW, false>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
+  if (t0 < n_steps) band_step<T, RAW, ANY, false>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
 
   // epilogue: normalise and store the local rows
   {
     typedef typename Frag<T>::v4 v4;
     const float l_tot = cross_half_sum(l_run);
-    if (srow < c.S && srow >= c.nb) {
+    // global rows are written by the combine
+    const bool local = srow < c.S && (ANY ? (c.gm[srow] & 0x7fff) != 0 : srow >= c.nb);
+    if (local) {
       const bool live = mask_live<RAW>(Elem<T>::to_f(c.mask[srow]));
       const float inv = live ? 1.0f / l_tot : 0.0f;
       T* dst = (T*)a.out + (size_t)c.b * a.out_sb + (size_t)c.h * a.out_sh + (size_t)srow * a.out_ss;
@@ -766,7 +817,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     __shared__ int s_last;
     if (threadIdx.x == 0) s_last = ticket == a.n_split - 1;
     __syncthreads();
-    if (s_last) global_combine<T, RAW>(a, c);
+    if (s_last) global_combine<T, RAW, ANY>(a, c);
   }
 }
 
@@ -782,10 +833,12 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
     hipError_t e0 = hipEventRecord(a.ev_begin, st);
     if (e0 != hipSuccess) return e0;
   }
-  if (a.raw)
-    attn_mfma_kernel<T, true><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles);
+  if (a.raw && a.any_pos)
+    attn_mfma_kernel<T, true, true><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles);
+  else if (a.raw)
+    attn_mfma_kernel<T, true, false><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles);
   else
-    attn_mfma_kernel<T, false><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles);
+    attn_mfma_kernel<T, false, false><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.ev_end) e = hipEventRecord(a.ev_end, st);

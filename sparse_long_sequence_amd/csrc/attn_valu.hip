@@ -11,7 +11,9 @@
 // rows s0..s0+63 or global rows r0..r0+63.  Keys stream through LDS in chunks of
 // 64 rows (K and V in fp32); every lane runs an exact online softmax for its own
 // query.  Global keys (positions global_idx[0..n_b)) come first for local rows;
-// band keys are [max(n_b, s0 - W/2), min(S-1, s0+63+W/2)].
+// band keys are [max(n_b, s0 - W/2), min(S-1, s0+63+W/2)] when the global tokens
+// lead, or [max(0, s0 - W/2), ...] minus the positions whose global-mask value is
+// zero when they may sit anywhere (any_pos).
 #include "lf_device.h"
 #include "lf_internal.h"
 
@@ -27,7 +29,7 @@ template <typename T>
 __device__ inline void stage_rows(const T* __restrict__ src_head, const int32_t* __restrict__ rows,
                                   int first, int count, int S, float* __restrict__ kl,
                                   const T* __restrict__ bias_row, float* __restrict__ bl,
-                                  bool gather) {
+                                  bool gather, const T* __restrict__ excl_row = nullptr) {
   // lane i stages key slot i: row = gather ? rows[first+i] : first+i
   const int i = threadIdx.x;
   int row = -1;
@@ -35,7 +37,9 @@ __device__ inline void stage_rows(const T* __restrict__ src_head, const int32_t*
   if (row >= S) row = -1;
   const T* src = src_head + (size_t)(row < 0 ? 0 : row) * 64;
   for (int d = 0; d < 64; ++d) kl[i * kLd + d] = row >= 0 ? Elem<T>::to_f(src[d]) : 0.0f;
-  if (bl) bl[i] = row >= 0 ? Elem<T>::to_f(bias_row[row]) : -INFINITY;
+  // excl_row: a position whose global-mask value is zero is not a band key
+  const bool excl = row >= 0 && excl_row && Elem<T>::to_f(excl_row[row]) == 0.0f;
+  if (bl) bl[i] = row >= 0 && !excl ? Elem<T>::to_f(bias_row[row]) : -INFINITY;
 }
 
 template <typename T>
@@ -57,6 +61,7 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a, int n_local_t
   const T* bias = (const T*)a.bias + (size_t)b * S;
   const int32_t* gidx = a.gidx + (size_t)b * S;
   const bool is_global_tile = tile >= n_local_tiles;
+  const T* gmask = a.any_pos ? (const T*)a.global_mask + (size_t)b * S : nullptr;
 
   int s;            // output position of this lane's row
   bool active;      // lane owns a row this kernel computes
@@ -64,7 +69,7 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a, int n_local_t
   if (!is_global_tile) {
     const int s0 = tile * kRows;
     s = s0 + lane;
-    active = s < S && s >= nb;
+    active = s < S && (gmask ? Elem<T>::to_f(gmask[s]) != 0.0f : s >= nb);
     qrow = (const T*)a.q + head + (size_t)(active ? s : 0) * 64;
   } else {
     const int r = (tile - n_local_tiles) * kRows + lane;
@@ -114,12 +119,12 @@ __global__ __launch_bounds__(64) void attn_valu_kernel(AttnArgs a, int n_local_t
       consume(cnt, 0, false);
     }
     const int s0 = tile * kRows;
-    const int lo = max(nb, s0 - half);
+    const int lo = max(gmask ? 0 : nb, s0 - half);
     const int hi = min(S - 1, s0 + kRows - 1 + half);
     for (int kb = lo; kb <= hi; kb += kChunk) {
       const int cnt = min(kChunk, hi - kb + 1);
       __syncthreads();
-      stage_rows<T>(kh, nullptr, kb, cnt, S, ks, bias, bs, false);
+      stage_rows<T>(kh, nullptr, kb, cnt, S, ks, bias, bs, false, gmask);
       stage_rows<T>(vh, nullptr, kb, cnt, S, vs, bias, nullptr, false);
       __syncthreads();
       consume(cnt, kb, true);

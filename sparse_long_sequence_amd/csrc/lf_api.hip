@@ -124,6 +124,7 @@ lf::AttnArgs make_args(int dtype, const void* q, const void* k, const void* v, c
   lf::AttnArgs a;
   a.dtype = dtype;
   a.raw = 0;
+  a.any_pos = 0;
   a.q = q; a.k = k; a.v = v; a.qg = qg; a.kg = kg; a.vg = vg;
   a.local_mask = nullptr; a.global_mask = nullptr;
   a.gidx = gidx; a.gcnt = gcnt; a.bias = bias; a.out = out;
@@ -457,8 +458,14 @@ int lf_attn_forward_pre(int dtype, const void* q, const void* k, const void* v, 
   return ok();
 }
 
-int lf_check_masks(int dtype, const void* local_mask, const void* global_mask, int B, int S,
-                   int G, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The mask precondition check; leading: the global tokens must also be contiguous at
+// the head of the sequence (lf_attn_forward), not when they may sit anywhere.
+int check_masks_impl(int dtype, const void* local_mask, const void* global_mask, int B, int S,
+                     int G, void* stream, bool leading) {
   if (!known_dtype(dtype)) return fail(LF_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
   if (B < 1 || S < 1 || G < 0) return fail(LF_ERR_INVALID_ARGUMENT, "bad B, S or G");
   if ((int64_t)B * S >= INT_MAX) return fail(LF_ERR_INVALID_ARGUMENT, "B*S too large");
@@ -482,7 +489,7 @@ int lf_check_masks(int dtype, const void* local_mask, const void* global_mask, i
     return fail(LF_ERR_PRECONDITION, "local_mask[%d] is neither 0 nor 1", flags[0] - 1);
   if (flags[1] != INT_MAX)
     return fail(LF_ERR_PRECONDITION, "global_mask[%d] is neither 0 nor -10000", flags[1] - 1);
-  if (flags[2] != INT_MAX)
+  if (leading && flags[2] != INT_MAX)
     return fail(LF_ERR_PRECONDITION,
                 "global tokens of batch row %d are not contiguous at the sequence head",
                 flags[2] - 1);
@@ -492,10 +499,12 @@ int lf_check_masks(int dtype, const void* local_mask, const void* global_mask, i
   return ok();
 }
 
-int lf_attn_forward(int dtype, const void* q, const void* k, const void* v, const void* qg,
-                    const void* kg, const void* vg, const void* local_mask,
-                    const void* global_mask, int B, int H, int S, int W, int G, void* out,
-                    void* stream) {
+// lf_attn_forward (any_pos = false: the global tokens lead) and
+// lf_attn_forward_any_globals (any_pos = true).
+int attn_forward_impl(int dtype, const void* q, const void* k, const void* v, const void* qg,
+                      const void* kg, const void* vg, const void* local_mask,
+                      const void* global_mask, int B, int H, int S, int W, int G, void* out,
+                      void* stream, bool any_pos) {
   if (int e = validate_attn(dtype, B, H, S, W, G)) return e;
   if (int e = null_check("q,k,v,kg,vg,local_mask,global_mask,out",
                          {q, k, v, kg, vg, local_mask, global_mask, out}))
@@ -503,19 +512,36 @@ int lf_attn_forward(int dtype, const void* q, const void* k, const void* v, cons
   if (G > 0 && !qg) return fail(LF_ERR_INVALID_ARGUMENT, "null pointer: qg (G > 0)");
   hipStream_t st = (hipStream_t)stream;
   if (debug_check_enabled()) {
-    if (int e = lf_check_masks(dtype, local_mask, global_mask, B, S, G, stream)) return e;
+    if (int e = check_masks_impl(dtype, local_mask, global_mask, B, S, G, stream, !any_pos))
+      return e;
   }
   const AttnWs ws = attn_ws(B, H, S, G);
   if (dtype != LF_F32) {
-    // one launch: the kernel reads both masks itself (count of the leading global
-    // tokens, live-key test of the shifted mask)
+    // leading globals: one launch, the kernel reads both masks itself (count of the
+    // leading global tokens, live-key test of the local mask).  Globals anywhere: the
+    // index partition first (into the cached workspace, after the partials), then
+    // the kernel, which gathers the global keys through it.
     char* base = nullptr;
     size_t part_off = 0;
-    if (int e = cached_workspace(st, (size_t)B * H, ws.total - ws.partials_off, &base, &part_off))
+    const size_t part_bytes = ws.total - ws.partials_off;
+    const size_t idx_bytes = any_pos ? align256((size_t)B * S * sizeof(int32_t)) +
+                                           align256((size_t)B * sizeof(int32_t))
+                                     : 0;
+    if (int e = cached_workspace(st, (size_t)B * H, part_bytes + idx_bytes, &base, &part_off))
       return e;
-    lf::AttnArgs a = make_args(dtype, q, k, v, qg, kg, vg, nullptr, nullptr, nullptr, B, H, S, W,
-                               G, out, base, ws, part_off);
+    int32_t* gidx = nullptr;
+    int32_t* gcnt = nullptr;
+    if (any_pos) {
+      gidx = (int32_t*)(base + part_off + part_bytes);
+      gcnt = (int32_t*)(base + part_off + part_bytes + align256((size_t)B * S * sizeof(int32_t)));
+      hipError_t he = lf::launch_prep(dtype, global_mask, nullptr, B, S, gidx, gcnt, nullptr,
+                                      nullptr, 0, st);
+      if (he != hipSuccess) return hip_fail(he, "lf_attn_forward_any_globals index");
+    }
+    lf::AttnArgs a = make_args(dtype, q, k, v, qg, kg, vg, gidx, gcnt, nullptr, B, H, S, W, G, out,
+                               base, ws, part_off);
     a.raw = 1;
+    a.any_pos = any_pos ? 1 : 0;
     a.local_mask = local_mask;
     a.global_mask = global_mask;
     hipError_t he = run_attention(a, st);
@@ -538,12 +564,39 @@ int lf_attn_forward(int dtype, const void* q, const void* k, const void* v, cons
   if (he == hipSuccess) {
     lf::AttnArgs a = make_args(dtype, q, k, v, qg, kg, vg, gidx, gcnt, bias, B, H, S, W, G, out,
                                nullptr, ws, 0);
+    a.any_pos = any_pos ? 1 : 0;
+    a.global_mask = global_mask;
     he = run_attention(a, st);
   }
   hipError_t he2 = hipFreeAsync(scratch, st);
   if (he != hipSuccess) return hip_fail(he, "lf_attn_forward");
   if (he2 != hipSuccess) return hip_fail(he2, "lf_attn_forward free");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int lf_check_masks(int dtype, const void* local_mask, const void* global_mask, int B, int S,
+                   int G, void* stream) {
+  return check_masks_impl(dtype, local_mask, global_mask, B, S, G, stream, true);
+}
+
+int lf_attn_forward(int dtype, const void* q, const void* k, const void* v, const void* qg,
+                    const void* kg, const void* vg, const void* local_mask,
+                    const void* global_mask, int B, int H, int S, int W, int G, void* out,
+                    void* stream) {
+  return attn_forward_impl(dtype, q, k, v, qg, kg, vg, local_mask, global_mask, B, H, S, W, G,
+                           out, stream, false);
+}
+
+int lf_attn_forward_any_globals(int dtype, const void* q, const void* k, const void* v,
+                                const void* qg, const void* kg, const void* vg,
+                                const void* local_mask, const void* global_mask, int B, int H,
+                                int S, int W, int G, void* out, void* stream) {
+  return attn_forward_impl(dtype, q, k, v, qg, kg, vg, local_mask, global_mask, B, H, S, W, G,
+                           out, stream, true);
 }
 
 int lf_kernel_timing_start(int capacity) {

@@ -13,6 +13,9 @@ namespace lf {
 struct AttnArgs {
   int dtype;
   int raw;                // 1: read local_mask / global_mask; 0: read gidx / gcnt / bias
+  int any_pos;            // 1: global tokens at any positions (raw mode on fp16 / bf16, pre
+                          // mode on fp32): band keys and output rows test global_mask, global
+                          // keys and rows go through gidx / gcnt
   const void *q, *k, *v, *qg, *kg, *vg;
   const void* local_mask;   // [B, S] dtype (raw mode)
   const void* global_mask;  // [B, S] dtype (raw mode)

@@ -47,11 +47,14 @@ def _fake(n=1):
     return ctypes.c_void_p(0x1000)
 
 
-def _attn(lib, dtype=1, B=1, H=2, S=64, W=16, G=2, null=None):
+ATTN_ENTRIES = ["lf_attn_forward", "lf_attn_forward_any_globals"]
+
+
+def _attn(lib, dtype=1, B=1, H=2, S=64, W=16, G=2, null=None, entry="lf_attn_forward"):
     p = {n: _fake() for n in ("q", "k", "v", "qg", "kg", "vg", "lm", "gm", "out")}
     if null:
         p[null] = None
-    return lib.lf_attn_forward(dtype, p["q"], p["k"], p["v"], p["qg"], p["kg"], p["vg"], p["lm"],
+    return getattr(lib, entry)(dtype, p["q"], p["k"], p["v"], p["qg"], p["kg"], p["vg"], p["lm"],
                                p["gm"], B, H, S, W, G, p["out"], None)
 
 
@@ -66,14 +69,16 @@ def _attn(lib, dtype=1, B=1, H=2, S=64, W=16, G=2, null=None):
     (dict(H=0), ">= 1"),
     (dict(dtype=7), "dtype"),
 ])
-def test_attn_shape_rules_rejected_on_host(lib, kw, msg):
-    assert _attn(lib, **kw) == INVALID
+@pytest.mark.parametrize("entry", ATTN_ENTRIES)
+def test_attn_shape_rules_rejected_on_host(lib, kw, msg, entry):
+    assert _attn(lib, entry=entry, **kw) == INVALID
     assert msg in lib.lf_last_error().decode()
 
 
 @pytest.mark.parametrize("name", ["q", "k", "v", "kg", "vg", "lm", "gm", "out", "qg"])
-def test_attn_null_pointers_rejected(lib, name):
-    assert _attn(lib, null=name) == INVALID
+@pytest.mark.parametrize("entry", ATTN_ENTRIES)
+def test_attn_null_pointers_rejected(lib, name, entry):
+    assert _attn(lib, null=name, entry=entry) == INVALID
     assert "null pointer" in lib.lf_last_error().decode()
 
 

@@ -1,0 +1,160 @@
+"""GPU parity of the globals-anywhere attention entry point against the float64 oracle.
+
+The oracle is the plain definition with the global positions taken from the global
+mask wherever they are (pinned against a dense brute force with scattered globals in
+the oracle tests).  [FT-LF] computation flow, per-layer steps 3-4, without the
+head-of-sequence constraint of section "使用前提：四条硬性约束".  Tolerances as for
+the leading-globals entry point: fp32 1e-5, fp16 3e-3, bf16 1e-2 max abs error.
+With leading global tokens the two entry points must agree bit for bit (same
+arithmetic, the index only reorders nothing)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"fp32": 1e-5, "fp16": 3e-3, "bf16": 1e-2}
+
+
+@pytest.fixture(scope="module")
+def lf():
+    import sparse_long_sequence_amd as m
+    m.load_library()
+    return m
+
+
+def _gpu(inp):
+    return {n: t.cuda() for n, t in inp.items()}
+
+
+def _run_any(lf, g, W, G):
+    return lf.attn_forward_any_globals(g["q"], g["k"], g["v"], g["qg"], g["kg"], g["vg"],
+                                       g["local_mask"], g["global_mask"], W, G)
+
+
+def _run_lead(lf, g, W, G):
+    return lf.attn_forward(g["q"], g["k"], g["v"], g["qg"], g["kg"], g["vg"], g["local_mask"],
+                           g["global_mask"], W, G)
+
+
+def _oracle(inp, W, G, rows=None):
+    return oracle.attention(inp["q"], inp["k"], inp["v"], inp["qg"], inp["kg"], inp["vg"],
+                            inp["local_mask"], inp["global_mask"], W, G, rows=rows)
+
+
+def _positions(seed, B, S, n, live_len=None):
+    """n distinct sorted positions per batch row, drawn below live_len[b] (default S)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for b in range(B):
+        hi = S if live_len is None else live_len[b]
+        out.append(sorted(int(x) for x in rng.choice(hi, n[b] if isinstance(n, list) else n,
+                                                     replace=False)))
+    return out
+
+
+def _compare_full(lf, inp, W, G, dtype):
+    g = _gpu(inp)
+    out = _run_any(lf, g, W, G)
+    torch.cuda.synchronize()
+    got = out.cpu()
+    assert torch.isfinite(got.float()).all()
+    ref = _oracle(inp, W, G)
+    err = np.abs(got.double().numpy() - ref)
+    assert err.max() <= TOL[dtype], f"max abs err {err.max():.3e} (tol {TOL[dtype]})"
+    live = (inp["local_mask"] == 1).numpy()
+    o = got.float().numpy()
+    for b in range(o.shape[0]):
+        pad = o[b][:, ~live[b]]
+        assert np.all(pad == 0.0) and not np.any(np.signbit(pad)), "padded rows must be +0.0"
+    return got
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16", "fp32"])
+@pytest.mark.parametrize("case", [
+    # B, H, S, W, G, pad
+    (1, 4, 1024, 256, 8, None),
+    (2, 2, 1024, 128, 33, (0.1, 0.25)),
+])
+def test_leading_globals_match_the_leading_entry_point_bitwise(lf, dtype, case):
+    B, H, S, W, G, pad = case
+    inp = workloads.random_attention_inputs(40 + G, B, H, S, W, G, dtype, pad_frac=pad)
+    g = _gpu(inp)
+    a = _run_any(lf, g, W, G)
+    b = _run_lead(lf, g, W, G)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16) if dtype != "fp32" else a.view(torch.int32),
+                       b.view(torch.int16) if dtype != "fp32" else b.view(torch.int32))
+
+
+# B, H, S, W, G, positions (per batch row, or ("rand", n) drawn with the case seed), pad
+SCATTER_CASES = [
+    # tile edges (128 / 256 rows), both sequence ends, adjacent runs, fewer than G
+    (2, 2, 1024, 128, 8, [[0, 127, 128, 500, 511, 512, 1000, 1023], [17, 300, 301, 302]], None),
+    # more than one 32-row split block and a nearly full 64-key global entry
+    (1, 2, 768, 256, 40, ("rand", 40), None),
+    # two global-key entries (G > 64)
+    (1, 2, 1024, 256, 70, ("rand", 70), None),
+    # padding (globals inside the live part), rows beyond the last full tile
+    (2, 2, 384, 96, 5, ("live", 5), (0.1, 0.3)),
+    # globals only at the end of the sequence
+    (1, 2, 512, 64, 4, [[508, 509, 510, 511]], None),
+    # capacity but no global token at all
+    (1, 2, 512, 64, 6, [[]], None),
+]
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16", "fp32"])
+@pytest.mark.parametrize("ci", range(len(SCATTER_CASES)))
+def test_scattered_globals_full_output(lf, dtype, ci):
+    B, H, S, W, G, pos, pad = SCATTER_CASES[ci]
+    seed = 900 + ci
+    if isinstance(pos, tuple):
+        if pos[0] == "live":
+            # draw the padding first (same draw as the generator), keep globals live
+            probe = workloads.random_attention_inputs(seed, B, H, S, W, G, dtype, pad_frac=pad)
+            live_len = [int((probe["local_mask"][b] == 1).sum()) for b in range(B)]
+            pos = _positions(seed, B, S, pos[1], live_len)
+        else:
+            pos = _positions(seed, B, S, pos[1])
+    inp = workloads.random_attention_inputs(seed, B, H, S, W, G, dtype, pad_frac=pad,
+                                            global_positions=pos)
+    _compare_full(lf, inp, W, G, dtype)
+
+
+def test_scattered_globals_stress_scale_fp16(lf):
+    # N(0,1) inputs: large scores exercise the running max and its rescaling
+    B, H, S, W, G = 1, 2, 1024, 256, 16
+    pos = _positions(77, B, S, G)
+    inp = workloads.random_attention_inputs(77, B, H, S, W, G, "fp16", std=1.0,
+                                            global_positions=pos)
+    _compare_full(lf, inp, W, G, "fp16")
+
+
+def test_scattered_globals_longformer_large_shape_sampled_rows(lf):
+    # the benchmark shape (B=1 H=16 S=4096 W=512 G=8 fp16) with the 8 global tokens
+    # spread over the sequence; every global row, the rows around each global token
+    # and the band edges are checked, plus random rows
+    B, H, S, W, G = 1, 16, 4096, 512, 8
+    pos = [[0, 255, 256, 1000, 2047, 2048, 3500, 4095]]
+    inp = workloads.random_attention_inputs(20260102, B, H, S, W, G, "fp16", global_positions=pos)
+    g = _gpu(inp)
+    out = _run_any(lf, g, W, G)
+    out2 = _run_any(lf, g, W, G)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16)), "not deterministic"
+    got = out.cpu()
+    assert torch.isfinite(got.float()).all()
+    rng = np.random.default_rng(5)
+    srows = set()
+    for p in pos[0]:
+        srows.update(x for x in (p - 257, p - 256, p - 1, p, p + 1, p + 256, p + 257) if 0 <= x < S)
+    srows.update(int(x) for x in rng.integers(0, S, 16))
+    rows = [(0, h, s) for h in (0, 7, 15) for s in sorted(srows)]
+    ref = _oracle(inp, W, G, rows=rows)
+    g_rows = np.stack([got[b, h, s].double().numpy() for (b, h, s) in rows])
+    err = np.abs(g_rows - ref).max()
+    assert err <= TOL["fp16"], f"max abs err {err:.3e} over {len(rows)} rows"

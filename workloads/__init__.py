@@ -13,7 +13,8 @@ round-to-nearest-even; the rounded tensor is the canonical input for both sides.
 Mask encodings follow the page's input list in section "Longformer Encoder
 计算流程": local mask 1.0 = attends, 0.0 = padding; global mask 0.0 = global
 token, -10000.0 = ordinary token.  Global tokens sit contiguously at the head of
-each sequence (the page's fourth hard constraint).
+each sequence (the page's fourth hard constraint), unless explicit per-sequence
+positions are given (the globals-anywhere entry point).
 """
 from __future__ import annotations
 
@@ -42,6 +43,7 @@ class AttnWorkload:
     std: float = 0.125
     pad_frac: tuple | None = None   # (lo, hi): per sequence a trailing U[lo,hi] share is padding
     n_global: tuple | None = None   # per-batch global count; default G for every sequence
+    global_positions: tuple | None = None   # per-batch position tuples (overrides n_global)
 
 
 @dataclass(frozen=True)
@@ -80,13 +82,20 @@ def _cast(x: np.ndarray, dtype: str) -> torch.Tensor:
 
 
 def make_masks(rng: np.random.Generator, B: int, S: int, G: int, dtype: str,
-               pad_frac=None, n_global=None):
-    """Local mask (1 = token, 0 = padding) and global mask (0 = global, -10000 = not)."""
+               pad_frac=None, n_global=None, global_positions=None):
+    """Local mask (1 = token, 0 = padding) and global mask (0 = global, -10000 = not).
+
+    Global tokens: positions 0 .. n-1 of each sequence (n = n_global[b], default G),
+    or, when ``global_positions`` is given, exactly ``global_positions[b]``.
+    """
     local = np.ones((B, S), np.float64)
     glob = np.full((B, S), NOT_GLOBAL, np.float64)
     counts = list(n_global) if n_global is not None else [G] * B
     for b in range(B):
-        glob[b, : counts[b]] = 0.0
+        if global_positions is not None:
+            glob[b, list(global_positions[b])] = 0.0
+        else:
+            glob[b, : counts[b]] = 0.0
     if pad_frac is not None:
         lo, hi = pad_frac
         for b in range(B):
@@ -109,7 +118,7 @@ def make_attention_inputs(wl: AttnWorkload, std: float | None = None) -> dict:
     for name, rows in (("q", S), ("k", S), ("v", S), ("qg", G), ("kg", S), ("vg", S)):
         out[name] = _cast(rng.standard_normal((B, H, rows, D)) * s, wl.dtype)
     out["local_mask"], out["global_mask"] = make_masks(
-        rng, B, S, G, wl.dtype, wl.pad_frac, wl.n_global)
+        rng, B, S, G, wl.dtype, wl.pad_frac, wl.n_global, wl.global_positions)
     return out
 
 
@@ -159,8 +168,11 @@ def random_layer_params(rng: np.random.Generator, D: int, F: int, dtype: str,
 
 
 def random_attention_inputs(seed: int, B: int, H: int, S: int, W: int, G: int, dtype: str,
-                            std: float = 0.125, pad_frac=None, n_global=None) -> dict:
+                            std: float = 0.125, pad_frac=None, n_global=None,
+                            global_positions=None) -> dict:
     """Same recipe as ``make_attention_inputs`` for an ad-hoc shape."""
+    gp = tuple(tuple(int(x) for x in p) for p in global_positions) if global_positions is not None \
+        else None
     wl = AttnWorkload("adhoc", B, H, S, W, G, dtype, seed, std, pad_frac,
-                      tuple(n_global) if n_global is not None else None)
+                      tuple(n_global) if n_global is not None else None, gp)
     return make_attention_inputs(wl)
