@@ -1,6 +1,7 @@
 """Timing driver for the library's entry points on seeded synthetic inputs.
 
     python sparse_long_sequence_amd/perf.py attn  [--iters N]   # longformer-large attention
+    python sparse_long_sequence_amd/perf.py attn_any [--iters N]  # same, 8 globals spread out
     python sparse_long_sequence_amd/perf.py prep  [--iters N]   # index compaction + mask shift
     python sparse_long_sequence_amd/perf.py layer [--iters N]   # one fp16 encoder layer
     python sparse_long_sequence_amd/perf.py stack [--iters N]   # 24-layer fp16 encoder, B1 S1024
@@ -16,7 +17,9 @@ import argparse
 import json
 import os
 import sys
+import time
 
+import numpy as np
 import torch
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -31,6 +34,12 @@ def _time(fn, iters: int, warmup: int) -> float:
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    # one second of untimed calls: the clocks ramp up over the first second of work
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 1.0:
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -53,6 +62,46 @@ def run_attn(iters: int, warmup: int) -> dict:
     flops = 256.0 * pairs * wl.B * wl.H
     return {"op": "attn_forward", "workload": wl.name, "ms": ms,
             "tflops": flops / (ms * 1e-3) / 1e12}
+
+
+def run_attn_any(iters: int, warmup: int) -> dict:
+    # the longformer-large shape with its 8 global tokens spread over the sequence
+    # (tile edges, the middle, both ends) through lf_attn_forward_any_globals
+    wl = workloads.LARGE_FP16
+    pos = [[0, 255, 256, 1000, 2047, 2048, 3500, 4095]]
+    inp = workloads.random_attention_inputs(wl.seed, wl.B, wl.H, wl.S, wl.W, wl.G, wl.dtype,
+                                            global_positions=pos)
+    g = {n: t.cuda() for n, t in inp.items()}
+    out = torch.empty_like(g["q"])
+    ms = _time(lambda: lf.attn_forward_any_globals(g["q"], g["k"], g["v"], g["qg"], g["kg"],
+                                                   g["vg"], g["local_mask"], g["global_mask"],
+                                                   wl.W, wl.G, out=out), iters, warmup)
+    pairs = oracle_free_pairs(inp["local_mask"], inp["global_mask"], wl.W)
+    flops = 256.0 * pairs * wl.H
+    return {"op": "attn_forward_any_globals", "workload": wl.name + "_globals_spread",
+            "ms": ms, "tflops": flops / (ms * 1e-3) / 1e12}
+
+
+def oracle_free_pairs(local_mask, global_mask, W: int) -> int:
+    """Allowed (query, key) pairs of one head, counted directly from the masks."""
+    lm = (local_mask == 1).cpu().numpy()
+    gl = (global_mask == 0).cpu().numpy()
+    total = 0
+    for b in range(lm.shape[0]):
+        live, glob = lm[b], gl[b]
+        S = live.shape[0]
+        n_live, n_glob_live = int(live.sum()), int((live & glob).sum())
+        band_ok = (live & ~glob).astype(np.int64)
+        csum = np.concatenate([[0], np.cumsum(band_ok)])
+        for s in range(S):
+            if not live[s]:
+                continue
+            if glob[s]:
+                total += n_live
+            else:
+                lo, hi = max(0, s - W // 2), min(S - 1, s + W // 2)
+                total += n_glob_live + int(csum[hi + 1] - csum[lo])
+    return total
 
 
 def run_prep(iters: int, warmup: int) -> dict:
@@ -136,11 +185,12 @@ def run_stack(iters: int, warmup: int, n_layers: int = 24) -> dict:
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("op", choices=["attn", "prep", "layer", "stack"])
+    ap.add_argument("op", choices=["attn", "attn_any", "prep", "layer", "stack"])
     ap.add_argument("--iters", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     a = ap.parse_args()
-    fn = {"attn": run_attn, "prep": run_prep, "layer": run_layer, "stack": run_stack}[a.op]
+    fn = {"attn": run_attn, "attn_any": run_attn_any, "prep": run_prep, "layer": run_layer,
+          "stack": run_stack}[a.op]
     print(json.dumps(fn(a.iters, a.warmup)), flush=True)
 
 
