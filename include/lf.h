@@ -188,11 +188,14 @@ size_t lf_encoder_layer_workspace_bytes(int dtype, int B, int S, int hidden, int
  * NULL when G == 0.  `workspace` (device, 256-byte aligned, ws_bytes >=
  * lf_encoder_layer_workspace_bytes) holds every intermediate: attention tickets
  * first, then q, k, v, kg, vg, qg, the attention output, the fp32 pre-LayerNorm
- * rows, h1 in fp32 and in `dtype`, the FFN intermediate.  Its first bytes (the
+ * rows, h1 in fp32 and in `dtype`, the FFN intermediate, and the fp32 partial sums of
+ * the GEMMs whose grids are split over K (those with few output tiles).  Its first bytes (the
  * tickets) must be zero before the first call that uses it (zero-fill it once after
  * allocating); every call leaves them zero.  The residual stream (x + projection,
  * h1) is kept in fp32; GEMM inputs are rounded to `dtype`.  Calls sharing a
- * workspace must not overlap in time.  Enqueues 8 launches on `stream`, no sync.
+ * workspace must not overlap in time.  Enqueues 8 to 9 launches on `stream` (the
+ * global-query projection adds a reduction when it is split over K), no sync.  The
+ * result does not depend on the split: partial sums are added in a fixed order.
  */
 int lf_encoder_layer(int dtype, const lf_layer_weights* w, const void* x,
                      const void* local_mask, const void* global_mask, int B, int S,
@@ -212,7 +215,7 @@ size_t lf_encoder_forward_workspace_bytes(int dtype, int B, int S, int hidden, i
  * between y and an activation buffer in the workspace so that the last layer writes
  * y.  Same shape rules, dtype, precision and workspace convention as
  * lf_encoder_layer (ws_bytes >= lf_encoder_forward_workspace_bytes; its first bytes
- * zero before the first use, left zero).  Enqueues 1 + 8 * n_layers launches.
+ * zero before the first use, left zero).  Enqueues 1 + (8 to 9) * n_layers launches.
  */
 int lf_encoder_forward(int dtype, const lf_layer_weights* w, int n_layers, const void* x,
                        const void* local_mask, const void* global_mask, int B, int S,

@@ -17,11 +17,17 @@
 // holds 8 consecutive k of one row).  The weight rows are the MFMA's first operand
 // and the activation rows its second, so each lane's 16 accumulators are 4 groups
 // of 4 consecutive output columns of ONE output row: the epilogue stores 8-byte
-// runs.  Workgroup tile 128 x 128, K step 64, 4 waves each owning 64 x 64 (2 x 2
-// MFMA tiles); operands staged through double-buffered LDS (pitch 144 B: the
-// 16-byte fragment reads are conflict-free); the next K step's global loads are in
-// flight while the current one is multiplied.  Rows of A past M read out of range
-// (zeros) and are not stored.
+// runs.  Two tile shapes of one kernel: 256 x 256 with 8 waves of 128 x 64 (4 x 2
+// MFMA tiles, 6 fragment reads per 8 MFMAs) for GEMMs whose grid still covers every
+// CU, else 128 x 128 with 4 waves of 64 x 64 (two workgroups per CU).  K step 64;
+// the operand tiles go from global memory straight into LDS (buffer_load_dwordx4 ...
+// lds: lane L of a wave's load lands at LDS base + 16 L, every lane's global address
+// is free), double-buffered, so there is no register staging and no LDS store
+// phase: each K step issues the next step's loads into the other buffer, multiplies
+// the current one, waits for this wave's loads and meets the others at a barrier.
+// Rows of A past M read out of range (zeros) and are not stored.
+#include <type_traits>
+
 #include "lf_device.h"
 #include "lf_internal.h"
 
@@ -29,10 +35,8 @@ namespace lf {
 
 namespace {
 
-constexpr int kGT = 128;      // tile rows and columns
+constexpr int kGT = 128;      // smallest tile: N must be a multiple of it
 constexpr int kGK = 64;       // K step
-constexpr int kGld = 72;      // LDS row pitch (elements)
-constexpr int kGThreads = 256;
 constexpr int kGroupM = 8;    // m-tiles per group of the tile order (L2 reuse of W tiles)
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -41,25 +45,192 @@ __device__ inline rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-// The erf form of GELU ([FT-LF] step 6 names GELU; the exact form is the reading).
-__device__ inline float gelu(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+// The erf form of GELU ([FT-LF] step 6 names GELU; the exact form is the reading),
+// x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2)), with erf from Abramowitz & Stegun,
+// Handbook of Mathematical Functions, formula 7.1.26: for z >= 0,
+// erf z = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2), t = 1 / (1 + p z),
+// absolute error at most 1.5e-7; erf is odd.  About a dozen vector instructions,
+// against several dozen for the library erff, which dominated the FFN1 epilogue.
+__device__ inline float gelu(float x) {
+  const float z = fabsf(x) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+  float poly = fmaf(1.061405429f, t, -1.453152027f);
+  poly = fmaf(poly, t, 1.421413741f);
+  poly = fmaf(poly, t, -0.284496736f);
+  poly = fmaf(poly, t, 0.254829592f);
+  poly *= t;
+  const float e = __builtin_amdgcn_exp2f(-z * z * 1.4426950408889634f);
+  const float erf_abs = fmaf(-poly, e, 1.0f);
+  const float erf_x = __builtin_copysignf(erf_abs, x);
+  return 0.5f * x * (1.0f + erf_x);
+}
 
+// Epilogue of 4 consecutive output columns nb .. nb + 3 of row m (acc = the raw sums).
 template <typename T, int EPI>
-__global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs g) {
-  typedef typename Elem<T>::vec8 v8;
+__device__ __forceinline__ void epilogue4(const GemmArgs& g, int m, int nb, const float acc[4]) {
   typedef typename Elem<T>::vec4 v4;
-  __shared__ __attribute__((aligned(16))) T sa[2][kGT * kGld];
-  __shared__ __attribute__((aligned(16))) T sw[2][kGT * kGld];
+  const v4 bv = *(const v4*)((const T*)g.bias + nb);
+  float r[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = acc[e] + Elem<T>::to_f(bv[e]);
+  if (EPI == kEpiHeads) {
+    // n -> tensor n / D, head (n % D) / 64, dim n % 64; m -> (batch, row)
+    const int ti = nb / g.D, nn = nb - ti * g.D;
+    const int h = nn >> 6, d = nn & 63;
+    const int bb = m / g.rows, rr = m - bb * g.rows;
+    T* dst = (T*)g.heads[ti] + (((size_t)bb * g.H + h) * g.rows + rr) * 64 + d;
+    v4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = Elem<T>::from_f(r[e]);
+    *(v4*)dst = w;
+  } else if (EPI == kEpiGelu) {
+    v4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = Elem<T>::from_f(gelu(r[e]));
+    *(v4*)((T*)g.out + (size_t)m * g.ldo + nb) = w;
+  } else {
+    f32x4 z;
+    if (EPI == kEpiResidF32) {
+      const f32x4 rv = *(const f32x4*)((const float*)g.resid + (size_t)m * g.ldr + nb);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) z[e] = r[e] + rv[e];
+    } else {
+      const v4 rv = *(const v4*)((const T*)g.resid + (size_t)m * g.ldr + nb);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) z[e] = r[e] + Elem<T>::to_f(rv[e]);
+    }
+    *(f32x4*)((float*)g.out + (size_t)m * g.ldo + nb) = z;
+  }
+}
+
+// Epilogue of one 32 x 32 MFMA tile: the lane's 16 sums are columns cbase + 8 jj +
+// 4 gq .. + 3 (jj = 0..3) of output row m; cbase (a multiple of 32) is the same for
+// the whole wave, and D is a multiple of 64, so for the head split the tensor and
+// head come from cbase alone (one scalar division per tile, none per element).
+template <typename T, int EPI>
+__device__ __forceinline__ void epilogue_tile(const GemmArgs& g, int m, int cbase, int gq,
+                                              const f32x16& acc, int split) {
+  typedef typename Elem<T>::vec4 v4;
+  if (EPI == kEpiPartial) {
+    float* dst = g.part + ((size_t)split * g.M + m) * g.N + cbase + 4 * gq;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+      *(f32x4*)(dst + 8 * jj) = f32x4{acc[4 * jj], acc[4 * jj + 1], acc[4 * jj + 2], acc[4 * jj + 3]};
+    return;
+  }
+  if (EPI == kEpiHeads) {
+    const int ti = cbase / g.D, nn = cbase - ti * g.D;
+    const int h = nn >> 6, d0 = nn & 63;
+    const int bb = m / g.rows, rr = m - bb * g.rows;
+    T* dst = (T*)g.heads[ti] + (((size_t)bb * g.H + h) * g.rows + rr) * 64 + d0 + 4 * gq;
+    const T* bias = (const T*)g.bias + cbase + 4 * gq;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const v4 bv = *(const v4*)(bias + 8 * jj);
+      v4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = Elem<T>::from_f(acc[4 * jj + e] + Elem<T>::to_f(bv[e]));
+      *(v4*)(dst + 8 * jj) = w;
+    }
+    return;
+  }
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const float r[4] = {acc[4 * jj], acc[4 * jj + 1], acc[4 * jj + 2], acc[4 * jj + 3]};
+    epilogue4<T, EPI>(g, m, cbase + 8 * jj + 4 * gq, r);
+  }
+}
+
+__device__ inline int xcd_chunk(int i, int n) {
+  // consecutive workgroup ids go round-robin over the 8 XCDs: give each XCD a
+  // contiguous run of tile indices, so its workgroups share W tiles in its L2
+  const int per = n / 8;
+  const int full = per * 8;
+  if (i >= full) return i;
+  return (i % 8) * per + i / 8;
+}
+
+// Tile layout in LDS: rows of CH chunks of 16 B (8 k values each; CH = KS / 8), no
+// padding; slot s of row r holds chunk s ^ swz(r), swz(r) = r & 7 for 8-chunk rows,
+// (r >> 1) & 3 for 4-chunk rows, so the fragment reads of 8 consecutive rows (same
+// chunk) fall in 8 different 16-byte bank groups.  Load i of wave w fills chunks
+// (NL w + i) 64 + lane, i.e. row (64 / CH) (NL w + i) + lane / CH, slot lane % CH.
+template <int CH>
+__device__ inline int swz(int r) {
+  return CH == 8 ? (r & 7) : ((r >> 1) & 3);
+}
+
+template <typename T, int NL>
+__device__ inline void dma_tile(rsrc_t r, const int off[NL], int kb, T* lds_tile, int wave) {
+#pragma unroll
+  for (int i = 0; i < NL; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (__attribute__((address_space(3))) void*)(lds_tile + (wave * NL + i) * 64 * 8), 16,
+        off[i] < 0 ? -1 : off[i] + kb, 0, 0, 0);
+}
+
+// Workgroup barrier without __syncthreads' release fence: that fence would wait for
+// every load in flight (the direct-to-LDS loads count as pending LDS writes), which
+// would drain the prefetch pipeline at every step.  Each step has already consumed
+// all of its LDS reads (the MFMAs wait for them) and waited for the loads the next
+// step reads; the empty asm keeps the compiler from moving memory accesses across.
+__device__ inline void step_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// s_waitcnt with only the vector-memory count set (expcnt and lgkmcnt left free).
+template <int VM>
+__device__ inline void wait_vm() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup tile TM x TN (rows of A x rows of W), WAVES waves of WM x WN each, K step
+// KS, ST LDS stages: the loads of step ks + ST - 1 are issued at step ks.  The stages
+// are separate LDS objects and the K loop is unrolled by ST steps, so every access
+// names its stage statically: the compiler then knows that the loads in flight write
+// other stages and does not make the current step's LDS reads wait for them.
+template <typename T, int EPI, int TM, int TN, int WAVES, int WM, int WN, int KS, int ST>
+__global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs g) {
+  typedef typename Elem<T>::vec8 v8;
+  constexpr int MI = WM / 32, NI = WN / 32;    // MFMA tiles per wave
+  constexpr int WAVES_M = TM / WM;
+  constexpr int CH = KS / 8;                   // 16-byte chunks per tile row
+  constexpr int RPL = 64 / CH;                 // tile rows per wave-wide load
+  constexpr int NLA = TM / (RPL * WAVES), NLW = TN / (RPL * WAVES);   // loads per step
+  constexpr int NL = NLA + NLW;
+  constexpr int D = ST - 1;                    // prefetch distance in steps
+  static_assert(WAVES_M * (TN / WN) == WAVES, "waves tile the workgroup tile");
+  static_assert(NLA * RPL * WAVES == TM && NLW * RPL * WAVES == TN, "whole loads per wave");
+  static_assert(CH == 4 || CH == 8, "K step 32 or 64");
+  static_assert(ST >= 2 && ST <= 4 && (D - 1) * NL < 64, "stages");
+  // one LDS object per stage (A tile, then W tile): the compiler tells in-flight
+  // direct-to-LDS loads apart from later LDS reads by the object they write, and
+  // only for a few objects, so the two tiles of a stage share one
+  __shared__ __attribute__((aligned(16))) T st0[(TM + TN) * KS], st1[(TM + TN) * KS];
+  __shared__ __attribute__((aligned(16))) T st2[ST > 2 ? (TM + TN) * KS : 8];
+  __shared__ __attribute__((aligned(16))) T st3[ST > 3 ? (TM + TN) * KS : 8];
+  auto abuf = [&](auto J) -> T* {
+    constexpr int j = decltype(J)::value % ST;
+    if constexpr (j == 0) return st0;
+    else if constexpr (j == 1) return st1;
+    else if constexpr (j == 2) return st2;
+    else return st3;
+  };
+  auto wbuf = [&](auto J) -> T* { return abuf(J) + TM * KS; };
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int n = lane & 31, gq = lane >> 5;
 
-  // tile order: groups of kGroupM m-tiles sweep all n-tiles, so a W tile is reused
-  // by neighbouring workgroups while it is in L2
-  const int tiles_n = g.N / kGT;
-  const int tiles_m = (g.M + kGT - 1) / kGT;
-  const int bid = blockIdx.x;
+  // tile order: per XCD a contiguous run of tile indices; within it, groups of
+  // kGroupM m-tiles sweep all n-tiles, so a W tile is reused while it is in L2; with
+  // split-K the grid holds every tile once per split
+  const int tiles_n = g.N / TN;
+  const int tiles_m = (g.M + TM - 1) / TM;
+  const int flat = xcd_chunk(blockIdx.x, tiles_m * tiles_n * g.splits);
+  const int split = __builtin_amdgcn_readfirstlane(flat / (tiles_m * tiles_n));
+  const int bid = flat - split * (tiles_m * tiles_n);
   const int per_group = kGroupM * tiles_n;
   const int grp = bid / per_group;
   const int first_m = grp * kGroupM;
@@ -67,115 +238,90 @@ __global__ __launch_bounds__(kGThreads) void gemm_kernel(GemmArgs g) {
   const int in_grp = bid - grp * per_group;
   const int tm = __builtin_amdgcn_readfirstlane(first_m + in_grp % gsize);
   const int tn = __builtin_amdgcn_readfirstlane(in_grp / gsize);
-  const int m0 = tm * kGT, n0 = tn * kGT;
+  const int m0 = tm * TM, n0 = tn * TN;
 
-  // global -> register mapping: thread t loads 16 B at column 8 (t % 8) of rows
-  // t / 8 + 32 i (i = 0..3) of both tiles
-  const int lr = t >> 3, lc = 8 * (t & 7);
   const rsrc_t ra = make_rsrc(g.a, 0x7fffffff);
   const rsrc_t rw = make_rsrc(g.w, 0x7fffffff);
-  int aoff[4], woff[4];
+  const int lrow = lane / CH;
+  const int lchunk = (lane % CH) ^ swz<CH>(lrow);   // rows start at multiples of RPL
+  const int kspan = g.K / g.splits, k0 = split * kspan;
+  int aoff[NLA], woff[NLW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + lr + 32 * i;
+  for (int i = 0; i < NLA; ++i) {
+    const int m = m0 + RPL * (NLA * wave + i) + lrow;
     const int arow = g.a_group > 0 ? (m / g.a_group) * g.a_group_stride + m % g.a_group : m;
-    aoff[i] = m < g.M ? (arow * g.lda + lc) * (int)sizeof(T) : -1;
-    woff[i] = ((n0 + lr + 32 * i) * g.ldw + lc) * (int)sizeof(T);
+    aoff[i] = m < g.M ? (arow * g.lda + k0 + 8 * lchunk) * (int)sizeof(T) : -1;
   }
-  u32x4 pa[4], pw[4];
-  auto load = [&](int ks) {
-    const int kb = ks * kGK * (int)sizeof(T);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pa[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[i] < 0 ? -1 : aoff[i] + kb, 0, 0);
-      pw[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, woff[i] + kb, 0, 0);
-    }
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *(u32x4*)&sa[buf][(lr + 32 * i) * kGld + lc] = pa[i];
-      *(u32x4*)&sw[buf][(lr + 32 * i) * kGld + lc] = pw[i];
-    }
-  };
+  for (int i = 0; i < NLW; ++i)
+    woff[i] = ((n0 + RPL * (NLW * wave + i) + lrow) * g.ldw + k0 + 8 * lchunk) * (int)sizeof(T);
 
-  const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;
-  f32x16 acc[2][2];   // [n sub-tile][m sub-tile]
+  const int wm = (wave % WAVES_M) * WM, wn = (wave / WAVES_M) * WN;
+  f32x16 acc[NI][MI];   // [n sub-tile][m sub-tile]
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < MI; ++j) acc[i][j] = f32x16{};
 
-  const int nk = g.K / kGK;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int ks = 0; ks < nk; ++ks) {
-    if (ks + 1 < nk) load(ks + 1);
-    const int buf = ks & 1;
+  // fragment of tile row rr (sub-tiles start at multiples of 32), chunk c
+  auto frag = [&](const T* tile, int rr, int c) {
+    return *(const v8*)(tile + (rr * CH + (c ^ swz<CH>(rr))) * 8);
+  };
+  const int nk = kspan / KS;
+  const int kstep = KS * (int)sizeof(T);
+  auto issue = [&](auto J, int ks) {   // loads of step ks into stage J
+    dma_tile<T, NLA>(ra, aoff, ks * kstep, abuf(J), wave);
+    dma_tile<T, NLW>(rw, woff, ks * kstep, wbuf(J), wave);
+  };
+  // step ks (stage J = ks % ST): issue step ks + D into stage J + D, multiply stage J,
+  // wait until step ks + 1 has landed (the D - 1 later steps may stay in flight), barrier
+  auto step = [&](auto J, int ks) {
+    constexpr int j = decltype(J)::value;
+    if (ks + D < nk) issue(std::integral_constant<int, j + D>{}, ks + D);
+    const T* ca = abuf(J);
+    const T* cw = wbuf(J);
 #pragma unroll
-    for (int kk = 0; kk < kGK / 16; ++kk) {
-      v8 wf[2], xf[2];
+    for (int kk = 0; kk < KS / 16; ++kk) {
+      v8 wf[NI], xf[MI];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        wf[i] = *(const v8*)&sw[buf][(wn + 32 * i + n) * kGld + 16 * kk + 8 * gq];
+      for (int i = 0; i < NI; ++i) wf[i] = frag(cw, wn + 32 * i + n, 2 * kk + gq);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        xf[j] = *(const v8*)&sa[buf][(wm + 32 * j + n) * kGld + 16 * kk + 8 * gq];
+      for (int q = 0; q < MI; ++q) xf[q] = frag(ca, wm + 32 * q + n, 2 * kk + gq);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(wf[i], xf[j], acc[i][j]);
+        for (int q = 0; q < MI; ++q) acc[i][q] = mfma32(wf[i], xf[q], acc[i][q]);
     }
-    if (ks + 1 < nk) store((ks + 1) & 1);
-    __syncthreads();
+    if (ks + D < nk) wait_vm<(D - 1) * NL>();
+    else wait_vm<0>();
+    step_barrier();
+  };
+  // prologue: steps 0 .. D - 1 in flight, step 0 landed
+  issue(std::integral_constant<int, 0>{}, 0);
+  if (D > 1 && 1 < nk) issue(std::integral_constant<int, 1>{}, 1);
+  if (D > 2 && 2 < nk) issue(std::integral_constant<int, 2>{}, 2);
+  if (nk >= D) wait_vm<(D - 1) * NL>();
+  else wait_vm<0>();
+  step_barrier();
+  int ks = 0;
+  for (; ks + ST <= nk; ks += ST) {
+    step(std::integral_constant<int, 0>{}, ks);
+    step(std::integral_constant<int, 1>{}, ks + 1);
+    if constexpr (ST > 2) step(std::integral_constant<int, 2>{}, ks + 2);
+    if constexpr (ST > 3) step(std::integral_constant<int, 3>{}, ks + 3);
   }
+  if (ks < nk) step(std::integral_constant<int, 0>{}, ks);
+  if (ks + 1 < nk) step(std::integral_constant<int, 1>{}, ks + 1);
+  if constexpr (ST > 2) if (ks + 2 < nk) step(std::integral_constant<int, 2>{}, ks + 2);
 
   // epilogue: lane holds, for output row m, columns nb .. nb + 3 of each group
-  const T* bias = (const T*)g.bias;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < MI; ++j) {
     const int m = m0 + wm + 32 * j + n;
     if (m >= g.M) continue;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int nb = n0 + wn + 32 * i + 8 * jj + 4 * gq;
-        const v4 bv = *(const v4*)(bias + nb);
-        float r[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) r[e] = acc[i][j][4 * jj + e] + Elem<T>::to_f(bv[e]);
-        if (EPI == kEpiHeads) {
-          // n -> tensor n / D, head (n % D) / 64, dim n % 64; m -> (batch, row)
-          const int ti = nb / g.D, nn = nb - ti * g.D;
-          const int h = nn >> 6, d = nn & 63;
-          const int bb = m / g.rows, rr = m - bb * g.rows;
-          T* dst = (T*)g.heads[ti] + (((size_t)bb * g.H + h) * g.rows + rr) * 64 + d;
-          v4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = Elem<T>::from_f(r[e]);
-          *(v4*)dst = w;
-        } else if (EPI == kEpiGelu) {
-          v4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = Elem<T>::from_f(gelu(r[e]));
-          *(v4*)((T*)g.out + (size_t)m * g.ldo + nb) = w;
-        } else {
-          f32x4 z;
-          if (EPI == kEpiResidF32) {
-            const f32x4 rv = *(const f32x4*)((const float*)g.resid + (size_t)m * g.ldr + nb);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) z[e] = r[e] + rv[e];
-          } else {
-            const v4 rv = *(const v4*)((const T*)g.resid + (size_t)m * g.ldr + nb);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) z[e] = r[e] + Elem<T>::to_f(rv[e]);
-          }
-          *(f32x4*)((float*)g.out + (size_t)m * g.ldo + nb) = z;
-        }
-      }
-    }
+    for (int i = 0; i < NI; ++i)
+      epilogue_tile<T, EPI>(g, m, n0 + wn + 32 * i, gq, acc[i][j], split);
   }
 }
 
@@ -232,14 +378,160 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict_
   }
 }
 
+template <typename T, int TM, int TN, int WAVES, int WM, int WN, int KS, int ST>
+hipError_t gemm_launch(const GemmArgs& g, int tiles, hipStream_t st) {
+  switch (g.epi) {
+    case kEpiHeads:
+      gemm_kernel<T, kEpiHeads, TM, TN, WAVES, WM, WN, KS, ST><<<tiles, 64 * WAVES, 0, st>>>(g);
+      break;
+    case kEpiGelu:
+      gemm_kernel<T, kEpiGelu, TM, TN, WAVES, WM, WN, KS, ST><<<tiles, 64 * WAVES, 0, st>>>(g);
+      break;
+    case kEpiResidT:
+      gemm_kernel<T, kEpiResidT, TM, TN, WAVES, WM, WN, KS, ST><<<tiles, 64 * WAVES, 0, st>>>(g);
+      break;
+    case kEpiResidF32:
+      gemm_kernel<T, kEpiResidF32, TM, TN, WAVES, WM, WN, KS, ST><<<tiles, 64 * WAVES, 0, st>>>(g);
+      break;
+    case kEpiPartial:
+      gemm_kernel<T, kEpiPartial, TM, TN, WAVES, WM, WN, KS, ST><<<tiles, 64 * WAVES, 0, st>>>(g);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t gemm_t(const GemmArgs& g, hipStream_t st) {
-  const int tiles = ((g.M + kGT - 1) / kGT) * (g.N / kGT);
-  switch (g.epi) {
-    case kEpiHeads: gemm_kernel<T, kEpiHeads><<<tiles, kGThreads, 0, st>>>(g); break;
-    case kEpiGelu: gemm_kernel<T, kEpiGelu><<<tiles, kGThreads, 0, st>>>(g); break;
-    case kEpiResidT: gemm_kernel<T, kEpiResidT><<<tiles, kGThreads, 0, st>>>(g); break;
-    case kEpiResidF32: gemm_kernel<T, kEpiResidF32><<<tiles, kGThreads, 0, st>>>(g); break;
+  // 256 x 256 tiles when their grid still covers every CU at least once
+  const int big_tiles = g.N % 256 == 0 ? ((g.M + 255) / 256) * (g.N / 256) : 0;
+  if (big_tiles >= 256 && g.splits == 1)
+    return gemm_launch<T, 256, 256, 8, 128, 64, 64, 2>(g, big_tiles, st);
+  return gemm_launch<T, 128, 128, 4, 64, 64, 64, 2>(
+      g, ((g.M + 127) / 128) * (g.N / 128) * g.splits, st);
+}
+
+// LayerNorm of z = sum_s part[s] + bias + resid, one row per wave (the split-K
+// reduction of the row's GEMM, in a fixed order, fused into the row kernel).
+template <typename T, int NPL, bool RESID_F32>
+__global__ __launch_bounds__(256) void layernorm_parts_kernel(
+    const float* __restrict__ part, int splits, const T* __restrict__ bias,
+    const void* __restrict__ resid, const T* __restrict__ gamma, const T* __restrict__ beta,
+    float eps, int M, int N, float* __restrict__ out_f32, T* __restrict__ out_t) {
+  typedef typename Elem<T>::vec4 v4;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= M) return;
+  const size_t sstride = (size_t)M * N;
+  f32x4 x[NPL];
+#pragma unroll
+  for (int c = 0; c < NPL; ++c) {
+    const int col = 4 * (lane + 64 * c);
+    const size_t at = (size_t)row * N + col;
+    f32x4 z = *(const f32x4*)(part + at);
+    int sp = 1;
+    for (; sp + 4 <= splits; sp += 4) {   // four loads in flight; the sum keeps the order
+      f32x4 p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = *(const f32x4*)(part + (sp + i) * sstride + at);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z += p[i];
+    }
+    for (; sp < splits; ++sp) z += *(const f32x4*)(part + sp * sstride + at);
+    const v4 bv = *(const v4*)(bias + col);
+    if (RESID_F32) {
+      z += *(const f32x4*)((const float*)resid + at);
+    } else {
+      const v4 rv = *(const v4*)((const T*)resid + at);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) z[e] += Elem<T>::to_f(rv[e]);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) z[e] += Elem<T>::to_f(bv[e]);
+    x[c] = z;
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NPL; ++c) s += (x[c][0] + x[c][1]) + (x[c][2] + x[c][3]);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) s += __shfl_xor(s, d, 64);
+  const float mean = s / (float)N;
+  float q = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NPL; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float dv = x[c][e] - mean;
+      q += dv * dv;
+    }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) q += __shfl_xor(q, d, 64);
+  const float inv = 1.0f / sqrtf(q / (float)N + eps);
+#pragma unroll
+  for (int c = 0; c < NPL; ++c) {
+    const int col = 4 * (lane + 64 * c);
+    const v4 gv = *(const v4*)(gamma + col);
+    const v4 bv = *(const v4*)(beta + col);
+    f32x4 y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      y[e] = (x[c][e] - mean) * inv * Elem<T>::to_f(gv[e]) + Elem<T>::to_f(bv[e]);
+    if (out_f32) *(f32x4*)(out_f32 + (size_t)row * N + col) = y;
+    if (out_t) {
+      v4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = Elem<T>::from_f(y[e]);
+      *(v4*)(out_t + (size_t)row * N + col) = w;
+    }
+  }
+}
+
+// Head-split epilogue of a split-K GEMM: thread per 4 consecutive columns of a row.
+template <typename T>
+__global__ __launch_bounds__(256) void splitk_heads_kernel(GemmArgs g) {
+  typedef typename Elem<T>::vec4 v4;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int per_row = g.N / 4;
+  if (idx >= (int64_t)g.M * per_row) return;
+  const int m = (int)(idx / per_row), n = 4 * (int)(idx - (int64_t)m * per_row);
+  const size_t sstride = (size_t)g.M * g.N, at = (size_t)m * g.N + n;
+  // loads of four splits in flight at a time; the sum keeps the split order
+  f32x4 z = *(const f32x4*)(g.part + at);
+  int sp = 1;
+  for (; sp + 4 <= g.splits; sp += 4) {
+    f32x4 p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = *(const f32x4*)(g.part + (sp + i) * sstride + at);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) z += p[i];
+  }
+  for (; sp < g.splits; ++sp) z += *(const f32x4*)(g.part + sp * sstride + at);
+  const v4 bv = *(const v4*)((const T*)g.bias + n);
+  const int ti = n / g.D, nn = n - ti * g.D;
+  const int h = nn >> 6, d = nn & 63;
+  const int bb = m / g.rows, rr = m - bb * g.rows;
+  v4 w;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = Elem<T>::from_f(z[e] + Elem<T>::to_f(bv[e]));
+  *(v4*)((T*)g.heads[ti] + (((size_t)bb * g.H + h) * g.rows + rr) * 64 + d) = w;
+}
+
+template <typename T, bool RESID_F32>
+hipError_t layernorm_parts_t(const float* part, int splits, const void* bias, const void* resid,
+                             const void* gamma, const void* beta, float eps, int M, int N,
+                             float* out_f32, void* out_t, hipStream_t st) {
+  const int grid = (M + 3) / 4;
+  const T* b = (const T*)bias;
+  const T* gm = (const T*)gamma;
+  const T* bt = (const T*)beta;
+  switch (N / 256) {
+#define LF_LNP(C)                                                                          \
+  case C:                                                                                  \
+    layernorm_parts_kernel<T, C, RESID_F32><<<grid, 256, 0, st>>>(part, splits, b, resid, gm, bt, \
+                                                                  eps, M, N, out_f32, (T*)out_t); \
+    break;
+    LF_LNP(1) LF_LNP(2) LF_LNP(3) LF_LNP(4) LF_LNP(8) LF_LNP(16)
+#undef LF_LNP
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -269,6 +561,44 @@ bool gemm_shape_ok(int M, int N, int K) {
   return M >= 1 && N >= kGT && N % kGT == 0 && K >= kGK && K % kGK == 0;
 }
 
+int gemm_splits(int M, int N, int K) {
+  const int tiles = ((M + 127) / 128) * (N / 128);
+  int s = 1;
+  while (s < 16 && tiles * s < 256 && (K / (2 * s)) % 64 == 0 && K / (2 * s) >= 64) s *= 2;
+  return s;
+}
+
+hipError_t launch_layernorm_parts(int dtype, const float* part, int splits, const void* bias,
+                                  const void* resid, bool resid_f32, const void* gamma,
+                                  const void* beta, float eps, int M, int N, float* out_f32,
+                                  void* out_t, hipStream_t st) {
+  if (!layernorm_width_ok(N) || splits < 1) return hipErrorInvalidValue;
+  switch (dtype) {
+    case 1:
+      return resid_f32 ? layernorm_parts_t<f16, true>(part, splits, bias, resid, gamma, beta, eps,
+                                                      M, N, out_f32, out_t, st)
+                       : layernorm_parts_t<f16, false>(part, splits, bias, resid, gamma, beta, eps,
+                                                       M, N, out_f32, out_t, st);
+    case 2:
+      return resid_f32 ? layernorm_parts_t<bf16, true>(part, splits, bias, resid, gamma, beta,
+                                                       eps, M, N, out_f32, out_t, st)
+                       : layernorm_parts_t<bf16, false>(part, splits, bias, resid, gamma, beta,
+                                                        eps, M, N, out_f32, out_t, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_splitk_heads(const GemmArgs& g, hipStream_t st) {
+  const int64_t n = (int64_t)g.M * (g.N / 4);
+  const unsigned grid = (unsigned)((n + 255) / 256);
+  switch (g.dtype) {
+    case 1: splitk_heads_kernel<f16><<<grid, 256, 0, st>>>(g); break;
+    case 2: splitk_heads_kernel<bf16><<<grid, 256, 0, st>>>(g); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 bool layernorm_width_ok(int N) {
   const int c = N / 256;
   return N % 256 == 0 && (c == 1 || c == 2 || c == 3 || c == 4 || c == 8 || c == 16);
@@ -276,6 +606,8 @@ bool layernorm_width_ok(int N) {
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   if (!gemm_shape_ok(g.M, g.N, g.K)) return hipErrorInvalidValue;
+  if (g.splits < 1 || g.K % (64 * g.splits) != 0 || (g.splits > 1) != (g.epi == kEpiPartial))
+    return hipErrorInvalidValue;
   switch (g.dtype) {
     case 1: return gemm_t<f16>(g, st);
     case 2: return gemm_t<bf16>(g, st);

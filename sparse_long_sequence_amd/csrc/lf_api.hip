@@ -5,6 +5,7 @@
 // 端到端性能解析".  The shape rules are its four hard constraints (section
 // "使用前提：四条硬性约束"); where the page's implementation aborts the process on a
 // violation, these entry points return LF_ERR_INVALID_ARGUMENT instead.
+#include <algorithm>
 #include <climits>
 #include <cstdarg>
 #include <cstdio>
@@ -174,7 +175,8 @@ int validate_layer(int dtype, int B, int S, int hidden, int H, int ffn, int W, i
 // fp32 pre-LayerNorm buffer, h1 in fp32 and in the layer dtype, and the FFN
 // intermediate (which reuses the q..vg area when it fits: they are dead by then).
 struct LayerWs {
-  size_t act_bytes, qkv_off, qg_off, attn_off, z_off, h1f_off, h1t_off, u_off, total;
+  size_t act_bytes, qkv_off, qg_off, attn_off, z_off, h1f_off, h1t_off, u_off, part_off, total;
+  int split_qg, split_o, split_ffn2;   // split-K factors of the GEMMs with small grids
 };
 
 LayerWs layer_ws(int dtype, int B, int S, int hidden, int H, int ffn, int G) {
@@ -196,6 +198,17 @@ LayerWs layer_ws(int dtype, int B, int S, int hidden, int H, int ffn, int G) {
     L.u_off = off;
     off += u_bytes;
   }
+  // fp32 partial sums of the split-K GEMMs (global-query projection, output
+  // projection, FFN2), one at a time
+  L.split_qg = G > 0 ? lf::gemm_splits(B * G, hidden, hidden) : 1;
+  L.split_o = lf::gemm_splits((int)M, hidden, hidden);
+  L.split_ffn2 = lf::gemm_splits((int)M, hidden, ffn);
+  size_t part = 0;
+  if (L.split_qg > 1) part = (size_t)L.split_qg * B * G * hidden * 4;
+  if (L.split_o > 1) part = std::max(part, (size_t)L.split_o * M * hidden * 4);
+  if (L.split_ffn2 > 1) part = std::max(part, (size_t)L.split_ffn2 * M * hidden * 4);
+  L.part_off = off;
+  off += align256(part);
   L.total = off;
   return L;
 }
@@ -278,8 +291,10 @@ int run_layer(int dtype, const lf_layer_weights* w, const void* x, const LayerMa
     g.w = Wt; g.ldw = ldw; g.bias = bias;
     g.M = Mr; g.N = N; g.K = K;
     g.D = D; g.H = H; g.rows = S;
+    g.splits = 1;
     return g;
   };
+  float* part = (float*)(ws + L.part_off);
   hipError_t he;
   // step 1: packed projections, split into heads ([B, H, S, 64] each)
   {
@@ -292,7 +307,17 @@ int run_layer(int dtype, const lf_layer_weights* w, const void* x, const LayerMa
     lf::GemmArgs g = gemm(lf::kEpiHeads, x, D, G, S, w->w_qg, D, w->b_qg, B * G, D, D);
     g.heads[0] = qg;
     g.rows = G;
-    if ((he = lf::launch_gemm(g, st)) != hipSuccess) return hip_fail(he, "global-query GEMM");
+    if (L.split_qg > 1) {
+      // B * G rows: a handful of tiles, so the K range is split and reduced after
+      g.epi = lf::kEpiPartial;
+      g.splits = L.split_qg;
+      g.part = part;
+      if ((he = lf::launch_gemm(g, st)) != hipSuccess) return hip_fail(he, "global-query GEMM");
+      if ((he = lf::launch_splitk_heads(g, st)) != hipSuccess)
+        return hip_fail(he, "global-query reduction");
+    } else if ((he = lf::launch_gemm(g, st)) != hipSuccess) {
+      return hip_fail(he, "global-query GEMM");
+    }
   }
   // steps 3-4: attention, heads joined ([B, S, H * 64])
   {
@@ -309,7 +334,16 @@ int run_layer(int dtype, const lf_layer_weights* w, const void* x, const LayerMa
     if ((he = lf::launch_attention(a, st)) != hipSuccess) return hip_fail(he, "attention");
   }
   // step 5: output projection + bias + residual (fp32), LayerNorm
-  {
+  if (L.split_o > 1) {
+    // split-K partials, reduced with bias and residual inside the LayerNorm
+    lf::GemmArgs g = gemm(lf::kEpiPartial, attn, D, 0, 0, w->w_o, D, w->b_o, M, D, D);
+    g.splits = L.split_o;
+    g.part = part;
+    if ((he = lf::launch_gemm(g, st)) != hipSuccess) return hip_fail(he, "output GEMM");
+    if ((he = lf::launch_layernorm_parts(dtype, part, L.split_o, w->b_o, x, false, w->ln1_g,
+                                         w->ln1_b, ln_eps, M, D, h1f, h1t, st)) != hipSuccess)
+      return hip_fail(he, "LayerNorm 1");
+  } else {
     lf::GemmArgs g = gemm(lf::kEpiResidT, attn, D, 0, 0, w->w_o, D, w->b_o, M, D, D);
     g.out = z; g.ldo = D; g.resid = x; g.ldr = D;
     if ((he = lf::launch_gemm(g, st)) != hipSuccess) return hip_fail(he, "output GEMM");
@@ -322,12 +356,24 @@ int run_layer(int dtype, const lf_layer_weights* w, const void* x, const LayerMa
     lf::GemmArgs g = gemm(lf::kEpiGelu, h1t, D, 0, 0, w->w_ffn1, D, w->b_ffn1, M, ffn, D);
     g.out = u; g.ldo = ffn;
     if ((he = lf::launch_gemm(g, st)) != hipSuccess) return hip_fail(he, "FFN GEMM 1");
-    lf::GemmArgs g2 = gemm(lf::kEpiResidF32, u, ffn, 0, 0, w->w_ffn2, ffn, w->b_ffn2, M, D, ffn);
-    g2.out = z; g2.ldo = D; g2.resid = h1f; g2.ldr = D;
-    if ((he = lf::launch_gemm(g2, st)) != hipSuccess) return hip_fail(he, "FFN GEMM 2");
-    if ((he = lf::launch_layernorm(dtype, z, w->ln2_g, w->ln2_b, ln_eps, M, D, nullptr, y, st)) !=
-        hipSuccess)
-      return hip_fail(he, "LayerNorm 2");
+    if (L.split_ffn2 > 1) {
+      lf::GemmArgs g2 = gemm(lf::kEpiPartial, u, ffn, 0, 0, w->w_ffn2, ffn, w->b_ffn2, M, D, ffn);
+      g2.splits = L.split_ffn2;
+      g2.part = part;
+      if ((he = lf::launch_gemm(g2, st)) != hipSuccess) return hip_fail(he, "FFN GEMM 2");
+      if ((he = lf::launch_layernorm_parts(dtype, part, L.split_ffn2, w->b_ffn2, h1f, true,
+                                           w->ln2_g, w->ln2_b, ln_eps, M, D, nullptr, y, st)) !=
+          hipSuccess)
+        return hip_fail(he, "LayerNorm 2");
+    } else {
+      lf::GemmArgs g2 =
+          gemm(lf::kEpiResidF32, u, ffn, 0, 0, w->w_ffn2, ffn, w->b_ffn2, M, D, ffn);
+      g2.out = z; g2.ldo = D; g2.resid = h1f; g2.ldr = D;
+      if ((he = lf::launch_gemm(g2, st)) != hipSuccess) return hip_fail(he, "FFN GEMM 2");
+      if ((he = lf::launch_layernorm(dtype, z, w->ln2_g, w->ln2_b, ln_eps, M, D, nullptr, y,
+                                     st)) != hipSuccess)
+        return hip_fail(he, "LayerNorm 2");
+    }
   }
   return LF_OK;
 }

@@ -66,6 +66,8 @@ enum GemmEpi {
   kEpiGelu = 1,      // out[m * ldo + n] = gelu(acc + bias), dtype
   kEpiResidT = 2,    // out[m * ldo + n] = acc + bias + resid[m * ldr + n] (resid dtype), fp32
   kEpiResidF32 = 3,  // same with an fp32 residual
+  kEpiPartial = 4,   // split-K: part[split][m * N + n] = acc (fp32, no bias); reduced by
+                     // launch_layernorm_parts / launch_splitk_heads
 };
 
 struct GemmArgs {
@@ -82,13 +84,29 @@ struct GemmArgs {
   int ldo;
   const void* resid;
   int ldr;
+  int splits;            // split-K factor (kEpiPartial; else 1): split s sums k in
+                         // [s K / splits, (s + 1) K / splits)
+  float* part;           // kEpiPartial output: [splits][M][N] fp32
 };
 
 // N a positive multiple of 128, K of 64, M >= 1.
 bool gemm_shape_ok(int M, int N, int K);
+// Split-K factor for a GEMM whose 128 x 128 grid would leave CUs idle: the smallest
+// power of two (up to 16) that brings the grid to 256 workgroups, with K / splits a
+// multiple of 64; 1 when the grid is large enough.
+int gemm_splits(int M, int N, int K);
 // Row widths the LayerNorm kernel takes (multiples of 256 up to 4096).
 bool layernorm_width_ok(int N);
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
+// LayerNorm of z = sum_s part[s] + bias + resid (resid in the layer dtype, or fp32
+// when resid_f32): the reduction of a split-K GEMM fused into the row kernel.
+hipError_t launch_layernorm_parts(int dtype, const float* part, int splits, const void* bias,
+                                  const void* resid, bool resid_f32, const void* gamma,
+                                  const void* beta, float eps, int M, int N, float* out_f32,
+                                  void* out_t, hipStream_t st);
+// Head-split epilogue of a split-K GEMM: heads[0] gets sum_s part[s] + bias in the
+// kEpiHeads layout (row m -> (m / rows, m % rows), column n -> head n / 64, dim n % 64).
+hipError_t launch_splitk_heads(const GemmArgs& g, hipStream_t st);
 hipError_t launch_layernorm(int dtype, const float* z, const void* gamma, const void* beta,
                             float eps, int M, int N, float* out_f32, void* out_t,
                             hipStream_t st);
