@@ -116,6 +116,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the oracle CPU baseline (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-calls", type=int, default=20,
+                    help="after the timed steps, time this many single steps each right after "
+                         "a 512 MiB scrub write (caches cold; reported beside the value)")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="after the timed loop, run one plain elementwise copy of this many MiB "
                          "(fp32 in, fp32 out) so HBM counters can be scaled by a known size")
@@ -165,6 +168,27 @@ def main():
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     n_k, k_ms = args.steps * LAUNCHES_PER_STEP, e0.elapsed_time(e1)
+    # secondary: cold caches.  A 512 MiB fill evicts L2 and the 256 MiB Infinity Cache;
+    # the events and the step are enqueued while the fill still runs, so the interval
+    # holds only the step.
+    cold = None
+    if args.cold_calls > 0:
+        scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        times = []
+        for i in range(args.cold_calls):
+            scrub.fill_(i & 0xff)
+            c0 = torch.cuda.Event(enable_timing=True)
+            c1 = torch.cuda.Event(enable_timing=True)
+            c0.record()
+            step()
+            c1.record()
+            torch.cuda.synchronize()
+            times.append(c0.elapsed_time(c1))
+        del scrub
+        times.sort()
+        cold = {"ms_per_step_median": round(times[len(times) // 2], 6),
+                "ms_per_step_min": round(times[0], 6), "calls": args.cold_calls,
+                "scrub_mib": 512}
     if args.calibrate_copy_mb > 0:
         n = args.calibrate_copy_mb * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -224,6 +248,8 @@ def main():
         "pct_mfma_peak": round(100.0 * tflops / PEAK_FP16_TFLOPS, 3),
         "roofline": roof,
     }
+    if cold is not None:
+        res["cold_cache"] = cold
     if not args.no_cpu_baseline and args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(inp, wl, args.cpu_seconds)
     print(json.dumps(res), flush=True)
