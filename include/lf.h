@@ -180,11 +180,13 @@ size_t lf_encoder_layer_workspace_bytes(int dtype, int B, int S, int hidden, int
  *   [q|k|v|kg|vg] = x W_proj^T + b_proj, split into heads; qg = x[:, :G] W_qg^T + b_qg;
  *   a  = band + global attention (as lf_attn_forward, scale attn_scale), heads joined;
  *   h1 = LayerNorm(x + a W_o^T + b_o; ln1)    (biased variance, eps ln_eps)
- *   y  = LayerNorm(h1 + GELU(h1 W_1^T + b_1) W_2^T + b_2; ln2)   (exact erf GELU)
- * x, y: [B, S, hidden] in `dtype`, which must be LF_F16 or LF_BF16 (LF_F32 returns
- * LF_ERR_UNSUPPORTED).  Shape rules: the attention rules of lf_attn_forward, plus
- * hidden == 64*H, hidden and ffn multiples of 128, hidden one of 256, 512, 768,
- * 1024, 2048, 4096 (LayerNorm row widths), B*S*ffn*2 < 2^31.  w_qg / b_qg may be
+ *   y  = LayerNorm(h1 + GELU(h1 W_1^T + b_1) W_2^T + b_2; ln2)
+ *        (erf GELU; erf evaluated within 1.5e-7 absolute)
+ * x, y: [B, S, hidden] in `dtype` (LF_F16, LF_BF16 or LF_F32; fp32 runs its GEMMs on
+ * fp32 MFMA and its attention on the vector ALUs from masks preprocessed inside the
+ * call).  Shape rules: the attention rules of lf_attn_forward, plus hidden == 64*H,
+ * hidden and ffn multiples of 128, hidden one of 256, 512, 768, 1024, 2048, 4096
+ * (LayerNorm row widths), B*S*ffn*sizeof(dtype) < 2^31.  w_qg / b_qg may be
  * NULL when G == 0.  `workspace` (device, 256-byte aligned, ws_bytes >=
  * lf_encoder_layer_workspace_bytes) holds every intermediate: attention tickets
  * first, then q, k, v, kg, vg, qg, the attention output, the fp32 pre-LayerNorm

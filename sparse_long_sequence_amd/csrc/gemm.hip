@@ -162,12 +162,18 @@ __device__ inline int swz(int r) {
 
 template <typename T, int NL>
 __device__ inline void dma_tile(rsrc_t r, const int off[NL], int kb, T* lds_tile, int wave) {
+  constexpr int EPC = 16 / (int)sizeof(T);   // elements per 16-byte chunk
 #pragma unroll
   for (int i = 0; i < NL; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (__attribute__((address_space(3))) void*)(lds_tile + (wave * NL + i) * 64 * 8), 16,
+        r, (__attribute__((address_space(3))) void*)(lds_tile + (wave * NL + i) * 64 * EPC), 16,
         off[i] < 0 ? -1 : off[i] + kb, 0, 0, 0);
 }
+
+// 16-byte MFMA operand fragment: 8 fp16 / bf16 values (one 32x32x16 MFMA) or 4 fp32
+// values (four 32x32x2 MFMAs).
+template <typename T> struct GemmFrag { typedef typename Elem<T>::vec8 type; };
+template <> struct GemmFrag<float> { typedef f32x4 type; };
 
 // Workgroup barrier without __syncthreads' release fence: that fence would wait for
 // every load in flight (the direct-to-LDS loads count as pending LDS writes), which
@@ -192,10 +198,11 @@ __device__ inline void wait_vm() {
 // other stages and does not make the current step's LDS reads wait for them.
 template <typename T, int EPI, int TM, int TN, int WAVES, int WM, int WN, int KS, int ST>
 __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs g) {
-  typedef typename Elem<T>::vec8 v8;
+  typedef typename GemmFrag<T>::type v8;
   constexpr int MI = WM / 32, NI = WN / 32;    // MFMA tiles per wave
   constexpr int WAVES_M = TM / WM;
-  constexpr int CH = KS / 8;                   // 16-byte chunks per tile row
+  constexpr int EPC = 16 / (int)sizeof(T);     // elements per 16-byte chunk
+  constexpr int CH = KS / EPC;                 // 16-byte chunks per tile row
   constexpr int RPL = 64 / CH;                 // tile rows per wave-wide load
   constexpr int NLA = TM / (RPL * WAVES), NLW = TN / (RPL * WAVES);   // loads per step
   constexpr int NL = NLA + NLW;
@@ -250,11 +257,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs g) {
   for (int i = 0; i < NLA; ++i) {
     const int m = m0 + RPL * (NLA * wave + i) + lrow;
     const int arow = g.a_group > 0 ? (m / g.a_group) * g.a_group_stride + m % g.a_group : m;
-    aoff[i] = m < g.M ? (arow * g.lda + k0 + 8 * lchunk) * (int)sizeof(T) : -1;
+    aoff[i] = m < g.M ? (arow * g.lda + k0 + EPC * lchunk) * (int)sizeof(T) : -1;
   }
 #pragma unroll
   for (int i = 0; i < NLW; ++i)
-    woff[i] = ((n0 + RPL * (NLW * wave + i) + lrow) * g.ldw + k0 + 8 * lchunk) * (int)sizeof(T);
+    woff[i] = ((n0 + RPL * (NLW * wave + i) + lrow) * g.ldw + k0 + EPC * lchunk) * (int)sizeof(T);
 
   const int wm = (wave % WAVES_M) * WM, wn = (wave / WAVES_M) * WN;
   f32x16 acc[NI][MI];   // [n sub-tile][m sub-tile]
@@ -265,7 +272,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs g) {
 
   // fragment of tile row rr (sub-tiles start at multiples of 32), chunk c
   auto frag = [&](const T* tile, int rr, int c) {
-    return *(const v8*)(tile + (rr * CH + (c ^ swz<CH>(rr))) * 8);
+    return *(const v8*)(tile + (rr * CH + (c ^ swz<CH>(rr))) * EPC);
   };
   const int nk = kspan / KS;
   const int kstep = KS * (int)sizeof(T);
@@ -281,7 +288,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs g) {
     const T* ca = abuf(J);
     const T* cw = wbuf(J);
 #pragma unroll
-    for (int kk = 0; kk < KS / 16; ++kk) {
+    for (int kk = 0; kk < KS / (2 * EPC); ++kk) {   // two chunks (the g halves) per round
       v8 wf[NI], xf[MI];
 #pragma unroll
       for (int i = 0; i < NI; ++i) wf[i] = frag(cw, wn + 32 * i + n, 2 * kk + gq);
@@ -405,9 +412,10 @@ template <typename T>
 hipError_t gemm_t(const GemmArgs& g, hipStream_t st) {
   // 256 x 256 tiles when their grid still covers every CU at least once
   const int big_tiles = g.N % 256 == 0 ? ((g.M + 255) / 256) * (g.N / 256) : 0;
+  constexpr int KS = 128 / (int)sizeof(T);   // 128-byte tile rows: 64 fp16 / bf16, 32 fp32
   if (big_tiles >= 256 && g.splits == 1)
-    return gemm_launch<T, 256, 256, 8, 128, 64, 64, 2>(g, big_tiles, st);
-  return gemm_launch<T, 128, 128, 4, 64, 64, 64, 2>(
+    return gemm_launch<T, 256, 256, 8, 128, 64, KS, 2>(g, big_tiles, st);
+  return gemm_launch<T, 128, 128, 4, 64, 64, KS, 2>(
       g, ((g.M + 127) / 128) * (g.N / 128) * g.splits, st);
 }
 
@@ -574,6 +582,11 @@ hipError_t launch_layernorm_parts(int dtype, const float* part, int splits, cons
                                   void* out_t, hipStream_t st) {
   if (!layernorm_width_ok(N) || splits < 1) return hipErrorInvalidValue;
   switch (dtype) {
+    case 0:
+      return resid_f32 ? layernorm_parts_t<float, true>(part, splits, bias, resid, gamma, beta,
+                                                        eps, M, N, out_f32, out_t, st)
+                       : layernorm_parts_t<float, false>(part, splits, bias, resid, gamma, beta,
+                                                         eps, M, N, out_f32, out_t, st);
     case 1:
       return resid_f32 ? layernorm_parts_t<f16, true>(part, splits, bias, resid, gamma, beta, eps,
                                                       M, N, out_f32, out_t, st)
@@ -592,6 +605,7 @@ hipError_t launch_splitk_heads(const GemmArgs& g, hipStream_t st) {
   const int64_t n = (int64_t)g.M * (g.N / 4);
   const unsigned grid = (unsigned)((n + 255) / 256);
   switch (g.dtype) {
+    case 0: splitk_heads_kernel<float><<<grid, 256, 0, st>>>(g); break;
     case 1: splitk_heads_kernel<f16><<<grid, 256, 0, st>>>(g); break;
     case 2: splitk_heads_kernel<bf16><<<grid, 256, 0, st>>>(g); break;
     default: return hipErrorInvalidValue;
@@ -609,6 +623,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   if (g.splits < 1 || g.K % (64 * g.splits) != 0 || (g.splits > 1) != (g.epi == kEpiPartial))
     return hipErrorInvalidValue;
   switch (g.dtype) {
+    case 0: return gemm_t<float>(g, st);
     case 1: return gemm_t<f16>(g, st);
     case 2: return gemm_t<bf16>(g, st);
   }
@@ -620,6 +635,7 @@ hipError_t launch_layernorm(int dtype, const float* z, const void* gamma, const 
                             hipStream_t st) {
   if (!layernorm_width_ok(N)) return hipErrorInvalidValue;
   switch (dtype) {
+    case 0: return layernorm_t<float>(z, gamma, beta, eps, M, N, out_f32, out_t, st);
     case 1: return layernorm_t<f16>(z, gamma, beta, eps, M, N, out_f32, out_t, st);
     case 2: return layernorm_t<bf16>(z, gamma, beta, eps, M, N, out_f32, out_t, st);
   }

@@ -151,10 +151,7 @@ lf::AttnArgs make_args(int dtype, const void* q, const void* k, const void* v, c
 // Shape rules of the encoder layer: the attention rules plus hidden == 64 * H, hidden
 // and ffn multiples of 128 (GEMM tiles) and LayerNorm widths the row kernel takes.
 int validate_layer(int dtype, int B, int S, int hidden, int H, int ffn, int W, int G) {
-  if (dtype != LF_F16 && dtype != LF_BF16) {
-    if (!known_dtype(dtype)) return fail(LF_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
-    return fail(LF_ERR_UNSUPPORTED, "lf_encoder_layer runs in fp16 or bf16");
-  }
+  if (!known_dtype(dtype)) return fail(LF_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
   if (int e = validate_attn(dtype, B, H, S, W, G)) return e;
   if (hidden != 64 * H)
     return fail(LF_ERR_INVALID_ARGUMENT, "hidden must be 64*H (hidden=%d, H=%d)", hidden, H);
@@ -165,7 +162,7 @@ int validate_layer(int dtype, int B, int S, int hidden, int H, int ffn, int W, i
     return fail(LF_ERR_INVALID_ARGUMENT, "hidden must be 256, 512, 768, 1024, 2048 or 4096");
   if (G > S) return fail(LF_ERR_INVALID_ARGUMENT, "G must be <= S");
   const int64_t M = (int64_t)B * S;
-  if (M * ffn * 2 > INT_MAX || M * hidden * 4 > (int64_t)1 << 40)
+  if (M * ffn * (int64_t)dtype_size(dtype) > INT_MAX || M * hidden * 4 > (int64_t)1 << 40)
     return fail(LF_ERR_INVALID_ARGUMENT, "B*S*ffn too large for 32-bit GEMM offsets");
   return LF_OK;
 }
@@ -176,6 +173,7 @@ int validate_layer(int dtype, int B, int S, int hidden, int H, int ffn, int W, i
 // intermediate (which reuses the q..vg area when it fits: they are dead by then).
 struct LayerWs {
   size_t act_bytes, qkv_off, qg_off, attn_off, z_off, h1f_off, h1t_off, u_off, part_off, total;
+  size_t pidx_off, pcnt_off, pbias_off;   // fp32: preprocessed masks (index, count, bias)
   int split_qg, split_o, split_ffn2;   // split-K factors of the GEMMs with small grids
 };
 
@@ -209,6 +207,13 @@ LayerWs layer_ws(int dtype, int B, int S, int hidden, int H, int ffn, int G) {
   if (L.split_ffn2 > 1) part = std::max(part, (size_t)L.split_ffn2 * M * hidden * 4);
   L.part_off = off;
   off += align256(part);
+  // fp32 attention runs on the vector ALUs from preprocessed masks
+  L.pidx_off = L.pcnt_off = L.pbias_off = 0;
+  if (dtype == LF_F32) {
+    L.pidx_off = off; off += align256(M * 4);
+    L.pcnt_off = off; off += align256((size_t)B * 4);
+    L.pbias_off = off; off += align256(M * es);
+  }
   L.total = off;
   return L;
 }
@@ -267,6 +272,11 @@ StackWs stack_ws(int dtype, int B, int S, int hidden, int H, int ffn, int G) {
   return W;
 }
 
+// The attention launch of one call: MFMA kernel for fp16 / bf16, vector ALU for fp32.
+hipError_t run_attention(const lf::AttnArgs& a, hipStream_t st) {
+  return a.dtype == LF_F32 ? lf::launch_attention_fp32(a, st) : lf::launch_attention(a, st);
+}
+
 // One encoder layer ([FT-LF] per-layer steps 1-6) as 8 launches on `st`; arguments
 // already validated.
 int run_layer(int dtype, const lf_layer_weights* w, const void* x, const LayerMasks& mk, int B,
@@ -322,16 +332,33 @@ int run_layer(int dtype, const lf_layer_weights* w, const void* x, const LayerMa
   // steps 3-4: attention, heads joined ([B, S, H * 64])
   {
     AttnWs aw = attn_ws(B, H, S, G);
-    lf::AttnArgs a = make_args(dtype, qkv[0], qkv[1], qkv[2], qg, qkv[3], qkv[4], mk.gidx,
-                               mk.gcnt, mk.bias, B, H, S, W, G, attn, ws, aw, aw.partials_off);
-    a.raw = mk.raw ? 1 : 0;
+    const int32_t* gidx = mk.gidx;
+    const int32_t* gcnt = mk.gcnt;
+    const void* mbias = mk.bias;
+    bool raw = mk.raw;
+    if (dtype == LF_F32 && raw) {
+      // the fp32 attention reads preprocessed masks: index, count and shifted mask
+      int32_t* pidx = (int32_t*)(ws + L.pidx_off);
+      int32_t* pcnt = (int32_t*)(ws + L.pcnt_off);
+      void* pbias = ws + L.pbias_off;
+      if ((he = lf::launch_prep(dtype, mk.global_mask, mk.local_mask, B, S, pidx, pcnt, pbias,
+                                nullptr, 0, st)) != hipSuccess)
+        return hip_fail(he, "layer mask preprocessing");
+      gidx = pidx;
+      gcnt = pcnt;
+      mbias = pbias;
+      raw = false;
+    }
+    lf::AttnArgs a = make_args(dtype, qkv[0], qkv[1], qkv[2], qg, qkv[3], qkv[4], gidx, gcnt,
+                               mbias, B, H, S, W, G, attn, ws, aw, aw.partials_off);
+    a.raw = raw ? 1 : 0;
     a.local_mask = mk.local_mask;
     a.global_mask = mk.global_mask;
     a.out_ss = D;
     a.out_sh = 64;
     a.out_sb = (int64_t)S * D;
     a.scale = attn_scale;
-    if ((he = lf::launch_attention(a, st)) != hipSuccess) return hip_fail(he, "attention");
+    if ((he = run_attention(a, st)) != hipSuccess) return hip_fail(he, "attention");
   }
   // step 5: output projection + bias + residual (fp32), LayerNorm
   if (L.split_o > 1) {
@@ -426,9 +453,6 @@ int cached_workspace(hipStream_t st, size_t tickets, size_t part_bytes, char** b
   return LF_OK;
 }
 
-hipError_t run_attention(const lf::AttnArgs& a, hipStream_t st) {
-  return a.dtype == LF_F32 ? lf::launch_attention_fp32(a, st) : lf::launch_attention(a, st);
-}
 
 bool debug_check_enabled() {
   const char* e = getenv("LF_DEBUG_CHECK");

@@ -24,6 +24,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   typedef float vec8 __attribute__((ext_vector_type(8)));
+  typedef f32x4 vec4;
   __device__ static inline float to_f(float x) { return x; }
   __device__ static inline float from_f(float x) { return x; }
 };
@@ -48,6 +49,16 @@ __device__ inline f32x16 mfma32(const f16x8& a, const f16x8& b, const f32x16& c)
 }
 __device__ inline f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// fp32: D = A(32x2) * B(2x32) + C four times, one k pair per element of the 16-byte
+// fragments (lane (n, g) holds 4 consecutive k of row n; both operands pair the same
+// k values, so the sum over k is complete).
+__device__ inline f32x16 mfma32(const f32x4& a, const f32x4& b, const f32x16& c) {
+  f32x16 d = c;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) d = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], b[e], d, 0, 0, 0);
+  return d;
 }
 
 // Sum of a pair of 16-bit values accumulated in fp32 (v_dot2 with a (1,1) vector).

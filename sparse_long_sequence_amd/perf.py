@@ -3,8 +3,9 @@
     python sparse_long_sequence_amd/perf.py attn  [--iters N]   # longformer-large attention
     python sparse_long_sequence_amd/perf.py attn_any [--iters N]  # same, 8 globals spread out
     python sparse_long_sequence_amd/perf.py prep  [--iters N]   # index compaction + mask shift
-    python sparse_long_sequence_amd/perf.py layer [--iters N]   # one fp16 encoder layer
-    python sparse_long_sequence_amd/perf.py stack [--iters N]   # 24-layer fp16 encoder, B1 S1024
+    python sparse_long_sequence_amd/perf.py layer [--iters N] [--dtype fp16|bf16|fp32]
+    python sparse_long_sequence_amd/perf.py stack [--iters N] [--dtype fp16|bf16|fp32]
+                                           # one encoder layer / the 24-layer encoder, B1 S1024
 
 Prints one JSON line per run: time per call (HIP events on the current stream around
 N back-to-back calls after a warm-up) and the algorithmic throughput.  This is the
@@ -122,12 +123,13 @@ def run_prep(iters: int, warmup: int) -> dict:
             "gbs_mask_shift": shift_bytes / (ms_shift * 1e-3) / 1e9}
 
 
-def run_layer(iters: int, warmup: int) -> dict:
+def run_layer(iters: int, warmup: int, dtype: str = "fp16") -> dict:
     wl = workloads.LAYER_FP16
     t = workloads.make_layer_inputs(wl)
-    x = t["x"].cuda()
-    w = {n: t[n].cuda() for n in lf.LAYER_WEIGHT_FIELDS}
-    lm, gm = t["local_mask"].cuda(), t["global_mask"].cuda()
+    td = workloads.TORCH_DTYPES[dtype]
+    x = t["x"].cuda().to(td)
+    w = {n: t[n].cuda().to(td) for n in lf.LAYER_WEIGHT_FIELDS}
+    lm, gm = t["local_mask"].cuda().to(td), t["global_mask"].cuda().to(td)
     y = torch.empty_like(x)
     nbytes = lf.encoder_layer_workspace_bytes(x.dtype, wl.B, wl.S, wl.hidden, wl.H, wl.ffn,
                                               wl.W, wl.G)
@@ -138,18 +140,18 @@ def run_layer(iters: int, warmup: int) -> dict:
     gemm = 2.0 * M * D * (5 * D + D + 2 * F) + 2.0 * wl.B * G * D * D
     pairs = G * S + (S - G) * (W + 1 + G) - (W // 2) * (W // 2 + 1)
     attn = 256.0 * pairs * wl.B * wl.H
-    return {"op": "encoder_layer", "workload": wl.name, "ms": ms,
+    return {"op": "encoder_layer", "workload": wl.name.replace("fp16", dtype), "ms": ms,
             "gemm_gflop": gemm / 1e9, "attn_gflop": attn / 1e9,
             "tflops": (gemm + attn) / (ms * 1e-3) / 1e12}
 
 
-def run_stack(iters: int, warmup: int, n_layers: int = 24) -> dict:
+def run_stack(iters: int, warmup: int, dtype: str = "fp16", n_layers: int = 24) -> dict:
     # the pages' benchmark model: 16 heads x 64, FFN 4096, window 512, 24 layers, at
     # batch 1 and sequence 1024; 16 leading global tokens (the count is not stated)
     B, S, D, H, F, W, G = 1, 1024, 1024, 16, 4096, 512, 16
     gen = torch.Generator(device="cuda")
     gen.manual_seed(20260006)
-    dt = torch.float16
+    dt = workloads.TORCH_DTYPES[dtype]
 
     def rnd(*shape, std=0.02):
         return (torch.randn(*shape, generator=gen, device="cuda") * std).to(dt)
@@ -177,7 +179,7 @@ def run_stack(iters: int, warmup: int, n_layers: int = 24) -> dict:
     gemm = 2.0 * M * D * (5 * D + D + 2 * F) + 2.0 * B * G * D * D
     pairs = G * S + (S - G) * (W + 1 + G) - (W // 2) * (W // 2 + 1)
     attn = 256.0 * pairs * B * H
-    return {"op": "encoder_forward", "workload": f"longformer_large_24L_fp16_B{B}_S{S}_W{W}_G{G}",
+    return {"op": "encoder_forward", "workload": f"longformer_large_24L_{dtype}_B{B}_S{S}_W{W}_G{G}",
             "layers": n_layers, "ms": ms, "ms_per_layer": ms / n_layers,
             "tflops": n_layers * (gemm + attn) / (ms * 1e-3) / 1e12}
 
@@ -188,9 +190,14 @@ def main():
     ap.add_argument("op", choices=["attn", "attn_any", "prep", "layer", "stack"])
     ap.add_argument("--iters", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--dtype", default="fp16", choices=["fp16", "bf16", "fp32"],
+                    help="layer / stack only")
     a = ap.parse_args()
-    fn = {"attn": run_attn, "attn_any": run_attn_any, "prep": run_prep, "layer": run_layer,
-          "stack": run_stack}[a.op]
+    if a.op in ("layer", "stack"):
+        fn = {"layer": run_layer, "stack": run_stack}[a.op]
+        print(json.dumps(fn(a.iters, a.warmup, a.dtype)), flush=True)
+        return
+    fn = {"attn": run_attn, "attn_any": run_attn_any, "prep": run_prep}[a.op]
     print(json.dumps(fn(a.iters, a.warmup)), flush=True)
 
 

@@ -31,7 +31,7 @@ def _setup(seed, B, S, D, H, F, G, L, dtype, pad=None):
     return x, layers, lm, gm
 
 
-@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("dtype", ["fp16", "bf16", "fp32"])
 @pytest.mark.parametrize("case", [(1, 512, 256, 4, 512, 128, 8, None, 3),
                                   (2, 384, 512, 8, 1024, 64, 0, (0.1, 0.25), 2)],
                          ids=["B1_S512_G8_L3", "B2_S384_G0_pad_L2"])
@@ -45,7 +45,8 @@ def test_stack_equals_layer_after_layer(lf, dtype, case):
     for w in wg:
         cur = lf.encoder_layer(cur, w, lmg, gmg, H, W, G)
     torch.cuda.synchronize()
-    assert torch.equal(y.view(torch.int16), cur.view(torch.int16))
+    bits = torch.int32 if dtype == "fp32" else torch.int16
+    assert torch.equal(y.view(bits), cur.view(bits))
     assert torch.equal(x, xg.cpu()), "the stack must not write its input"
 
 
