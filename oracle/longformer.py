@@ -222,12 +222,19 @@ def layernorm(z, gamma, beta, eps: float = 1e-5):
     return (z - mean) / np.sqrt(var + eps) * _f64(gamma) + _f64(beta)
 
 
-def layer_projections(x, w, H: int, G: int):
-    """Step 1-2: the five projections of x plus the global query on the first G tokens.
+def layer_projections(x, w, H: int, G: int, global_mask=None):
+    """Step 1-2: the five projections of x plus the global query of the global tokens.
 
     Weights are [out, in] row-major: y = x @ W^T + b.  w_proj stacks the
     Q, K, V, global-K, global-V blocks along its rows; inside each block head h
     owns rows 64h .. 64h+63.  Returns q, k, v, kg, vg [B,H,S,d] and qg [B,H,G,d].
+
+    The global query is projected from the global tokens themselves: qg row r of
+    batch row b comes from x[b, p] with p the r-th entry of the global partition
+    (R9, R10: the r-th global position for r < n_b; rows from n_b on, which the
+    attention never reads, come from the partition's remaining entries).  With the
+    global tokens leading this is x[b, r] for every row the attention reads.
+    Without ``global_mask`` the first G tokens are taken.
     """
     xd = _f64(x)
     B, S, D = xd.shape
@@ -237,7 +244,12 @@ def layer_projections(x, w, H: int, G: int):
     for i in range(5):
         blk = proj[:, :, i * D:(i + 1) * D].reshape(B, S, H, d)
         parts.append(np.ascontiguousarray(blk.transpose(0, 2, 1, 3)))
-    qg = xd[:, :G, :] @ _f64(w["w_qg"]).T + _f64(w["b_qg"])      # [B,G,D]
+    if global_mask is None:
+        src = xd[:, :G, :]
+    else:
+        idx, _ = global_partition(global_mask)
+        src = np.stack([xd[b, idx[b, :G]] for b in range(B)]) if G > 0 else xd[:, :0, :]
+    qg = src @ _f64(w["w_qg"]).T + _f64(w["b_qg"])                 # [B,G,D]
     qg = np.ascontiguousarray(qg.reshape(B, G, H, d).transpose(0, 2, 1, 3))
     q, k, v, kg, vg = parts
     return q, k, v, qg, kg, vg
@@ -247,7 +259,7 @@ def encoder_layer(x, w, local_mask, global_mask, H: int, W: int, G: int,
                   scale: float = 0.125, eps: float = 1e-5, rows=None):
     """One Longformer encoder layer, float64, post-LayerNorm order.
 
-      [q|k|v|kg|vg] = x W_proj^T + b_proj;  qg = x[:, :G] W_qg^T + b_qg
+      [q|k|v|kg|vg] = x W_proj^T + b_proj;  qg = x[global positions] W_qg^T + b_qg
       a  = band + global attention, heads concatenated      -> [B,S,D]
       h1 = LN(x + a W_o^T + b_o; ln1)
       y  = LN(h1 + GELU(h1 W_1^T + b_1) W_2^T + b_2; ln2)
@@ -258,7 +270,7 @@ def encoder_layer(x, w, local_mask, global_mask, H: int, W: int, G: int,
     """
     xd = _f64(x)
     B, S, D = xd.shape
-    q, k, v, qg, kg, vg = layer_projections(x, w, H, G)
+    q, k, v, qg, kg, vg = layer_projections(x, w, H, G, global_mask)
     if rows is None:
         a = attention(q, k, v, qg, kg, vg, local_mask, global_mask, W, G, scale)
         a = a.transpose(0, 2, 1, 3).reshape(B, S, D)

@@ -70,7 +70,14 @@ def dense_layer(x, w, local_mask, global_mask, H, W, G, scale=0.125, eps=1e-5):
         return t.reshape(B, t.shape[1], H, d).transpose(1, 2)
 
     q, k, v, kg, vg = (heads(proj[..., i * D:(i + 1) * D]) for i in range(5))
-    qg = heads(F.linear(x[:, :G], ww["w_qg"], ww["b_qg"]))
+    # global queries from the global tokens: row r <- the r-th position whose global-mask
+    # value is 0 (rows past the count are never read by the attention: zeros)
+    gpos = [torch.nonzero(torch.as_tensor(global_mask)[b] == 0).flatten() for b in range(B)]
+    xg = torch.zeros(B, G, D, dtype=x.dtype)
+    for b in range(B):
+        n = min(G, len(gpos[b]))
+        xg[b, :n] = x[b, gpos[b][:n]]
+    qg = heads(F.linear(xg, ww["w_qg"], ww["b_qg"]))
     a = torch.as_tensor(dense_attention(q, k, v, qg, kg, vg, local_mask, global_mask, W, scale))
     a = a.transpose(1, 2).reshape(B, S, D)
     h1 = F.layer_norm(x + F.linear(a, ww["w_o"], ww["b_o"]), (D,), ww["ln1_g"], ww["ln1_b"], eps)

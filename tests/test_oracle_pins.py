@@ -271,6 +271,18 @@ def test_layer_matches_torch_library_composition():
     np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-11)
 
 
+def test_layer_with_scattered_globals_matches_torch_library_composition():
+    # the global queries come from the global tokens wherever they sit (the dense
+    # reference gathers them with torch.nonzero, independently of the oracle's partition)
+    x, w, lm, gm, H, W, G = _tiny_layer(24)
+    gm = torch.full(gm.shape, -10000.0)
+    gm[0, [2, 17, 40]] = 0
+    gm[1, [0, 5]] = 0
+    got = oracle.encoder_layer(x, w, lm, gm, H, W, G)
+    ref = dense_layer(x, w, lm, gm, H, W, G)
+    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-11)
+
+
 def test_layer_rows_subset_matches_full():
     x, w, lm, gm, H, W, G = _tiny_layer(22)
     full = oracle.encoder_layer(x, w, lm, gm, H, W, G)
