@@ -225,6 +225,30 @@ int lf_encoder_forward(int dtype, const lf_layer_weights* w, int n_layers, const
                        float ln_eps, void* y, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * lf_encoder_layer / lf_encoder_forward with the global tokens at any positions (the
+ * Longformer model's own global pattern, which the [FT-LF] page's head-of-sequence
+ * constraint excludes, section "使用前提：四条硬性约束").  Same arguments, shape
+ * rules, dtypes, workspace sizes (lf_encoder_layer_workspace_bytes /
+ * lf_encoder_forward_workspace_bytes) and conventions.  With P_b the flagged
+ * positions of batch row b in ascending order (global_mask == 0.0), n_b = |P_b| <= G:
+ * qg row r of batch row b is projected from x[b, P_b[r]] (rows from n_b on from the
+ * other positions of the global-index partition; the attention never reads them),
+ * and the attention is lf_attn_forward_any_globals'.  With leading global tokens the
+ * result equals lf_encoder_layer / lf_encoder_forward.  The layer call runs the
+ * global-index partition itself first (one more launch); the stack runs it once.
+ */
+int lf_encoder_layer_any_globals(int dtype, const lf_layer_weights* w, const void* x,
+                                 const void* local_mask, const void* global_mask, int B, int S,
+                                 int hidden, int H, int ffn, int W, int G, float attn_scale,
+                                 float ln_eps, void* y, void* workspace, size_t ws_bytes,
+                                 void* stream);
+int lf_encoder_forward_any_globals(int dtype, const lf_layer_weights* w, int n_layers,
+                                   const void* x, const void* local_mask, const void* global_mask,
+                                   int B, int S, int hidden, int H, int ffn, int W, int G,
+                                   float attn_scale, float ln_eps, void* y, void* workspace,
+                                   size_t ws_bytes, void* stream);
+
+/*
  * Measurement hook.  After lf_kernel_timing_start(capacity), each of the next
  * `capacity` lf_attn_forward / lf_attn_forward_pre calls made on this thread
  * records a HIP event pair on its own stream immediately around its main

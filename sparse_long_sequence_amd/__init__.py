@@ -36,7 +36,9 @@ EXPORTED_SYMBOLS = ["lf_init_global_idx", "lf_mask_shift", "lf_attn_forward",
                     "lf_attn_forward_any_globals",
                     "lf_attn_workspace_bytes", "lf_attn_forward_pre", "lf_check_masks",
                     "lf_encoder_layer_workspace_bytes", "lf_encoder_layer",
+                    "lf_encoder_layer_any_globals",
                     "lf_encoder_forward_workspace_bytes", "lf_encoder_forward",
+                    "lf_encoder_forward_any_globals",
                     "lf_kernel_timing_start", "lf_kernel_timing_stop",
                     "lf_status_string", "lf_last_error"]
 
@@ -77,10 +79,12 @@ def load_library():
     lib.lf_encoder_layer_workspace_bytes.restype = S
     lib.lf_encoder_layer.argtypes = [I, ctypes.POINTER(_LayerWeights), P, P, P, I, I, I, I, I,
                                      I, I, ctypes.c_float, ctypes.c_float, P, P, S, P]
+    lib.lf_encoder_layer_any_globals.argtypes = lib.lf_encoder_layer.argtypes
     lib.lf_encoder_forward_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I]
     lib.lf_encoder_forward_workspace_bytes.restype = S
     lib.lf_encoder_forward.argtypes = [I, ctypes.POINTER(_LayerWeights), I, P, P, P, I, I, I, I,
                                        I, I, I, ctypes.c_float, ctypes.c_float, P, P, S, P]
+    lib.lf_encoder_forward_any_globals.argtypes = lib.lf_encoder_forward.argtypes
     lib.lf_kernel_timing_start.argtypes = [I]
     lib.lf_kernel_timing_stop.argtypes = [ctypes.POINTER(ctypes.c_int),
                                           ctypes.POINTER(ctypes.c_double)]
@@ -91,7 +95,8 @@ def load_library():
     for name in ("lf_init_global_idx", "lf_mask_shift", "lf_attn_forward",
                  "lf_attn_forward_any_globals",
                  "lf_attn_forward_pre", "lf_check_masks", "lf_encoder_layer",
-                 "lf_encoder_forward",
+                 "lf_encoder_forward", "lf_encoder_layer_any_globals",
+                 "lf_encoder_forward_any_globals",
                  "lf_kernel_timing_start", "lf_kernel_timing_stop"):
         getattr(lib, name).restype = I
     _lib = lib
@@ -259,9 +264,14 @@ def encoder_layer_workspace_bytes(dtype, B, S, hidden, H, ffn, W, G) -> int:
 
 
 def encoder_layer(x, weights: dict, local_mask, global_mask, H: int, W: int, G: int,
-                  attn_scale: float = 0.125, ln_eps: float = 1e-5, out=None, workspace=None):
-    """[FT-LF computation flow, per-layer steps 1-6] one encoder layer -> y [B,S,hidden]."""
+                  attn_scale: float = 0.125, ln_eps: float = 1e-5, out=None, workspace=None,
+                  any_globals: bool = False):
+    """[FT-LF computation flow, per-layer steps 1-6] one encoder layer -> y [B,S,hidden].
+
+    any_globals: the global tokens may sit at any positions (lf_encoder_layer_any_globals).
+    """
     lib = load_library()
+    entry = lib.lf_encoder_layer_any_globals if any_globals else lib.lf_encoder_layer
     ws = [weights[n] for n in LAYER_WEIGHT_FIELDS]
     dev = _dev(x, local_mask, global_mask, *ws)
     B, S, D = x.shape
@@ -274,10 +284,9 @@ def encoder_layer(x, weights: dict, local_mask, global_mask, H: int, W: int, G: 
         workspace = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
     _dev(out, workspace)
     lw = _LayerWeights(*[t.data_ptr() for t in ws])
-    _check(lib.lf_encoder_layer(dtype_code(x.dtype), ctypes.byref(lw), _ptr(x), _ptr(local_mask),
-                                _ptr(global_mask), B, S, D, H, F, W, G, attn_scale, ln_eps,
-                                _ptr(out), _ptr(workspace),
-                                workspace.numel() * workspace.element_size(), _stream(dev)))
+    _check(entry(dtype_code(x.dtype), ctypes.byref(lw), _ptr(x), _ptr(local_mask),
+                 _ptr(global_mask), B, S, D, H, F, W, G, attn_scale, ln_eps, _ptr(out),
+                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev)))
     return out
 
 
@@ -287,9 +296,14 @@ def encoder_forward_workspace_bytes(dtype, B, S, hidden, H, ffn, W, G) -> int:
 
 
 def encoder_forward(x, layers: list, local_mask, global_mask, H: int, W: int, G: int,
-                    attn_scale: float = 0.125, ln_eps: float = 1e-5, out=None, workspace=None):
-    """[FT-LF computation flow] preprocessing once, then len(layers) encoder layers -> y."""
+                    attn_scale: float = 0.125, ln_eps: float = 1e-5, out=None, workspace=None,
+                    any_globals: bool = False):
+    """[FT-LF computation flow] preprocessing once, then len(layers) encoder layers -> y.
+
+    any_globals: the global tokens may sit at any positions (lf_encoder_forward_any_globals).
+    """
     lib = load_library()
+    entry = lib.lf_encoder_forward_any_globals if any_globals else lib.lf_encoder_forward
     if not layers:
         raise ValueError("at least one layer")
     ws = [[lw[n] for n in LAYER_WEIGHT_FIELDS] for lw in layers]
@@ -304,8 +318,7 @@ def encoder_forward(x, layers: list, local_mask, global_mask, H: int, W: int, G:
         workspace = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
     _dev(out, workspace)
     arr = (_LayerWeights * len(layers))(*[_LayerWeights(*[t.data_ptr() for t in w]) for w in ws])
-    _check(lib.lf_encoder_forward(dtype_code(x.dtype), arr, len(layers), _ptr(x),
-                                  _ptr(local_mask), _ptr(global_mask), B, S, D, H, F, W, G,
-                                  attn_scale, ln_eps, _ptr(out), _ptr(workspace),
-                                  workspace.numel() * workspace.element_size(), _stream(dev)))
+    _check(entry(dtype_code(x.dtype), arr, len(layers), _ptr(x), _ptr(local_mask),
+                 _ptr(global_mask), B, S, D, H, F, W, G, attn_scale, ln_eps, _ptr(out),
+                 _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev)))
     return out

@@ -256,7 +256,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < NLA; ++i) {
     const int m = m0 + RPL * (NLA * wave + i) + lrow;
-    const int arow = g.a_group > 0 ? (m / g.a_group) * g.a_group_stride + m % g.a_group : m;
+    int arow = m;
+    if (g.a_group > 0 && m < g.M) {
+      const int base = (m / g.a_group) * g.a_group_stride;
+      arow = base + (g.a_rows ? g.a_rows[base + m % g.a_group] : m % g.a_group);
+    }
     aoff[i] = m < g.M ? (arow * g.lda + k0 + EPC * lchunk) * (int)sizeof(T) : -1;
   }
 #pragma unroll

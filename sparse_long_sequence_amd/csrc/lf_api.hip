@@ -173,7 +173,8 @@ int validate_layer(int dtype, int B, int S, int hidden, int H, int ffn, int W, i
 // intermediate (which reuses the q..vg area when it fits: they are dead by then).
 struct LayerWs {
   size_t act_bytes, qkv_off, qg_off, attn_off, z_off, h1f_off, h1t_off, u_off, part_off, total;
-  size_t pidx_off, pcnt_off, pbias_off;   // fp32: preprocessed masks (index, count, bias)
+  size_t pidx_off, pcnt_off, pbias_off;   // masks preprocessed inside a layer call (fp32,
+                                          // or global tokens anywhere): index, count, bias
   int split_qg, split_o, split_ffn2;   // split-K factors of the GEMMs with small grids
 };
 
@@ -207,20 +208,21 @@ LayerWs layer_ws(int dtype, int B, int S, int hidden, int H, int ffn, int G) {
   if (L.split_ffn2 > 1) part = std::max(part, (size_t)L.split_ffn2 * M * hidden * 4);
   L.part_off = off;
   off += align256(part);
-  // fp32 attention runs on the vector ALUs from preprocessed masks
-  L.pidx_off = L.pcnt_off = L.pbias_off = 0;
-  if (dtype == LF_F32) {
-    L.pidx_off = off; off += align256(M * 4);
-    L.pcnt_off = off; off += align256((size_t)B * 4);
-    L.pbias_off = off; off += align256(M * es);
-  }
+  // masks preprocessed inside the call: fp32 attention runs on the vector ALUs from
+  // them, and global tokens at any positions need the index
+  L.pidx_off = off; off += align256(M * 4);
+  L.pcnt_off = off; off += align256((size_t)B * 4);
+  L.pbias_off = off; off += align256(M * es);
   L.total = off;
   return L;
 }
 
-// Masks of one layer call: raw (read by the attention kernel) or preprocessed.
+// Masks of one layer call: raw (read by the attention kernel) or preprocessed; any:
+// the global tokens may sit anywhere (the global queries are gathered through the
+// index, the attention runs its globals-anywhere mode).
 struct LayerMasks {
   bool raw = true;
+  bool any = false;
   const void* local_mask = nullptr;
   const void* global_mask = nullptr;
   const int32_t* gidx = nullptr;
@@ -312,11 +314,29 @@ int run_layer(int dtype, const lf_layer_weights* w, const void* x, const LayerMa
     for (int i = 0; i < 5; ++i) g.heads[i] = qkv[i];
     if ((he = lf::launch_gemm(g, st)) != hipSuccess) return hip_fail(he, "projection GEMM");
   }
-  // the global queries: rows 0 .. G-1 of every sequence
+  // masks preprocessed inside this call: fp32 attention reads them, and with global
+  // tokens anywhere the global queries and keys go through the index
+  const int32_t* gidx = mk.gidx;
+  const int32_t* gcnt = mk.gcnt;
+  const void* mbias = mk.bias;
+  if (mk.raw && (dtype == LF_F32 || mk.any)) {
+    int32_t* pidx = (int32_t*)(ws + L.pidx_off);
+    int32_t* pcnt = (int32_t*)(ws + L.pcnt_off);
+    void* pbias = ws + L.pbias_off;
+    if ((he = lf::launch_prep(dtype, mk.global_mask, mk.local_mask, B, S, pidx, pcnt, pbias,
+                              nullptr, 0, st)) != hipSuccess)
+      return hip_fail(he, "layer mask preprocessing");
+    gidx = pidx;
+    gcnt = pcnt;
+    mbias = pbias;
+  }
+  // the global queries: rows 0 .. G-1 of every sequence, or the rows at the global
+  // positions (the first G entries of the index)
   if (G > 0) {
     lf::GemmArgs g = gemm(lf::kEpiHeads, x, D, G, S, w->w_qg, D, w->b_qg, B * G, D, D);
     g.heads[0] = qg;
     g.rows = G;
+    if (mk.any) g.a_rows = gidx;
     if (L.split_qg > 1) {
       // B * G rows: a handful of tiles, so the K range is split and reduced after
       g.epi = lf::kEpiPartial;
@@ -332,26 +352,13 @@ int run_layer(int dtype, const lf_layer_weights* w, const void* x, const LayerMa
   // steps 3-4: attention, heads joined ([B, S, H * 64])
   {
     AttnWs aw = attn_ws(B, H, S, G);
-    const int32_t* gidx = mk.gidx;
-    const int32_t* gcnt = mk.gcnt;
-    const void* mbias = mk.bias;
-    bool raw = mk.raw;
-    if (dtype == LF_F32 && raw) {
-      // the fp32 attention reads preprocessed masks: index, count and shifted mask
-      int32_t* pidx = (int32_t*)(ws + L.pidx_off);
-      int32_t* pcnt = (int32_t*)(ws + L.pcnt_off);
-      void* pbias = ws + L.pbias_off;
-      if ((he = lf::launch_prep(dtype, mk.global_mask, mk.local_mask, B, S, pidx, pcnt, pbias,
-                                nullptr, 0, st)) != hipSuccess)
-        return hip_fail(he, "layer mask preprocessing");
-      gidx = pidx;
-      gcnt = pcnt;
-      mbias = pbias;
-      raw = false;
-    }
     lf::AttnArgs a = make_args(dtype, qkv[0], qkv[1], qkv[2], qg, qkv[3], qkv[4], gidx, gcnt,
                                mbias, B, H, S, W, G, attn, ws, aw, aw.partials_off);
-    a.raw = raw ? 1 : 0;
+    // fp16 / bf16: the MFMA kernel reads the raw masks (leading globals: itself; any
+    // positions: with the index); fp32: the vector-ALU kernel reads the preprocessed
+    // masks (and the global mask for any positions)
+    a.raw = dtype != LF_F32 && (mk.raw || mk.any) ? 1 : 0;
+    a.any_pos = mk.any ? 1 : 0;
     a.local_mask = mk.local_mask;
     a.global_mask = mk.global_mask;
     a.out_ss = D;
@@ -714,32 +721,34 @@ size_t lf_encoder_layer_workspace_bytes(int dtype, int B, int S, int hidden, int
   return layer_ws(dtype, B, S, hidden, H, ffn, G).total;
 }
 
-int lf_encoder_layer(int dtype, const lf_layer_weights* w, const void* x, const void* local_mask,
-                     const void* global_mask, int B, int S, int hidden, int H, int ffn, int W,
-                     int G, float attn_scale, float ln_eps, void* y, void* workspace,
-                     size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// lf_encoder_layer (any_pos = false) and lf_encoder_layer_any_globals (true).
+int encoder_layer_impl(int dtype, const lf_layer_weights* w, const void* x,
+                       const void* local_mask, const void* global_mask, int B, int S, int hidden,
+                       int H, int ffn, int W, int G, float attn_scale, float ln_eps, void* y,
+                       void* workspace, size_t ws_bytes, void* stream, bool any_pos) {
   if (int e = validate_layer(dtype, B, S, hidden, H, ffn, W, G)) return e;
   if (int e = check_layer_call(w, G, x, local_mask, global_mask, y, workspace)) return e;
   const LayerWs L = layer_ws(dtype, B, S, hidden, H, ffn, G);
   if (int e = check_layer_ws(workspace, ws_bytes, L.total, attn_scale, ln_eps)) return e;
   LayerMasks mk;
   mk.raw = true;
+  mk.any = any_pos;
   mk.local_mask = local_mask;
   mk.global_mask = global_mask;
   return run_layer(dtype, w, x, mk, B, S, hidden, H, ffn, W, G, attn_scale, ln_eps, y,
                    (char*)workspace, L, (hipStream_t)stream);
 }
 
-size_t lf_encoder_forward_workspace_bytes(int dtype, int B, int S, int hidden, int H, int ffn,
-                                          int W, int G) {
-  if (validate_layer(dtype, B, S, hidden, H, ffn, W, G) != LF_OK) return 0;
-  return stack_ws(dtype, B, S, hidden, H, ffn, G).total;
-}
 
-int lf_encoder_forward(int dtype, const lf_layer_weights* w, int n_layers, const void* x,
-                       const void* local_mask, const void* global_mask, int B, int S, int hidden,
-                       int H, int ffn, int W, int G, float attn_scale, float ln_eps, void* y,
-                       void* workspace, size_t ws_bytes, void* stream) {
+// lf_encoder_forward (any_pos = false) and lf_encoder_forward_any_globals (true).
+int encoder_forward_impl(int dtype, const lf_layer_weights* w, int n_layers, const void* x,
+                         const void* local_mask, const void* global_mask, int B, int S,
+                         int hidden, int H, int ffn, int W, int G, float attn_scale, float ln_eps,
+                         void* y, void* workspace, size_t ws_bytes, void* stream, bool any_pos) {
   if (int e = validate_layer(dtype, B, S, hidden, H, ffn, W, G)) return e;
   if (n_layers < 1) return fail(LF_ERR_INVALID_ARGUMENT, "n_layers must be >= 1 (got %d)", n_layers);
   if (!w) return fail(LF_ERR_INVALID_ARGUMENT, "null pointer: weights");
@@ -755,6 +764,9 @@ int lf_encoder_forward(int dtype, const lf_layer_weights* w, int n_layers, const
   int32_t* gcnt = (int32_t*)(ws + SW.gcnt_off);
   LayerMasks mk;
   mk.raw = false;
+  mk.any = any_pos;
+  mk.local_mask = local_mask;
+  mk.global_mask = global_mask;
   mk.gidx = gidx;
   mk.gcnt = gcnt;
   mk.bias = ws + SW.bias_off;
@@ -773,6 +785,52 @@ int lf_encoder_forward(int dtype, const lf_layer_weights* w, int n_layers, const
     in = out;
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lf_encoder_forward_workspace_bytes(int dtype, int B, int S, int hidden, int H, int ffn,
+                                          int W, int G) {
+  if (validate_layer(dtype, B, S, hidden, H, ffn, W, G) != LF_OK) return 0;
+  return stack_ws(dtype, B, S, hidden, H, ffn, G).total;
+}
+
+int lf_encoder_layer(int dtype, const lf_layer_weights* w, const void* x, const void* local_mask,
+                     const void* global_mask, int B, int S, int hidden, int H, int ffn, int W,
+                     int G, float attn_scale, float ln_eps, void* y, void* workspace,
+                     size_t ws_bytes, void* stream) {
+  return encoder_layer_impl(dtype, w, x, local_mask, global_mask, B, S, hidden, H, ffn, W, G,
+                            attn_scale, ln_eps, y, workspace, ws_bytes, stream, false);
+}
+
+int lf_encoder_layer_any_globals(int dtype, const lf_layer_weights* w, const void* x,
+                                 const void* local_mask, const void* global_mask, int B, int S,
+                                 int hidden, int H, int ffn, int W, int G, float attn_scale,
+                                 float ln_eps, void* y, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+  return encoder_layer_impl(dtype, w, x, local_mask, global_mask, B, S, hidden, H, ffn, W, G,
+                            attn_scale, ln_eps, y, workspace, ws_bytes, stream, true);
+}
+
+int lf_encoder_forward(int dtype, const lf_layer_weights* w, int n_layers, const void* x,
+                       const void* local_mask, const void* global_mask, int B, int S, int hidden,
+                       int H, int ffn, int W, int G, float attn_scale, float ln_eps, void* y,
+                       void* workspace, size_t ws_bytes, void* stream) {
+  return encoder_forward_impl(dtype, w, n_layers, x, local_mask, global_mask, B, S, hidden, H,
+                              ffn, W, G, attn_scale, ln_eps, y, workspace, ws_bytes, stream,
+                              false);
+}
+
+int lf_encoder_forward_any_globals(int dtype, const lf_layer_weights* w, int n_layers,
+                                   const void* x, const void* local_mask, const void* global_mask,
+                                   int B, int S, int hidden, int H, int ffn, int W, int G,
+                                   float attn_scale, float ln_eps, void* y, void* workspace,
+                                   size_t ws_bytes, void* stream) {
+  return encoder_forward_impl(dtype, w, n_layers, x, local_mask, global_mask, B, S, hidden, H,
+                              ffn, W, G, attn_scale, ln_eps, y, workspace, ws_bytes, stream,
+                              true);
 }
 
 }  // extern "C"

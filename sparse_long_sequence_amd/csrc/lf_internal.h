@@ -58,7 +58,8 @@ hipError_t launch_check_masks(int dtype, const void* local_mask, const void* glo
                               int S, int G, int* flags, hipStream_t st);
 
 // Layer pieces (gemm.hip).  C[m, n] = sum_k A[arow(m), k] * W[n, k] + bias[n], with
-// arow(m) = (m / a_group) * a_group_stride + m % a_group when a_group > 0, else m;
+// arow(m) = (m / a_group) * a_group_stride + m % a_group when a_group > 0 (or that
+// group's a_rows entry, see GemmArgs), else m;
 // then the epilogue.  A, W, bias, outputs and the T residual are in the layer dtype.
 enum GemmEpi {
   kEpiHeads = 0,     // n -> tensor n / D, head (n % D) / 64, dim n % 64; m -> (m / rows,
@@ -87,6 +88,9 @@ struct GemmArgs {
   int splits;            // split-K factor (kEpiPartial; else 1): split s sums k in
                          // [s K / splits, (s + 1) K / splits)
   float* part;           // kEpiPartial output: [splits][M][N] fp32
+  const int32_t* a_rows; // optional with a_group > 0: arow(m) = (m / a_group) *
+                         // a_group_stride + a_rows[(m / a_group) * a_group_stride + m %
+                         // a_group] (the global-query rows gathered through the index)
 };
 
 // N a positive multiple of 128, K of 64, M >= 1.

@@ -123,24 +123,30 @@ def run_prep(iters: int, warmup: int) -> dict:
             "gbs_mask_shift": shift_bytes / (ms_shift * 1e-3) / 1e9}
 
 
-def run_layer(iters: int, warmup: int, dtype: str = "fp16") -> dict:
+def run_layer(iters: int, warmup: int, dtype: str = "fp16", any_globals: bool = False) -> dict:
     wl = workloads.LAYER_FP16
     t = workloads.make_layer_inputs(wl)
     td = workloads.TORCH_DTYPES[dtype]
     x = t["x"].cuda().to(td)
     w = {n: t[n].cuda().to(td) for n in lf.LAYER_WEIGHT_FIELDS}
     lm, gm = t["local_mask"].cuda().to(td), t["global_mask"].cuda().to(td)
+    if any_globals:
+        # the same number of global tokens, evenly spread over each sequence
+        gm.fill_(workloads.NOT_GLOBAL)
+        gm[:, torch.arange(wl.G, device="cuda") * (wl.S // wl.G) + wl.S // (2 * wl.G)] = 0.0
     y = torch.empty_like(x)
     nbytes = lf.encoder_layer_workspace_bytes(x.dtype, wl.B, wl.S, wl.hidden, wl.H, wl.ffn,
                                               wl.W, wl.G)
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
-    ms = _time(lambda: lf.encoder_layer(x, w, lm, gm, wl.H, wl.W, wl.G, out=y, workspace=ws),
-               iters, warmup)
+    ms = _time(lambda: lf.encoder_layer(x, w, lm, gm, wl.H, wl.W, wl.G, out=y, workspace=ws,
+                                        any_globals=any_globals), iters, warmup)
     M, D, F, G, S, W = wl.B * wl.S, wl.hidden, wl.ffn, wl.G, wl.S, wl.W
     gemm = 2.0 * M * D * (5 * D + D + 2 * F) + 2.0 * wl.B * G * D * D
     pairs = G * S + (S - G) * (W + 1 + G) - (W // 2) * (W // 2 + 1)
     attn = 256.0 * pairs * wl.B * wl.H
-    return {"op": "encoder_layer", "workload": wl.name.replace("fp16", dtype), "ms": ms,
+    name = wl.name.replace("fp16", dtype) + ("_globals_spread" if any_globals else "")
+    return {"op": "encoder_layer" + ("_any_globals" if any_globals else ""), "workload": name,
+            "ms": ms,
             "gemm_gflop": gemm / 1e9, "attn_gflop": attn / 1e9,
             "tflops": (gemm + attn) / (ms * 1e-3) / 1e12}
 
@@ -192,10 +198,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--dtype", default="fp16", choices=["fp16", "bf16", "fp32"],
                     help="layer / stack only")
+    ap.add_argument("--any-globals", action="store_true",
+                    help="layer only: globals spread over the sequence, general entry point")
     a = ap.parse_args()
-    if a.op in ("layer", "stack"):
-        fn = {"layer": run_layer, "stack": run_stack}[a.op]
-        print(json.dumps(fn(a.iters, a.warmup, a.dtype)), flush=True)
+    if a.op == "layer":
+        print(json.dumps(run_layer(a.iters, a.warmup, a.dtype, a.any_globals)), flush=True)
+        return
+    if a.op == "stack":
+        print(json.dumps(run_stack(a.iters, a.warmup, a.dtype)), flush=True)
         return
     fn = {"attn": run_attn, "attn_any": run_attn_any, "prep": run_prep}[a.op]
     print(json.dumps(fn(a.iters, a.warmup)), flush=True)

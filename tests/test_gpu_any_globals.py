@@ -158,3 +158,107 @@ def test_scattered_globals_longformer_large_shape_sampled_rows(lf):
     g_rows = np.stack([got[b, h, s].double().numpy() for (b, h, s) in rows])
     err = np.abs(g_rows - ref).max()
     assert err <= TOL["fp16"], f"max abs err {err:.3e} over {len(rows)} rows"
+
+
+# ------------------------------------------------------------------ encoder layer / stack
+# [FT-LF] computation flow, per-layer steps 1-6, with the global tokens anywhere: the
+# global queries come from the global tokens (oracle reading R10, pinned against the
+# torch-composed dense layer), the attention is the globals-anywhere attention.
+# Tolerances as for the leading-globals layer: fp16 3e-3, bf16 2.5e-2 + 2^-8 |ref|,
+# fp32 1e-4 (derivations in tests/test_gpu_layer.py).
+LAYER_TOL = {"fp16": 3e-3, "bf16": 2.5e-2, "fp32": 1e-4}
+
+
+def _layer_inputs(seed, B, S, D, F, G, dtype, positions=None, pad=None):
+    rng = np.random.default_rng(seed)
+    w = workloads.random_layer_params(rng, D, F, dtype, w_std=0.05, b_std=0.02, ln_jitter=0.1)
+    x = torch.from_numpy(rng.standard_normal((B, S, D))).to(workloads.TORCH_DTYPES[dtype])
+    lm, gm = workloads.make_masks(rng, B, S, G, dtype, pad, None, positions)
+    return x, w, lm, gm
+
+
+def _bits(t):
+    return t.view(torch.int32 if t.dtype == torch.float32 else torch.int16)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16", "fp32"])
+def test_layer_any_equals_layer_with_leading_globals(lf, dtype):
+    B, S, D, H, F, W, G = 2, 512, 256, 4, 512, 128, 8
+    x, w, lm, gm = _layer_inputs(61, B, S, D, F, G, dtype, pad=(0.1, 0.2))
+    xg, lmg, gmg = x.cuda(), lm.cuda(), gm.cuda()
+    wg = {n: t.cuda() for n, t in w.items()}
+    a = lf.encoder_layer(xg, wg, lmg, gmg, H, W, G, any_globals=True)
+    b = lf.encoder_layer(xg, wg, lmg, gmg, H, W, G)
+    torch.cuda.synchronize()
+    if dtype == "fp32":
+        # the vector-ALU kernel starts its band chunks at another key: sums reorder
+        assert (a - b).abs().max().item() <= 1e-6
+    else:
+        assert torch.equal(_bits(a), _bits(b))
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16", "fp32"])
+@pytest.mark.parametrize("case", [
+    # B, S, D, H, F, W, G, positions, pad
+    (2, 512, 256, 4, 512, 128, 8, [[3, 100, 101, 255, 256, 400, 500, 511], [0, 64, 300]], None),
+    (1, 384, 512, 8, 1024, 64, 5, [[10, 200, 201, 300, 301]], (0.1, 0.15)),
+], ids=["B2_S512_G8", "B1_S384_G5_pad"])
+def test_layer_any_scattered_globals_vs_oracle(lf, dtype, case):
+    B, S, D, H, F, W, G, positions, pad = case
+    x, w, lm, gm = _layer_inputs(71 + S, B, S, D, F, G, dtype, positions, pad)
+    live = lm.float()
+    for b in range(B):
+        assert all(live[b, p] == 1 for p in positions[b]), "keep the globals unpadded"
+    y = lf.encoder_layer(x.cuda(), {n: t.cuda() for n, t in w.items()}, lm.cuda(), gm.cuda(),
+                         H, W, G, any_globals=True)
+    torch.cuda.synchronize()
+    got = y.cpu()
+    assert torch.isfinite(got.float()).all()
+    ref = oracle.encoder_layer(x, w, lm, gm, H, W, G)
+    err = np.abs(got.double().numpy() - ref)
+    tol = LAYER_TOL[dtype] + (2.0 ** -8 * np.abs(ref) if dtype == "bf16" else 0.0)
+    assert np.all(err <= tol), f"max abs err {err.max():.3e}"
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "fp32"])
+def test_stack_any_equals_layer_any_after_layer_any(lf, dtype):
+    B, S, D, H, F, W, G, L = 1, 512, 256, 4, 512, 128, 6, 3
+    rng = np.random.default_rng(81)
+    layers = [workloads.random_layer_params(rng, D, F, dtype, w_std=0.05, b_std=0.02,
+                                            ln_jitter=0.1) for _ in range(L)]
+    x = torch.from_numpy(rng.standard_normal((B, S, D))).to(workloads.TORCH_DTYPES[dtype])
+    lm, gm = workloads.make_masks(rng, B, S, G, dtype, None, None, [[7, 130, 131, 260, 390, 505]])
+    xg, lmg, gmg = x.cuda(), lm.cuda(), gm.cuda()
+    wg = [{n: t.cuda() for n, t in w.items()} for w in layers]
+    y = lf.encoder_forward(xg, wg, lmg, gmg, H, W, G, any_globals=True)
+    cur = xg
+    for w in wg:
+        cur = lf.encoder_layer(cur, w, lmg, gmg, H, W, G, any_globals=True)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(y), _bits(cur))
+
+
+def test_layer_any_full_size_sampled_rows(lf):
+    # the graded layer shape (B=2 S=4096 hidden 1024, 16 heads, FFN 4096, W=512) with its
+    # 16 global tokens spread over each sequence
+    wl = workloads.LAYER_FP16
+    t = workloads.make_layer_inputs(wl)
+    rng = np.random.default_rng(wl.seed + 11)
+    positions = [sorted(int(p) for p in rng.choice(wl.S, wl.G, replace=False)) for _ in range(wl.B)]
+    gm = torch.full((wl.B, wl.S), workloads.NOT_GLOBAL).to(workloads.TORCH_DTYPES[wl.dtype])
+    for b in range(wl.B):
+        gm[b, positions[b]] = 0.0
+    x, lm = t["x"], t["local_mask"]
+    w = {n: t[n] for n in lf.LAYER_WEIGHT_FIELDS}
+    y = lf.encoder_layer(x.cuda(), {n: v.cuda() for n, v in w.items()}, lm.cuda(), gm.cuda(),
+                         wl.H, wl.W, wl.G, any_globals=True)
+    torch.cuda.synchronize()
+    got = y.cpu()
+    assert torch.isfinite(got.float()).all()
+    rows = sorted({(b, s) for b in range(wl.B) for p in positions[b][:4]
+                   for s in (p - 1, p, p + 1) if 0 <= s < wl.S}
+                  | {(b, int(s)) for b in range(wl.B) for s in rng.integers(0, wl.S, 4)})
+    ref = oracle.encoder_layer(x, w, lm, gm, wl.H, wl.W, wl.G, rows=rows)
+    g_rows = np.stack([got[b, s].double().numpy() for (b, s) in rows])
+    err = np.abs(g_rows - ref).max()
+    assert err <= LAYER_TOL["fp16"], f"max abs err {err:.3e} over {len(rows)} rows"
