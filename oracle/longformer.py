@@ -222,6 +222,18 @@ def layernorm(z, gamma, beta, eps: float = 1e-5):
     return (z - mean) / np.sqrt(var + eps) * _f64(gamma) + _f64(beta)
 
 
+def ffn_block(h, resid, w1, b1, w2, b2, ln_g, ln_b, eps: float = 1e-5):
+    """Step 6: LN(resid + GELU(h W_1^T + b_1) W_2^T + b_2) over rows of [M, D].
+
+    ``h`` is the FFN input and ``resid`` the residual added after the second
+    projection (in the layer both are h1; they are separate here so that a caller
+    can hand in the two copies it keeps, e.g. a rounded GEMM input and a wider
+    residual).  Weights [out, in]: W_1 [F, D], W_2 [D, F].
+    """
+    f = gelu(_f64(h) @ _f64(w1).T + _f64(b1))
+    return layernorm(_f64(resid) + f @ _f64(w2).T + _f64(b2), ln_g, ln_b, eps)
+
+
 def layer_projections(x, w, H: int, G: int, global_mask=None):
     """Step 1-2: the five projections of x plus the global query of the global tokens.
 
@@ -281,8 +293,8 @@ def encoder_layer(x, w, local_mask, global_mask, H: int, W: int, G: int,
         a = a.reshape(len(rows), D)
         xr = np.stack([xd[b, s] for (b, s) in rows]) if len(rows) else np.zeros((0, D))
     h1 = layernorm(xr + a @ _f64(w["w_o"]).T + _f64(w["b_o"]), w["ln1_g"], w["ln1_b"], eps)
-    f = gelu(h1 @ _f64(w["w_ffn1"]).T + _f64(w["b_ffn1"]))
-    return layernorm(h1 + f @ _f64(w["w_ffn2"]).T + _f64(w["b_ffn2"]), w["ln2_g"], w["ln2_b"], eps)
+    return ffn_block(h1, h1, w["w_ffn1"], w["b_ffn1"], w["w_ffn2"], w["b_ffn2"], w["ln2_g"],
+                     w["ln2_b"], eps)
 
 
 # ---------------------------------------------------------------------------

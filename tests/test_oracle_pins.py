@@ -300,3 +300,38 @@ def test_layer_zero_output_projection_is_layernorm_of_input():
     ln = F.layer_norm(x.double(), (x.shape[-1],), eps=1e-5)
     ln2 = F.layer_norm(ln, (x.shape[-1],), eps=1e-5)   # h1 + GELU(0) W2 = h1
     np.testing.assert_allclose(got, ln2.numpy(), rtol=0, atol=1e-12)
+
+
+def test_ffn_block_one_hot_closed_form():
+    # [FT-LF] per-layer step 6.  A one-hot W1 picks input column 1 into F column 2; a
+    # one-hot W2 puts 2x its GELU into output column 3.  A transposed weight, a dropped
+    # or misplaced bias, or adding h instead of the residual changes that value (GELU
+    # and LayerNorm themselves are pinned above).
+    M, D, F = 3, 4, 3
+    h = np.array([[0.3, -1.2, 0.7, 2.0], [1.5, 0.4, -0.6, 0.1], [-0.8, 2.2, 0.0, -1.1]])
+    resid = np.arange(M * D, dtype=np.float64).reshape(M, D) * 0.25 - 1.0
+    w1 = np.zeros((F, D)); w1[2, 1] = 1.0
+    b1 = np.array([0.0, 0.0, 0.5])
+    w2 = np.zeros((D, F)); w2[3, 2] = 2.0
+    b2 = np.array([0.1, 0.2, 0.3, 0.4])
+    gamma, beta = np.array([1.0, 2.0, 0.5, 1.0]), np.array([0.0, 0.1, 0.0, -0.2])
+    got = oracle.ffn_block(h, resid, w1, b1, w2, b2, gamma, beta)
+    for m in range(M):
+        z = resid[m] + b2
+        z[3] += 2.0 * float(oracle.gelu(h[m, 1] + 0.5))
+        mu = z.mean()
+        var = ((z - mu) ** 2).mean()
+        expect = (z - mu) / math.sqrt(var + 1e-5) * gamma + beta
+        np.testing.assert_allclose(got[m], expect, rtol=0, atol=1e-14)
+
+
+def test_ffn_block_is_the_layer_step():
+    # the layer's last step is the FFN block with h = resid = h1: zero attention output
+    # projection makes h1 = LN(x), so the layer is ffn_block(LN(x), LN(x), ...)
+    x, w, lm, gm, H, W, G = _tiny_layer(25, b_std=0.0, ln_jitter=0.0)
+    w["w_o"] = torch.zeros_like(w["w_o"])
+    got = oracle.encoder_layer(x, w, lm, gm, H, W, G)
+    h1 = F.layer_norm(x.double(), (x.shape[-1],), eps=1e-5).numpy()
+    ref = oracle.ffn_block(h1, h1, w["w_ffn1"], w["b_ffn1"], w["w_ffn2"], w["b_ffn2"],
+                           w["ln2_g"], w["ln2_b"])
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
