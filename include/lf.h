@@ -204,6 +204,35 @@ int lf_encoder_layer(int dtype, const lf_layer_weights* w, const void* x,
                      int hidden, int H, int ffn, int W, int G, float attn_scale,
                      float ln_eps, void* y, void* workspace, size_t ws_bytes, void* stream);
 
+/* Workspace bytes lf_ffn_block needs (0 on bad arguments). */
+size_t lf_ffn_block_workspace_bytes(int dtype, int M, int D, int F, int fused);
+
+/*
+ * The FFN block of a layer ([FT-LF] computation flow, per-layer step 6), on its own:
+ *   y = LayerNorm(resid + GELU(h W_1^T + b_1) W_2^T + b_2; ln_g, ln_b)
+ * over M rows (biased variance, eps ln_eps; erf GELU evaluated within 1.5e-7).
+ * h: [M, D] in `dtype` (the GEMM input); resid: [M, D] fp32 (the residual stream);
+ * w1: [F, D], w2: [D, F], b1: [F], b2, ln_g, ln_b: [D], all in `dtype`; y: [M, D] in
+ * `dtype`.  Device pointers; nothing is written but y and the workspace.
+ *   fused = 0: two GEMMs, as lf_encoder_layer runs them (the GELU output goes
+ *     through memory in `dtype`, [M, F]); 2 or 3 launches.
+ *   fused = 1: one kernel forms GELU(h W_1^T + b_1) chunk by chunk on chip (rounded
+ *     to `dtype`, as the two-GEMM path stores it) and multiplies it into W_2 at once,
+ *     the operator fusion of the page "300%加速！PaddleNLP FastFFN如何让大模型训练"飞"起来"
+ *     (section "技术原理深入解析", item 1); then the LayerNorm kernel sums its fp32
+ *     partials (one per F slice when M is small) with b_2 and resid.  fp16 / bf16,
+ *     D in {256, 512, 768, 1024}; else LF_ERR_UNSUPPORTED.  2 launches.
+ * Shape rules: D and F multiples of 128, D a LayerNorm width (256, 512, 768, 1024,
+ * 2048, 4096), M*F*sizeof(dtype) < 2^31.  `workspace`: device, 256-byte aligned,
+ * ws_bytes >= lf_ffn_block_workspace_bytes (no zeroing needed).  The two modes agree
+ * to rounding (their partial sums are grouped differently); each is deterministic.
+ * Enqueued on `stream`, no sync.
+ */
+int lf_ffn_block(int dtype, const void* h, const float* resid, const void* w1, const void* b1,
+                 const void* w2, const void* b2, const void* ln_g, const void* ln_b, int M,
+                 int D, int F, float ln_eps, int fused, void* y, void* workspace,
+                 size_t ws_bytes, void* stream);
+
 /* Workspace bytes lf_encoder_forward needs (0 on bad arguments). */
 size_t lf_encoder_forward_workspace_bytes(int dtype, int B, int S, int hidden, int H, int ffn,
                                           int W, int G);

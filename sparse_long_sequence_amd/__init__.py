@@ -19,6 +19,7 @@ __all__ = ["LFError", "library_path", "load_library", "init_global_idx", "mask_s
            "check_masks",
            "encoder_layer", "encoder_layer_workspace_bytes", "encoder_forward",
            "encoder_forward_workspace_bytes", "LAYER_WEIGHT_FIELDS",
+           "ffn_block", "ffn_block_workspace_bytes",
            "kernel_timing_start", "kernel_timing_stop",
            "EXPORTED_SYMBOLS", "dtype_code"]
 
@@ -39,6 +40,7 @@ EXPORTED_SYMBOLS = ["lf_init_global_idx", "lf_mask_shift", "lf_attn_forward",
                     "lf_encoder_layer_any_globals",
                     "lf_encoder_forward_workspace_bytes", "lf_encoder_forward",
                     "lf_encoder_forward_any_globals",
+                    "lf_ffn_block_workspace_bytes", "lf_ffn_block",
                     "lf_kernel_timing_start", "lf_kernel_timing_stop",
                     "lf_status_string", "lf_last_error"]
 
@@ -85,6 +87,10 @@ def load_library():
     lib.lf_encoder_forward.argtypes = [I, ctypes.POINTER(_LayerWeights), I, P, P, P, I, I, I, I,
                                        I, I, I, ctypes.c_float, ctypes.c_float, P, P, S, P]
     lib.lf_encoder_forward_any_globals.argtypes = lib.lf_encoder_forward.argtypes
+    lib.lf_ffn_block_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.lf_ffn_block_workspace_bytes.restype = S
+    lib.lf_ffn_block.argtypes = [I, P, P, P, P, P, P, P, P, I, I, I, ctypes.c_float, I, P, P, S,
+                                 P]
     lib.lf_kernel_timing_start.argtypes = [I]
     lib.lf_kernel_timing_stop.argtypes = [ctypes.POINTER(ctypes.c_int),
                                           ctypes.POINTER(ctypes.c_double)]
@@ -96,7 +102,7 @@ def load_library():
                  "lf_attn_forward_any_globals",
                  "lf_attn_forward_pre", "lf_check_masks", "lf_encoder_layer",
                  "lf_encoder_forward", "lf_encoder_layer_any_globals",
-                 "lf_encoder_forward_any_globals",
+                 "lf_encoder_forward_any_globals", "lf_ffn_block",
                  "lf_kernel_timing_start", "lf_kernel_timing_stop"):
         getattr(lib, name).restype = I
     _lib = lib
@@ -321,4 +327,35 @@ def encoder_forward(x, layers: list, local_mask, global_mask, H: int, W: int, G:
     _check(entry(dtype_code(x.dtype), arr, len(layers), _ptr(x), _ptr(local_mask),
                  _ptr(global_mask), B, S, D, H, F, W, G, attn_scale, ln_eps, _ptr(out),
                  _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(dev)))
+    return out
+
+
+def ffn_block_workspace_bytes(dtype, M, D, F, fused: bool) -> int:
+    return int(load_library().lf_ffn_block_workspace_bytes(dtype_code(dtype), M, D, F,
+                                                           1 if fused else 0))
+
+
+def ffn_block(h, resid, w1, b1, w2, b2, ln_g, ln_b, fused: bool, ln_eps: float = 1e-5,
+              out=None, workspace=None):
+    """[FT-LF computation flow, per-layer step 6] y = LN(resid + GELU(h W1^T + b1) W2^T + b2).
+
+    h [M, D] (fp16 / bf16 / fp32), resid [M, D] fp32; fused selects the one-kernel
+    path (the intermediate stays on chip) over the two GEMMs the layer runs.
+    """
+    lib = load_library()
+    dev = _dev(h, resid, w1, b1, w2, b2, ln_g, ln_b)
+    if resid.dtype != torch.float32:
+        raise TypeError("resid must be float32 (the residual stream)")
+    M, D = h.shape
+    F = w1.shape[0]
+    if out is None:
+        out = torch.empty_like(h)
+    nbytes = ffn_block_workspace_bytes(h.dtype, M, D, F, fused)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    _dev(out, workspace)
+    _check(lib.lf_ffn_block(dtype_code(h.dtype), _ptr(h), _ptr(resid), _ptr(w1), _ptr(b1),
+                            _ptr(w2), _ptr(b2), _ptr(ln_g), _ptr(ln_b), M, D, F, ln_eps,
+                            1 if fused else 0, _ptr(out), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(dev)))
     return out

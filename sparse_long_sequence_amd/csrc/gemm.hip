@@ -567,6 +567,145 @@ hipError_t layernorm_t(const float* z, const void* gamma, const void* beta, floa
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ fused FFN
+// [FastFFN] = the page "300%加速！PaddleNLP FastFFN如何让大模型训练"飞"起来", sections
+// "FastFFN技术架构" and "技术原理深入解析" (item 1, operator fusion): the FFN's two
+// projections and its activation run as one kernel, and the activation is not
+// written to global memory.  Here a workgroup owns 32 rows and one slice of the F
+// columns.  For each chunk of 32 F columns it forms H = GELU(X W1_c^T + b1_c) in LDS
+// (rounded to T, as the two-GEMM path stores its intermediate) and adds H W2_c^T to a
+// 32 x D fp32 accumulator held in registers; the accumulator leaves as one fp32
+// partial per F slice, and the row LayerNorm kernel sums the partials with b2 and the
+// residual ([FT-LF] per-layer step 6).
+//
+// Wave w: in the first product it takes K range [w D/8, (w + 1) D/8) of the chunk's
+// 32 x 32 tile of H^T (the eight K partials are summed in LDS, in a fixed order); in
+// the second it owns output columns [w D/8, (w + 1) D/8).  Every W1 and W2 fragment is
+// used once per workgroup, so they are read straight into registers: W1 one chunk
+// ahead, W2 at the start of its chunk (its latency hides behind the first product).
+constexpr int kFfnRows = 32;    // rows per workgroup
+constexpr int kFfnChunk = 32;   // F columns per chunk
+
+template <typename T, int NT>   // NT = D / 256: 32-column output tiles per wave
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void ffn_fused_kernel(
+    const T* __restrict__ x, const T* __restrict__ w1, const T* __restrict__ b1,
+    const T* __restrict__ w2, int M, int F, int f_per_split, float* __restrict__ part) {
+  constexpr int D = 256 * NT;
+  constexpr int KW = D / 8;             // K columns per wave (first product) = output columns per wave
+  constexpr int NK1 = KW / 16;          // MFMAs per wave in the first product
+  constexpr int XP = D + 8;             // LDS row pitch of X (elements): rows 16 bytes apart in banks
+  constexpr int HP = kFfnChunk + 8;     // LDS row pitch of H
+  typedef typename Elem<T>::vec8 v8;
+  __shared__ __attribute__((aligned(16))) T xs[kFfnRows * XP];
+  __shared__ __attribute__((aligned(16))) float hp[8][16][64];   // K partials of the H^T tile
+  __shared__ __attribute__((aligned(16))) T hs[kFfnRows * HP];
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31, g = lane >> 5;
+  const int r0 = blockIdx.x * kFfnRows;
+  const int f_lo = blockIdx.y * f_per_split;
+  const int nchunk = f_per_split / kFfnChunk;
+
+  // the workgroup's rows of X into LDS (rows past M read zeros)
+  const int rows = min(M - r0, kFfnRows);
+  const rsrc_t rx = make_rsrc(x + (size_t)r0 * D, (uint32_t)(rows * D * (int)sizeof(T)));
+  for (int i = threadIdx.x; i < kFfnRows * D / 8; i += 512) {
+    const int r = i / (D / 8), c8 = i % (D / 8);
+    *(u32x4*)&xs[r * XP + 8 * c8] =
+        __builtin_amdgcn_raw_buffer_load_b128(rx, (r * D + 8 * c8) * (int)sizeof(T), 0, 0);
+  }
+  const rsrc_t rw1 = make_rsrc(w1, (uint32_t)((size_t)F * D * sizeof(T)));
+  const rsrc_t rw2 = make_rsrc(w2, (uint32_t)((size_t)D * F * sizeof(T)));
+  // first product: A operand = W1 row f0 + n, k = w KW + 16 i + 8 g (8 elements)
+  auto load_w1 = [&](v8 (&f)[NK1], int f0) {
+#pragma unroll
+    for (int i = 0; i < NK1; ++i)
+      f[i] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(
+                                        rw1, ((f0 + n) * D + wave * KW + 16 * i + 8 * g) * (int)sizeof(T), 0, 0));
+  };
+  // second product: A operand = W2 row (output column) w KW + 32 j + n, k = f0 + 16 kk + 8 g
+  auto load_w2 = [&](v8 (&f)[NT][2], int f0) {
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+        f[j][kk] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rw2, ((wave * KW + 32 * j + n) * F + f0 + 16 * kk + 8 * g) * (int)sizeof(T), 0, 0));
+  };
+
+  f32x16 acc[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) acc[j] = f32x16{};
+  v8 w1f[NK1];
+  load_w1(w1f, f_lo);
+  __syncthreads();   // X in LDS
+  for (int c = 0; c < nchunk; ++c) {
+    const int f0 = f_lo + c * kFfnChunk;
+    v8 w2f[NT][2], w1n[NK1];
+    load_w2(w2f, f0);
+    if (c + 1 < nchunk) load_w1(w1n, f0 + kFfnChunk);
+    // H^T tile (F columns f0 .., rows of X) over this wave's K range
+    f32x16 h = f32x16{};
+#pragma unroll
+    for (int i = 0; i < NK1; ++i)
+      h = mfma32(w1f[i], *(const v8*)&xs[n * XP + wave * KW + 16 * i + 8 * g], h);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) hp[wave][v][lane] = h[v];
+    __syncthreads();
+    // the eight K partials in order, + b1, GELU, rounded to T; element (v, l) of the
+    // tile is H[row l % 32][f0 + 8 (v / 4) + 4 (l / 32) + v % 4]
+    for (int e = threadIdx.x; e < 16 * 64; e += 512) {
+      const int v = e >> 6, l = e & 63;
+      float sum = hp[0][v][l];
+#pragma unroll
+      for (int w = 1; w < 8; ++w) sum += hp[w][v][l];
+      const int fi = 8 * (v >> 2) + 4 * (l >> 5) + (v & 3);
+      sum += Elem<T>::to_f(b1[f0 + fi]);
+      hs[(l & 31) * HP + fi] = Elem<T>::from_f(gelu(sum));
+    }
+    __syncthreads();
+    // second product: output columns w KW + 32 j .., rows of X
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const v8 hf = *(const v8*)&hs[n * HP + 16 * kk + 8 * g];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) acc[j] = mfma32(w2f[j][kk], hf, acc[j]);
+    }
+    if (c + 1 < nchunk) {
+#pragma unroll
+      for (int i = 0; i < NK1; ++i) w1f[i] = w1n[i];
+    }
+  }
+  // partial of this F slice: lane holds row r0 + n, columns w KW + 32 j + 8 jj + 4 g .. + 3
+  if (r0 + n < M) {
+    float* dst = part + ((size_t)blockIdx.y * M + r0 + n) * D + wave * KW + 4 * g;
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        *(f32x4*)(dst + 32 * j + 8 * jj) =
+            f32x4{acc[j][4 * jj], acc[j][4 * jj + 1], acc[j][4 * jj + 2], acc[j][4 * jj + 3]};
+  }
+}
+
+template <typename T>
+hipError_t ffn_fused_t(const void* x, const void* w1, const void* b1, const void* w2, int M, int D,
+                       int F, int splits, float* part, hipStream_t st) {
+  const dim3 grid((M + kFfnRows - 1) / kFfnRows, splits);
+  const int fps = F / splits;
+#define LF_FFN(NT)                                                                          \
+  case NT:                                                                                  \
+    ffn_fused_kernel<T, NT><<<grid, 512, 0, st>>>((const T*)x, (const T*)w1, (const T*)b1, \
+                                                  (const T*)w2, M, F, fps, part);           \
+    break;
+  switch (D / 256) {
+    LF_FFN(1) LF_FFN(2) LF_FFN(3) LF_FFN(4)
+    default: return hipErrorInvalidValue;
+  }
+#undef LF_FFN
+  return hipGetLastError();
+}
+
 }  // namespace
 
 bool gemm_shape_ok(int M, int N, int K) {
@@ -578,6 +717,29 @@ int gemm_splits(int M, int N, int K) {
   int s = 1;
   while (s < 16 && tiles * s < 256 && (K / (2 * s)) % 64 == 0 && K / (2 * s) >= 64) s *= 2;
   return s;
+}
+
+int ffn_fused_splits(int M, int F) {
+  // enough workgroups to fill the chip: split F while there are fewer than 256 row
+  // blocks, keeping whole chunks per slice
+  const int blocks = (M + kFfnRows - 1) / kFfnRows;
+  int s = 1;
+  while (s < 16 && blocks * s < 256 && (F / (2 * s)) % kFfnChunk == 0) s *= 2;
+  return s;
+}
+
+bool ffn_fused_ok(int dtype, int D, int F, int splits) {
+  return (dtype == 1 || dtype == 2) && D % 256 == 0 && D >= 256 && D <= 1024 && splits >= 1 &&
+         F % (kFfnChunk * splits) == 0 && (int64_t)F * D * 2 <= INT_MAX;
+}
+
+hipError_t launch_ffn_fused(int dtype, const void* x, const void* w1, const void* b1,
+                            const void* w2, int M, int D, int F, int splits, float* part,
+                            hipStream_t st) {
+  if (!ffn_fused_ok(dtype, D, F, splits) || M <= 0) return hipErrorInvalidValue;
+  if ((int64_t)M * D * 2 > INT_MAX) return hipErrorInvalidValue;
+  return dtype == 1 ? ffn_fused_t<f16>(x, w1, b1, w2, M, D, F, splits, part, st)
+                    : ffn_fused_t<bf16>(x, w1, b1, w2, M, D, F, splits, part, st);
 }
 
 hipError_t launch_layernorm_parts(int dtype, const float* part, int splits, const void* bias,

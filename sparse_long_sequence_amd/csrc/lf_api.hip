@@ -279,6 +279,45 @@ hipError_t run_attention(const lf::AttnArgs& a, hipStream_t st) {
   return a.dtype == LF_F32 ? lf::launch_attention_fp32(a, st) : lf::launch_attention(a, st);
 }
 
+// [FT-LF] per-layer step 6 on two GEMMs: u = GELU(h W1^T + b1) (layer dtype, [M, F]),
+// then u W2^T + b2 + resid (fp32) and LayerNorm; FFN2 split over K into `part` when
+// its grid is small (the sum happens inside the LayerNorm kernel), else written to
+// the fp32 buffer z.  Used by the layer and by lf_ffn_block.
+hipError_t run_ffn_two_gemm(int dtype, const void* h, const float* resid, const void* w1,
+                            const void* b1, const void* w2, const void* b2, const void* ln_g,
+                            const void* ln_b, float ln_eps, int M, int D, int F, int split_ffn2,
+                            void* u, float* z, float* part, void* y, hipStream_t st) {
+  lf::GemmArgs g;
+  memset(&g, 0, sizeof g);
+  g.dtype = dtype; g.epi = lf::kEpiGelu;
+  g.a = h; g.lda = D;
+  g.w = w1; g.ldw = D; g.bias = b1;
+  g.M = M; g.N = F; g.K = D;
+  g.splits = 1;
+  g.out = u; g.ldo = F;
+  hipError_t he = lf::launch_gemm(g, st);
+  if (he != hipSuccess) return he;
+  lf::GemmArgs g2;
+  memset(&g2, 0, sizeof g2);
+  g2.dtype = dtype;
+  g2.a = u; g2.lda = F;
+  g2.w = w2; g2.ldw = F; g2.bias = b2;
+  g2.M = M; g2.N = D; g2.K = F;
+  g2.splits = 1;
+  if (split_ffn2 > 1) {
+    g2.epi = lf::kEpiPartial;
+    g2.splits = split_ffn2;
+    g2.part = part;
+    if ((he = lf::launch_gemm(g2, st)) != hipSuccess) return he;
+    return lf::launch_layernorm_parts(dtype, part, split_ffn2, b2, resid, true, ln_g, ln_b,
+                                      ln_eps, M, D, nullptr, y, st);
+  }
+  g2.epi = lf::kEpiResidF32;
+  g2.out = z; g2.ldo = D; g2.resid = resid; g2.ldr = D;
+  if ((he = lf::launch_gemm(g2, st)) != hipSuccess) return he;
+  return lf::launch_layernorm(dtype, z, ln_g, ln_b, ln_eps, M, D, nullptr, y, st);
+}
+
 // One encoder layer ([FT-LF] per-layer steps 1-6) as 8 launches on `st`; arguments
 // already validated.
 int run_layer(int dtype, const lf_layer_weights* w, const void* x, const LayerMasks& mk, int B,
@@ -386,29 +425,10 @@ int run_layer(int dtype, const lf_layer_weights* w, const void* x, const LayerMa
       return hip_fail(he, "LayerNorm 1");
   }
   // step 6: FFN with GELU, second GEMM + bias + residual (fp32), LayerNorm
-  {
-    lf::GemmArgs g = gemm(lf::kEpiGelu, h1t, D, 0, 0, w->w_ffn1, D, w->b_ffn1, M, ffn, D);
-    g.out = u; g.ldo = ffn;
-    if ((he = lf::launch_gemm(g, st)) != hipSuccess) return hip_fail(he, "FFN GEMM 1");
-    if (L.split_ffn2 > 1) {
-      lf::GemmArgs g2 = gemm(lf::kEpiPartial, u, ffn, 0, 0, w->w_ffn2, ffn, w->b_ffn2, M, D, ffn);
-      g2.splits = L.split_ffn2;
-      g2.part = part;
-      if ((he = lf::launch_gemm(g2, st)) != hipSuccess) return hip_fail(he, "FFN GEMM 2");
-      if ((he = lf::launch_layernorm_parts(dtype, part, L.split_ffn2, w->b_ffn2, h1f, true,
-                                           w->ln2_g, w->ln2_b, ln_eps, M, D, nullptr, y, st)) !=
-          hipSuccess)
-        return hip_fail(he, "LayerNorm 2");
-    } else {
-      lf::GemmArgs g2 =
-          gemm(lf::kEpiResidF32, u, ffn, 0, 0, w->w_ffn2, ffn, w->b_ffn2, M, D, ffn);
-      g2.out = z; g2.ldo = D; g2.resid = h1f; g2.ldr = D;
-      if ((he = lf::launch_gemm(g2, st)) != hipSuccess) return hip_fail(he, "FFN GEMM 2");
-      if ((he = lf::launch_layernorm(dtype, z, w->ln2_g, w->ln2_b, ln_eps, M, D, nullptr, y,
-                                     st)) != hipSuccess)
-        return hip_fail(he, "LayerNorm 2");
-    }
-  }
+  if ((he = run_ffn_two_gemm(dtype, h1t, h1f, w->w_ffn1, w->b_ffn1, w->w_ffn2, w->b_ffn2,
+                             w->ln2_g, w->ln2_b, ln_eps, M, D, ffn, L.split_ffn2, u, z, part, y,
+                             st)) != hipSuccess)
+    return hip_fail(he, "FFN");
   return LF_OK;
 }
 
@@ -831,6 +851,100 @@ int lf_encoder_forward_any_globals(int dtype, const lf_layer_weights* w, int n_l
   return encoder_forward_impl(dtype, w, n_layers, x, local_mask, global_mask, B, S, hidden, H,
                               ffn, W, G, attn_scale, ln_eps, y, workspace, ws_bytes, stream,
                               true);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- FFN block
+namespace {
+
+// FFN-block workspace.  Two GEMMs: the intermediate u [M, F] in the layer dtype, then
+// the fp32 split-K partials of FFN2 or the fp32 pre-LayerNorm rows.  Fused: the fp32
+// partials of the F slices only.
+struct FfnWs {
+  int split;   // FFN2 split-K factor (two GEMMs) or F slices (fused)
+  size_t u_off, z_off, total;
+};
+
+FfnWs ffn_ws(int dtype, int M, int D, int F, bool fused) {
+  FfnWs W;
+  const size_t es = dtype_size(dtype);
+  if (fused) {
+    W.split = lf::ffn_fused_splits(M, F);
+    W.u_off = 0;
+    W.z_off = 0;
+    W.total = align256((size_t)W.split * M * D * 4);
+    return W;
+  }
+  W.split = lf::gemm_splits(M, D, F);
+  W.u_off = 0;
+  W.z_off = align256((size_t)M * F * es);
+  W.total = W.z_off + align256((size_t)std::max(W.split, 1) * M * D * 4);
+  return W;
+}
+
+int validate_ffn(int dtype, int M, int D, int F, int fused) {
+  if (!known_dtype(dtype)) return fail(LF_ERR_INVALID_ARGUMENT, "unknown dtype %d", dtype);
+  if (M <= 0) return fail(LF_ERR_INVALID_ARGUMENT, "M must be > 0 (got %d)", M);
+  if (D % 128 != 0 || F % 128 != 0 || F < 128)
+    return fail(LF_ERR_INVALID_ARGUMENT, "D and F must be multiples of 128 (got %d, %d)", D, F);
+  if (!lf::layernorm_width_ok(D))
+    return fail(LF_ERR_INVALID_ARGUMENT, "D must be 256, 512, 768, 1024, 2048 or 4096");
+  if ((int64_t)M * F * (int64_t)dtype_size(dtype) > INT_MAX ||
+      (int64_t)M * D * 4 * 16 > (int64_t)1 << 40)
+    return fail(LF_ERR_INVALID_ARGUMENT, "M*F too large for 32-bit GEMM offsets");
+  if (fused) {
+    if (dtype == LF_F32) return fail(LF_ERR_UNSUPPORTED, "fused FFN: fp16 / bf16 only");
+    if (D > 1024 || D % 256 != 0)
+      return fail(LF_ERR_UNSUPPORTED, "fused FFN: D must be 256, 512, 768 or 1024 (got %d)", D);
+    const int sp = lf::ffn_fused_splits(M, F);
+    if (!lf::ffn_fused_ok(dtype, D, F, sp))
+      return fail(LF_ERR_UNSUPPORTED, "fused FFN: F must be a multiple of %d (got %d)", 32 * sp, F);
+  }
+  return LF_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lf_ffn_block_workspace_bytes(int dtype, int M, int D, int F, int fused) {
+  if (validate_ffn(dtype, M, D, F, fused) != LF_OK) return 0;
+  return ffn_ws(dtype, M, D, F, fused != 0).total;
+}
+
+int lf_ffn_block(int dtype, const void* h, const float* resid, const void* w1, const void* b1,
+                 const void* w2, const void* b2, const void* ln_g, const void* ln_b, int M,
+                 int D, int F, float ln_eps, int fused, void* y, void* workspace,
+                 size_t ws_bytes, void* stream) {
+  if (int e = validate_ffn(dtype, M, D, F, fused)) return e;
+  if (int e = null_check("h,resid,w1,b1,w2,b2,ln_g,ln_b,y,workspace",
+                         {h, resid, w1, b1, w2, b2, ln_g, ln_b, y, workspace}))
+    return e;
+  const FfnWs W = ffn_ws(dtype, M, D, F, fused != 0);
+  if (ws_bytes < W.total)
+    return fail(LF_ERR_INVALID_ARGUMENT, "workspace too small: %zu < %zu bytes", ws_bytes, W.total);
+  if ((uintptr_t)workspace % 256 != 0)
+    return fail(LF_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if (!(ln_eps > 0.0f)) return fail(LF_ERR_INVALID_ARGUMENT, "ln_eps must be > 0");
+  hipStream_t st = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  hipError_t he;
+  if (fused) {
+    float* part = (float*)ws;
+    if ((he = lf::launch_ffn_fused(dtype, h, w1, b1, w2, M, D, F, W.split, part, st)) !=
+        hipSuccess)
+      return hip_fail(he, "fused FFN");
+    if ((he = lf::launch_layernorm_parts(dtype, part, W.split, b2, resid, true, ln_g, ln_b,
+                                         ln_eps, M, D, nullptr, y, st)) != hipSuccess)
+      return hip_fail(he, "fused FFN LayerNorm");
+    return LF_OK;
+  }
+  float* zp = (float*)(ws + W.z_off);
+  if ((he = run_ffn_two_gemm(dtype, h, resid, w1, b1, w2, b2, ln_g, ln_b, ln_eps, M, D, F,
+                             W.split, ws + W.u_off, zp, zp, y, st)) != hipSuccess)
+    return hip_fail(he, "FFN");
+  return LF_OK;
 }
 
 }  // extern "C"

@@ -111,6 +111,14 @@ hipError_t launch_layernorm_parts(int dtype, const float* part, int splits, cons
 // Head-split epilogue of a split-K GEMM: heads[0] gets sum_s part[s] + bias in the
 // kEpiHeads layout (row m -> (m / rows, m % rows), column n -> head n / 64, dim n % 64).
 hipError_t launch_splitk_heads(const GemmArgs& g, hipStream_t st);
+// Fused FFN (gemm.hip): part[s][m][:] = GELU(x[m] W1^T + b1) W2^T over F slice s of
+// `splits` equal slices, the GELU output kept on chip; fp16 / bf16, D in
+// {256, 512, 768, 1024}, F a multiple of 32 * splits.
+int ffn_fused_splits(int M, int F);
+bool ffn_fused_ok(int dtype, int D, int F, int splits);
+hipError_t launch_ffn_fused(int dtype, const void* x, const void* w1, const void* b1,
+                            const void* w2, int M, int D, int F, int splits, float* part,
+                            hipStream_t st);
 hipError_t launch_layernorm(int dtype, const float* z, const void* gamma, const void* beta,
                             float eps, int M, int N, float* out_f32, void* out_t,
                             hipStream_t st);

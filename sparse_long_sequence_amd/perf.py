@@ -5,6 +5,7 @@
     python sparse_long_sequence_amd/perf.py prep  [--iters N]   # index compaction + mask shift
     python sparse_long_sequence_amd/perf.py layer [--iters N] [--dtype fp16|bf16|fp32]
     python sparse_long_sequence_amd/perf.py stack [--iters N] [--dtype fp16|bf16|fp32]
+    python sparse_long_sequence_amd/perf.py ffn   [--iters N]   # FFN block, both paths
                                            # one encoder layer / the 24-layer encoder, B1 S1024
 
 Prints one JSON line per run: time per call (HIP events on the current stream around
@@ -190,10 +191,39 @@ def run_stack(iters: int, warmup: int, dtype: str = "fp16", n_layers: int = 24) 
             "tflops": n_layers * (gemm + attn) / (ms * 1e-3) / 1e12}
 
 
+def run_ffn(iters: int, warmup: int, dtype: str = "fp16") -> dict:
+    # the FFN block (step 6) at the layer's rows (B 2 x S 4096) and at the stack
+    # benchmark's (B 1 x S 1024), D 1024, F 4096, both paths
+    D, F = 1024, 4096
+    td = workloads.TORCH_DTYPES[dtype]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(20260007)
+    w1 = (torch.randn(F, D, generator=gen, device="cuda") * 0.02).to(td)
+    w2 = (torch.randn(D, F, generator=gen, device="cuda") * 0.02).to(td)
+    b1 = torch.zeros(F, dtype=td, device="cuda")
+    b2, beta = (torch.zeros(D, dtype=td, device="cuda") for _ in range(2))
+    gamma = torch.ones(D, dtype=td, device="cuda")
+    res = {"op": "ffn_block", "dtype": dtype, "D": D, "F": F}
+    for M in (8192, 1024):
+        resid = torch.randn(M, D, generator=gen, device="cuda")
+        h = resid.to(td)
+        y = torch.empty_like(h)
+        flop = 4.0 * M * D * F
+        for fused in (False, True):
+            nb = lf.ffn_block_workspace_bytes(td, M, D, F, fused)
+            ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+            ms = _time(lambda: lf.ffn_block(h, resid, w1, b1, w2, b2, gamma, beta, fused,
+                                            out=y, workspace=ws), iters, warmup)
+            key = f"M{M}_{'fused' if fused else 'two_gemm'}"
+            res[key + "_ms"] = ms
+            res[key + "_tflops"] = flop / (ms * 1e-3) / 1e12
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("op", choices=["attn", "attn_any", "prep", "layer", "stack"])
+    ap.add_argument("op", choices=["attn", "attn_any", "prep", "layer", "stack", "ffn"])
     ap.add_argument("--iters", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--dtype", default="fp16", choices=["fp16", "bf16", "fp32"],
@@ -206,6 +236,9 @@ def main():
         return
     if a.op == "stack":
         print(json.dumps(run_stack(a.iters, a.warmup, a.dtype)), flush=True)
+        return
+    if a.op == "ffn":
+        print(json.dumps(run_ffn(a.iters, a.warmup, a.dtype)), flush=True)
         return
     fn = {"attn": run_attn, "attn_any": run_attn_any, "prep": run_prep}[a.op]
     print(json.dumps(fn(a.iters, a.warmup)), flush=True)

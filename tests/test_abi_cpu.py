@@ -121,3 +121,27 @@ def test_python_binding_refuses_cpu_tensors(lib):
     x = torch.zeros(1, 8, dtype=torch.float16)
     with pytest.raises(ValueError, match="GPU"):
         lf.mask_shift(x)
+
+
+def test_ffn_block_validates_on_host(lib):
+    # [FT-LF] per-layer step 6 on its own; the fused mode covers fp16 / bf16 and
+    # D <= 1024 only (no GPU work happens for any of these calls)
+    p = _fake()
+    assert lib.lf_ffn_block_workspace_bytes(1, 8192, 1024, 4096, 0) > 0
+    assert lib.lf_ffn_block_workspace_bytes(1, 8192, 1024, 4096, 1) > 0
+    assert lib.lf_ffn_block_workspace_bytes(1, 8192, 1000, 4096, 0) == 0    # D % 128
+    assert lib.lf_ffn_block_workspace_bytes(0, 8192, 1024, 4096, 1) == 0    # fp32 fused
+    assert lib.lf_ffn_block_workspace_bytes(1, 64, 2048, 4096, 1) == 0      # D > 1024 fused
+    assert lib.lf_ffn_block_workspace_bytes(1, 64, 2048, 4096, 0) > 0
+    args = lambda dt, M, D, F, fused, ws: (dt, p, p, p, p, p, p, p, p, M, D, F,
+                                           ctypes.c_float(1e-5), fused, p, p, ws, None)
+    need = lib.lf_ffn_block_workspace_bytes(1, 64, 256, 512, 1)
+    assert lib.lf_ffn_block(*args(0, 64, 256, 512, 1, 1 << 30)) == UNSUPPORTED
+    assert "fp16 / bf16" in lib.lf_last_error().decode()
+    assert lib.lf_ffn_block(*args(1, 64, 256, 500, 1, 1 << 30)) == INVALID
+    assert lib.lf_ffn_block(*args(1, 0, 256, 512, 0, 1 << 30)) == INVALID
+    assert lib.lf_ffn_block(*args(1, 64, 256, 512, 1, need - 1)) == INVALID
+    assert "too small" in lib.lf_last_error().decode()
+    st = lib.lf_ffn_block(1, p, None, p, p, p, p, p, p, 64, 256, 512, ctypes.c_float(1e-5), 0,
+                          p, p, 1 << 30, None)
+    assert st == INVALID and "resid" in lib.lf_last_error().decode()
