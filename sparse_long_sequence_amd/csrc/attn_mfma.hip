@@ -44,11 +44,13 @@
 //
 // Global rows (r < n_b) attend to all live keys through kg / vg.  The first
 // n_split tiles of each (b, h) also take one key split of those rows (split_len
-// keys, 32 per wave per round) before their band work (its first loads go out with
-// the band's): the eight wave states are merged in LDS and one partial
-// (m, l, o[64]) per row is published with write-through stores (coherent across
-// XCDs without cache maintenance).  Then the workgroup takes an atomic ticket; after
-// its band work, the one whose ticket completed the (b, h) reads all partials with
+// keys, 32 per wave per round) after their band work.  The split's first-round
+// entries continue the ring's entry list, so the band loop's last steps stage them
+// like band entries: their kg / vg loads stream while the loop computes instead of
+// joining the launch's first burst of loads.  The eight wave states are merged in
+// LDS and one partial (m, l, o[64]) per row is published with write-through stores
+// (coherent across XCDs without cache maintenance).  Then the workgroup takes an
+// atomic ticket; the one whose ticket completed the (b, h) reads all partials with
 // coherent loads, writes the global rows and resets the ticket.
 #include "lf_device.h"
 #include "lf_internal.h"
@@ -68,6 +70,7 @@ constexpr int kVld = 72;             // LDS row pitch of V^T (elements): 144 B, 
 constexpr int kRing = 8;             // LDS entry slots (the global-row split merges 8 wave states)
 constexpr int kAhead = 5;            // entry t + kAhead is written at step t
 constexpr int kDepth = 2;            // register sets of loads in flight
+constexpr int kSplitEnt = kWaves * kBlk / kEnt;   // entries per round of the global-row split
 constexpr int kStPitch = 67;         // floats per row of a wave state in LDS: m, l, o[64], pad
 constexpr int kMaxSplit = 32;        // at most this many key splits per (b, h)
 constexpr int kSc1 = 16;             // cache-policy bit of coherent (write-through / bypass) access
@@ -368,6 +371,7 @@ __device__ inline void load_q(typename Frag<T>::v8 qf[4], const T* __restrict__ 
 template <typename T>
 struct Ctx {
   int b, h, bh, tile, S, W, G, nb, ngp, r0, kbase, n_list;
+  bool split;                // this tile runs a key split of the global rows
   int sp_lo, sp_hi;          // key range of the split
   const T *kh, *vh;          // k, v of this head
   const T *kgh, *vgh;        // kg, vg of this head (split tiles; else k, v)
@@ -378,27 +382,35 @@ struct Ctx {
 
 // List entry i: global-key entry i (positions 64i.., live below n_b; under the
 // head-of-sequence precondition the global positions are 0 .. n_b - 1) or band
-// entry i - ngp (keys kbase + 64(i - ngp).., live in [n_b, S)).  Entries past the
-// list read out of range (no memory traffic) and are never used.
-template <typename T>
+// entry i - ngp (keys kbase + 64(i - ngp).., live in [n_b, S)).  Past the list come
+// the kSplitEnt entries of the first round of the global-row split (kg / vg keys
+// sp_lo + 64(i - n_list).., split tiles only): the band loop's last steps stage them
+// like any other entry, so the split after the band work finds them loaded.  Entries
+// past those read out of range (no memory traffic) and are never used.
+// PAST: entries past the list may be the split's (else they read nothing, and the
+// code is shorter).
+template <typename T, bool PAST>
 __device__ inline int entry_base(const Ctx<T>& c, int i) {
   const int ngp = c.ngp, n_list = c.n_list, S = c.S;
   const int base = i < ngp ? kEnt * i : c.kbase + kEnt * (i - ngp);
-  return i < n_list ? base : S;
+  const int e = i - n_list;
+  const int past = PAST && c.split && e < kSplitEnt ? c.sp_lo + kEnt * e : S;
+  return i < n_list ? base : past;
 }
 
 // ANY (globals-anywhere mode): global-key entries gather the global positions
 // through the index, band entries also load the global-mask values of their keys.
-template <typename T, bool ANY>
+template <typename T, bool ANY, bool PAST>
 __device__ inline void load_entry(Stage<T>& s, const Ctx<T>& c, int i) {
   const uint32_t bytes = (uint32_t)c.S * 128u;
-  const rsrc_t rk = make_rsrc(c.kh, bytes), rv = make_rsrc(c.vh, bytes);
+  const bool past = PAST && i >= c.n_list;
+  const rsrc_t rk = make_rsrc(past ? c.kgh : c.kh, bytes), rv = make_rsrc(past ? c.vgh : c.vh, bytes);
   const rsrc_t rm = make_rsrc(c.mask, (uint32_t)c.S * 2u);
   if (ANY && i < c.ngp) {
     stage_gather<T>(s, rk, rv, rm, c.gi, kEnt * i, c.G, c.S);
     return;
   }
-  const int base = entry_base(c, i);
+  const int base = entry_base<T, PAST>(c, i);
   stage_load<T>(s, rk, rv, rm, base);
   if (ANY) {
     const int t = threadIdx.x;
@@ -407,31 +419,31 @@ __device__ inline void load_entry(Stage<T>& s, const Ctx<T>& c, int i) {
   }
 }
 
-template <typename T, bool RAW, bool ANY>
+template <typename T, bool RAW, bool ANY, bool PAST>
 __device__ inline void store_entry(Slot<T>& sl, const Stage<T>& s, const Ctx<T>& c, int i) {
   const int nb = c.nb, S = c.S;
-  const bool glob = i < c.ngp;
+  const bool glob = i < c.ngp, past = PAST && i >= c.n_list;
   // band keys: from n_b on when the globals lead, anywhere but the global positions
-  // otherwise
-  stage_store<T, RAW>(sl, s, entry_base(c, i), glob || ANY ? 0 : nb, glob ? nb : S, ANY && !glob);
+  // otherwise; split keys: the split's range
+  const int lo = past ? c.sp_lo : glob || ANY ? 0 : nb;
+  const int hi = past ? c.sp_hi : glob ? nb : S;
+  stage_store<T, RAW>(sl, s, entry_base<T, PAST>(c, i), lo, hi, ANY && !glob && !past);
 }
 
 // ------------------------------------------------------------------ global rows
-// Key split `sp` of the global rows of (b, h), run before the band work: rounds of
+// Key split `sp` of the global rows of (b, h), run after the band work: rounds of
 // kWaves blocks (one per wave, four entries), then the wave states are merged in
 // LDS and one partial (m, l, o[64]) per row is published with write-through
-// stores.  The first round of the first query block arrives already loaded
-// (`first` and `qf0`, issued with the workgroup's first loads; `qf0` holds rows
-// 0 .. 31 below G, and rows from n_b on are computed but not published).
-constexpr int kSplitEnt = kWaves * kBlk / kEnt;   // entries per round
+// stores.  The first round of the first query block is already in the ring (slots
+// slot0 .. slot0 + 3, staged by the band loop) and its queries in `qf0` (rows
+// 0 .. 31 below G; rows from n_b on are computed but not published).
 
 // ANY is unused in the body: it gives each kernel instantiation a copy of its own
 // (with one copy shared by the two raw-mask kernels, the compiler allocated the
 // leading-globals kernel's prologue registers worse: 14 spilled VGPRs instead of 1).
 template <typename T, bool RAW, bool ANY>
 __device__ void global_split_run(const AttnArgs& a, const Ctx<T>& c, int sp, Slot<T>* ring,
-                                 const Stage<T> first[kSplitEnt],
-                                 const typename Frag<T>::v8 qf0[4]) {
+                                 int slot0, const typename Frag<T>::v8 qf0[4]) {
   typedef typename Frag<T>::v8 v8;
   const int t = threadIdx.x;
   const int lane = lane_id();
@@ -458,11 +470,8 @@ __device__ void global_split_run(const AttnArgs& a, const Ctx<T>& c, int sp, Slo
     float m_run = kNegBig, l_run = 0.0f;
     for (int u = 0; u < n_rounds; ++u) {
       const int base = k_lo + kBlk * kWaves * u;
-      if (qb == 0 && u == 0) {
-#pragma unroll
-        for (int e = 0; e < kSplitEnt; ++e)
-          stage_store<T, RAW>(ring[e], first[e], base + kEnt * e, k_lo, k_hi);
-      } else {
+      const bool staged = qb == 0 && u == 0;
+      if (!staged) {
         Stage<T> st[kSplitEnt];
 #pragma unroll
         for (int e = 0; e < kSplitEnt; ++e)
@@ -475,7 +484,8 @@ __device__ void global_split_run(const AttnArgs& a, const Ctx<T>& c, int sp, Slo
           stage_store<T, RAW>(ring[e], st[e], base + kEnt * e, k_lo, k_hi);
       }
       __syncthreads();
-      block_step<T>(ring[wave >> 1], wave & 1, qf, o, m_run, l_run, c2);
+      block_step<T>(ring[staged ? (slot0 + (wave >> 1)) % kRing : wave >> 1], wave & 1, qf, o,
+                    m_run, l_run, c2);
     }
     __syncthreads();   // every wave is done with its block before the states go in
     float* stp = (float*)&ring[wave];
@@ -620,10 +630,10 @@ __device__ inline int xcd_remap(int i, int n) {
 // Number of global tokens of batch row b: raw mode counts the zeros (+0 or -0: the
 // bits other than the sign are clear, in fp16 and bf16 alike) among the first G
 // global-mask values (the tokens are leading, so this is their number); pre mode and
-// the globals-anywhere mode read global_count.  Every wave counts for itself with ballots, so no barrier is needed:
-// count_load issues the first load (the first 64 mask values, one per lane) before
-// any other load of the workgroup, and since vector loads complete in order, the wait
-// in count_globals does not wait for the staging loads issued after it.
+// the globals-anywhere mode read global_count.  Wave 0 counts with ballots (count_load
+// issues the first load of the workgroup, the first 64 mask values, one per lane; since
+// vector loads complete in order, the wait in count_globals does not wait for the
+// staging loads issued after it).
 template <typename T, bool RAW, bool ANY>
 __device__ inline int count_load(const AttnArgs& a, int b) {
   if (!RAW || ANY) return a.gcnt[b];
@@ -651,7 +661,7 @@ __device__ inline int count_globals(const AttnArgs& a, int b, int first) {
 // entry t + kAhead and the loads of entry t + kAhead + kDepth, then (BAR: second
 // step of a pair) the barrier.  Entries t .. t + 3 are read during the step and
 // t + 5 is written.
-template <typename T, bool RAW, bool ANY, bool BAR>
+template <typename T, bool RAW, bool ANY, bool PAST, bool BAR>
 __device__ __forceinline__ void band_step(const Ctx<T>& c, Slot<T>* ring, int tt, int rg, int sb,
                                           float c2, Stage<T>& set,
                                           const typename Frag<T>::v8 qf[4], f32x16 o[2],
@@ -684,9 +694,9 @@ __device__ __forceinline__ void band_step(const Ctx<T>& c, Slot<T>* ring, int tt
   pv_frag<T>(vf0, p0, o);
   pv_frag<T>(vf1, p1, o);
   const int e = tt + kAhead;
-  store_entry<T, RAW, ANY>(ring[e % kRing], set, c, e);
+  store_entry<T, RAW, ANY, PAST>(ring[e % kRing], set, c, e);
   __builtin_amdgcn_sched_barrier(0);
-  load_entry<T, ANY>(set, c, e + kDepth);
+  load_entry<T, ANY, PAST>(set, c, e + kDepth);
   if (BAR) __syncthreads();
 }
 
@@ -728,6 +738,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   c.gm = ANY ? (const unsigned short*)a.global_mask + (size_t)c.b * c.S : nullptr;
   const float c2 = a.scale * kLog2e;
   const bool split = a.G > 0 && c.tile < a.n_split;
+  c.split = split;
   c.sp_lo = split ? c.tile * a.split_len : 0;
   c.sp_hi = split ? min(c.S, c.sp_lo + a.split_len) : 0;
   c.kh = (const T*)a.k + head;
@@ -736,24 +747,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   c.vgh = split ? (const T*)a.vg + head : c.vh;
 
   // every load the prologue needs is issued before anything waits: the global-mask
-  // values, the first round of the global-row split (split tiles), the first ring
-  // entries, Q, the register sets
-  const int gfirst = count_load<T, RAW, ANY>(a, c.b);
+  // values, the first ring entries, Q, the register sets.  Only wave 0 counts the
+  // global tokens: it alone writes the per-key terms, the one use of the count before
+  // the band loop, and hands the count to the other waves at the prologue barrier.
+  // (Every workgroup of a batch row reads the same mask values: one request per
+  // workgroup instead of one per wave keeps that cache line from becoming a hot spot.)
+  const bool counter = wave == 0;
+  const int gfirst = counter ? count_load<T, RAW, ANY>(a, c.b) : 0;
   __builtin_amdgcn_sched_barrier(0);
-  Stage<T> spl[kSplitEnt];
-  v8 qg0[4];
-  if (split) {
-    const int r = n;   // split rows 0 .. 31 below G (rows from n_b on are not published)
-    load_q<T>(qg0, (const T*)a.qg + ((size_t)c.bh * a.G + (r < a.G ? r : 0)) * 64, r < a.G);
-#pragma unroll
-    for (int e = 0; e < kSplitEnt; ++e)
-      stage_load<T>(spl[e], make_rsrc(c.kgh, (uint32_t)c.S * 128u),
-                    make_rsrc(c.vgh, (uint32_t)c.S * 128u), make_rsrc(c.mask, (uint32_t)c.S * 2u),
-                    c.sp_lo + kEnt * e);
-  }
   Stage<T> pro[kAhead];
 #pragma unroll
-  for (int i = 0; i < kAhead; ++i) load_entry<T, ANY>(pro[i], c, i);
+  for (int i = 0; i < kAhead; ++i) load_entry<T, ANY, true>(pro[i], c, i);
   // Q before the register sets: in the loop its wait count then never holds back
   // the sets in flight
   v8 qf[4];
@@ -761,34 +765,48 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   load_q<T>(qf, (const T*)a.q + head + (size_t)(srow < c.S ? srow : 0) * 64, srow < c.S);
   __builtin_amdgcn_sched_barrier(0);
   static_assert(kDepth == 2, "steps run in pairs: entry e uses set e % 2");
+  // after the band loop the ring holds list entries up to n_list + 1 and the register
+  // sets n_list + 2, n_list + 3: the split's first round
+  static_assert(kAhead - 3 + kDepth == kSplitEnt, "split round = two staged + two in registers");
   Stage<T> st[kDepth];
 #pragma unroll
   for (int u = 0; u < kDepth; ++u) {
-    load_entry<T, ANY>(st[(kAhead + u) % kDepth], c, kAhead + u);
+    load_entry<T, ANY, true>(st[(kAhead + u) % kDepth], c, kAhead + u);
     __builtin_amdgcn_sched_barrier(0);
   }
-  c.nb = count_globals<T, RAW, ANY>(a, c.b, gfirst);
-  // the split of the global rows first (its loads were issued first), then the
-  // ticket, whose value is looked at after the band work
-  int ticket = 0;
-  if (split && c.nb > 0) {
-    global_split_run<T, RAW, ANY>(a, c, c.tile, ring, spl, qg0);
-    ticket = take_ticket<T>(a, c);
-  }
+  c.nb = counter ? count_globals<T, RAW, ANY>(a, c.b, gfirst) : 0;
 
 #pragma unroll
-  for (int i = 0; i < kAhead; ++i) store_entry<T, RAW, ANY>(ring[i], pro[i], c, i);
+  for (int i = 0; i < kAhead; ++i) store_entry<T, RAW, ANY, true>(ring[i], pro[i], c, i);
+  __shared__ int s_nb;
+  if (counter && lane == 0) s_nb = c.nb;
   __syncthreads();
+  c.nb = __builtin_amdgcn_readfirstlane(s_nb);
 
   f32x16 o[2] = {f32x16{}, f32x16{}};
   float m_run = kNegBig, l_run = 0.0f;
   constexpr int s0i = kAhead % kDepth, s1i = (kAhead + 1) % kDepth;
+  // steps t < n_steps - 4 stage and load entries of the list only; on split tiles
+  // the last four reach past it (the split's entries)
+  const int n_plain = split ? n_steps - 4 : n_steps;
   int t0 = 0;
-  for (; t0 + 2 <= n_steps; t0 += 2) {
-    band_step<T, RAW, ANY, false>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
-    band_step<T, RAW, ANY, true>(c, ring, t0 + 1, rg, sb, c2, st[s1i], qf, o, m_run, l_run);
+  for (; t0 + 2 <= n_plain; t0 += 2) {
+    band_step<T, RAW, ANY, false, false>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
+    band_step<T, RAW, ANY, false, true>(c, ring, t0 + 1, rg, sb, c2, st[s1i], qf, o, m_run, l_run);
   }
-  if (t0 < n_steps) band_step<T, RAW, ANY, false>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
+  for (; t0 + 2 <= n_steps; t0 += 2) {
+    band_step<T, RAW, ANY, true, false>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
+    band_step<T, RAW, ANY, true, true>(c, ring, t0 + 1, rg, sb, c2, st[s1i], qf, o, m_run, l_run);
+  }
+  if (t0 < n_steps)
+    band_step<T, RAW, ANY, true, false>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
+
+  // the split's queries (rows 0 .. 31 below G; rows from n_b on are computed but not
+  // published) go out before the epilogue, which hides their latency
+  const bool do_split = split && c.nb > 0;
+  v8 qg0[4];
+  if (do_split)
+    load_q<T>(qg0, (const T*)a.qg + ((size_t)c.bh * a.G + (n < a.G ? n : 0)) * 64, n < a.G);
 
   // epilogue: normalise and store the local rows
   {
@@ -813,7 +831,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   }
 
-  if (split && c.nb > 0) {
+  // the global-row split: list entries n_list, n_list + 1 are in the ring,
+  // n_list + 2, n_list + 3 in the register sets; then the ticket
+  if (do_split) {
+    __syncthreads();   // band reads done
+    // entry e sits in set e % 2: a uniform branch keeps the set index static (an
+    // index known only at run time would put the sets in scratch memory)
+    const int e2 = c.n_list + 2;
+    if ((e2 & 1) == 0) {
+      store_entry<T, RAW, ANY, true>(ring[e2 % kRing], st[0], c, e2);
+      store_entry<T, RAW, ANY, true>(ring[(e2 + 1) % kRing], st[1], c, e2 + 1);
+    } else {
+      store_entry<T, RAW, ANY, true>(ring[e2 % kRing], st[1], c, e2);
+      store_entry<T, RAW, ANY, true>(ring[(e2 + 1) % kRing], st[0], c, e2 + 1);
+    }
+    __syncthreads();
+    global_split_run<T, RAW, ANY>(a, c, c.tile, ring, c.n_list % kRing, qg0);
+    const int ticket = take_ticket<T>(a, c);
     __shared__ int s_last;
     if (threadIdx.x == 0) s_last = ticket == a.n_split - 1;
     __syncthreads();
