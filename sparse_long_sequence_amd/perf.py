@@ -1,6 +1,6 @@
 """Timing driver for the library's entry points on seeded synthetic inputs.
 
-    python sparse_long_sequence_amd/perf.py attn  [--iters N]   # longformer-large attention
+    python sparse_long_sequence_amd/perf.py attn  [--iters N] [--shape large|padded|long]
     python sparse_long_sequence_amd/perf.py attn_any [--iters N]  # same, 8 globals spread out
     python sparse_long_sequence_amd/perf.py prep  [--iters N]   # index compaction + mask shift
     python sparse_long_sequence_amd/perf.py layer [--iters N] [--dtype fp16|bf16|fp32]
@@ -52,18 +52,23 @@ def _time(fn, iters: int, warmup: int) -> float:
     return e0.elapsed_time(e1) / iters
 
 
-def run_attn(iters: int, warmup: int) -> dict:
-    wl = workloads.LARGE_FP16
-    g = {n: t.cuda() for n, t in workloads.make_attention_inputs(wl).items()}
+ATTN_SHAPES = {"large": workloads.LARGE_FP16, "padded": workloads.PADDED_FP16,
+               "long": workloads.LONG_BF16}
+
+
+def run_attn(iters: int, warmup: int, shape: str = "large") -> dict:
+    wl = ATTN_SHAPES[shape]
+    inp = workloads.make_attention_inputs(wl)
+    g = {n: t.cuda() for n, t in inp.items()}
     out = torch.empty_like(g["q"])
     ms = _time(lambda: lf.attn_forward(g["q"], g["k"], g["v"], g["qg"], g["kg"], g["vg"],
                                        g["local_mask"], g["global_mask"], wl.W, wl.G, out=out),
                iters, warmup)
-    S, W, G = wl.S, wl.W, wl.G
-    pairs = G * S + (S - G) * (W + 1 + G) - (W // 2) * (W // 2 + 1)
-    flops = 256.0 * pairs * wl.B * wl.H
+    # allowed pairs counted from the masks (padding excluded)
+    flops = 256.0 * oracle_free_pairs(inp["local_mask"], inp["global_mask"], wl.W) * wl.H
+    nbytes = sum(t.numel() * t.element_size() for t in inp.values()) + g["q"].numel() * g["q"].element_size()
     return {"op": "attn_forward", "workload": wl.name, "ms": ms,
-            "tflops": flops / (ms * 1e-3) / 1e12}
+            "tflops": flops / (ms * 1e-3) / 1e12, "alg_gbs": nbytes / (ms * 1e-3) / 1e9}
 
 
 def run_attn_any(iters: int, warmup: int) -> dict:
@@ -228,6 +233,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--dtype", default="fp16", choices=["fp16", "bf16", "fp32"],
                     help="layer / stack only")
+    ap.add_argument("--shape", default="large", choices=sorted(ATTN_SHAPES),
+                    help="attn only: longformer-large, padded (B4 H12 G32) or long (bf16 S16384)")
     ap.add_argument("--any-globals", action="store_true",
                     help="layer only: globals spread over the sequence, general entry point")
     a = ap.parse_args()
@@ -240,7 +247,10 @@ def main():
     if a.op == "ffn":
         print(json.dumps(run_ffn(a.iters, a.warmup, a.dtype)), flush=True)
         return
-    fn = {"attn": run_attn, "attn_any": run_attn_any, "prep": run_prep}[a.op]
+    if a.op == "attn":
+        print(json.dumps(run_attn(a.iters, a.warmup, a.shape)), flush=True)
+        return
+    fn = {"attn_any": run_attn_any, "prep": run_prep}[a.op]
     print(json.dumps(fn(a.iters, a.warmup)), flush=True)
 
 
