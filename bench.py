@@ -124,9 +124,10 @@ def main():
                          "(fp32 in, fp32 out) so HBM counters can be scaled by a known size")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
-              f"(--gpus {args.gpus} requested). Attention heads shard across GPUs with no "
-              f"communication; see the design notes.", file=sys.stderr)
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path "
+              f"(--gpus {args.gpus} requested). The (batch, head) pairs of the attention are "
+              f"independent, so they would shard across GPUs with no communication.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
