@@ -419,8 +419,14 @@ hipError_t gemm_t(const GemmArgs& g, hipStream_t st) {
   constexpr int KS = 128 / (int)sizeof(T);   // 128-byte tile rows: 64 fp16 / bf16, 32 fp32
   if (big_tiles >= 256 && g.splits == 1)
     return gemm_launch<T, 256, 256, 8, 128, 64, KS, 2>(g, big_tiles, st);
-  return gemm_launch<T, 128, 128, 4, 64, 64, KS, 2>(
-      g, ((g.M + 127) / 128) * (g.N / 128) * g.splits, st);
+  // small grids (at most 320 tiles of 128 x 128, e.g. 1024 rows): 64 x 128 tiles,
+  // three workgroups per CU (24 KB of LDS per stage), so more K steps are in flight
+  // per CU than with 128 x 128 tiles at two per CU
+  const int t128 = ((g.M + 127) / 128) * (g.N / 128) * g.splits;
+  if (t128 <= 320)
+    return gemm_launch<T, 64, 128, 4, 32, 64, KS, 2>(g, ((g.M + 63) / 64) * (g.N / 128) * g.splits,
+                                                     st);
+  return gemm_launch<T, 128, 128, 4, 64, 64, KS, 2>(g, t128, st);
 }
 
 // LayerNorm of z = sum_s part[s] + bias + resid, one row per wave (the split-K
