@@ -26,3 +26,22 @@ def test_multi_gpu_request_exits_with_message(capsys):
     finally:
         sys.argv = argv
     assert "one GPU" in capsys.readouterr().err
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_perf_pair_counter_matches_oracle_with_padding_and_scattered_globals(seed):
+    # perf.py counts the allowed pairs straight from the masks (its throughput figures
+    # for the padded workload and for global tokens anywhere); the oracle enumerates
+    # the definition
+    import torch
+    from sparse_long_sequence_amd import perf
+    rng = np.random.default_rng(seed)
+    B, S, W, G = 2, 512, 64, 12
+    lm = np.ones((B, S))
+    lm[0, 400:] = 0.0
+    lm[1, 300:] = 0.0
+    gm = np.full((B, S), -10000.0)
+    for b, live in enumerate((400, 300)):
+        gm[b, rng.choice(live, G - 2 * b, replace=False)] = 0.0
+    got = perf.oracle_free_pairs(torch.tensor(lm), torch.tensor(gm), W)
+    assert got == oracle.allowed_pairs(lm, gm, W, G)

@@ -262,3 +262,22 @@ def test_layer_any_full_size_sampled_rows(lf):
     g_rows = np.stack([got[b, s].double().numpy() for (b, s) in rows])
     err = np.abs(g_rows - ref).max()
     assert err <= LAYER_TOL["fp16"], f"max abs err {err:.3e} over {len(rows)} rows"
+
+
+def test_stack_any_last_layer_matches_oracle(lf):
+    # two layers with the global tokens scattered: the stack's output against the
+    # oracle layer applied to the GPU's first-layer output
+    B, S, D, H, F, W, G = 1, 512, 256, 4, 512, 128, 6
+    rng = np.random.default_rng(91)
+    layers = [workloads.random_layer_params(rng, D, F, "fp16", w_std=0.05, b_std=0.02,
+                                            ln_jitter=0.1) for _ in range(2)]
+    x = torch.from_numpy(rng.standard_normal((B, S, D))).to(torch.float16)
+    lm, gm = workloads.make_masks(rng, B, S, G, "fp16", None, None, [[3, 130, 131, 260, 390, 500]])
+    xg, lmg, gmg = x.cuda(), lm.cuda(), gm.cuda()
+    wg = [{n: t.cuda() for n, t in w.items()} for w in layers]
+    y1 = lf.encoder_layer(xg, wg[0], lmg, gmg, H, W, G, any_globals=True)
+    y = lf.encoder_forward(xg, wg, lmg, gmg, H, W, G, any_globals=True)
+    torch.cuda.synchronize()
+    ref = oracle.encoder_layer(y1.cpu(), layers[1], lm, gm, H, W, G)
+    err = np.abs(y.cpu().double().numpy() - ref).max()
+    assert err <= LAYER_TOL["fp16"], f"max abs err {err:.3e}"

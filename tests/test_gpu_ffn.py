@@ -89,14 +89,15 @@ def test_fused_and_two_gemm_agree_and_fused_is_deterministic(lf, dtype):
 
 
 @pytest.mark.parametrize("fused", [False, True], ids=["two_gemm", "fused"])
-@pytest.mark.parametrize("M", [8192, 1024], ids=["layer_rows", "stack_rows"])
-def test_ffn_block_full_size_sampled_rows(lf, M, fused):
-    # the graded layer's FFN (M = 2 x 4096 rows, D 1024, F 4096) and the stack
-    # benchmark's (M = 1024: the fused path splits F over workgroups), fp16
+@pytest.mark.parametrize("M,dtype", [(8192, "fp16"), (1024, "fp16"), (8192, "bf16")],
+                         ids=["layer_rows_fp16", "stack_rows_fp16", "layer_rows_bf16"])
+def test_ffn_block_full_size_sampled_rows(lf, M, dtype, fused):
+    # the layer's FFN (M = 2 x 4096 rows, D 1024, F 4096) and the stack benchmark's
+    # (M = 1024: the fused path splits F over workgroups)
     D, F = 1024, 4096
-    h, resid, w = _inputs(603 + M, M, D, F, "fp16")
+    h, resid, w = _inputs(603 + M, M, D, F, dtype)
     got = _run(lf, h, resid, w, fused)
     assert torch.isfinite(got.float()).all()
     rng = np.random.default_rng(7)
     rows = sorted(set([0, 31, 32, M - 1]) | set(int(r) for r in rng.integers(0, M, 28)))
-    _check(got[rows], _oracle(h, resid, w, rows), "fp16")
+    _check(got[rows], _oracle(h, resid, w, rows), dtype)

@@ -136,3 +136,24 @@ def test_layer_rejects_bad_arguments(lf):
     with pytest.raises(TypeError, match="unsupported dtype"):
         lf.encoder_layer(x64, {n: t.double() for n, t in wg.items()}, lmg.double(), gmg.double(),
                          H, W, G)
+
+
+def test_layer_full_size_bf16_sampled_rows(lf):
+    # the full-size shape in bf16 (the fp16 inputs rounded to bf16; the oracle reads
+    # the rounded values)
+    wl = workloads.LAYER_FP16
+    t = workloads.make_layer_inputs(wl)
+    cast = {n: v.to(torch.bfloat16) for n, v in t.items()}
+    x, lm, gm = cast["x"], cast["local_mask"], cast["global_mask"]
+    w = {n: cast[n] for n in lf.LAYER_WEIGHT_FIELDS}
+    y = _run(lf, x, w, lm, gm, wl.H, wl.W, wl.G)
+    assert torch.isfinite(y.float()).all()
+    got = y.cpu()
+    rng = np.random.default_rng(wl.seed + 11)
+    rows = sorted({(b, s) for b in range(wl.B)
+                   for s in [0, wl.G - 1, wl.G, wl.W // 2, wl.S // 2, wl.S - 1]
+                   + [int(v) for v in rng.integers(0, wl.S, 8)]})
+    ref = oracle.encoder_layer(x, w, lm, gm, wl.H, wl.W, wl.G, rows=rows)
+    g_rows = np.stack([got[b, s].double().numpy() for (b, s) in rows])
+    err = np.abs(g_rows - ref)
+    assert np.all(err <= TOL["bf16"] + 2.0 ** -8 * np.abs(ref)), f"max abs err {err.max():.3e}"
