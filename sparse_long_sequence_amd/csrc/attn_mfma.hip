@@ -540,9 +540,8 @@ __device__ void global_split_run(const AttnArgs& a, const Ctx<T>& c, int sp, Slo
 }
 
 // Ticket of a split workgroup, taken right after its partial is published: every
-// wave waits for its write-through stores, then one atomic increment.  The old
-// value (thread 0) is first looked at after the band work, so the atomic's round
-// trip is hidden behind it.
+// wave waits for its write-through stores, then one atomic increment (its old value,
+// in thread 0, tells whether this workgroup's partial completed the (b, h)).
 template <typename T>
 __device__ inline int take_ticket(const AttnArgs& a, const Ctx<T>& c) {
   __builtin_amdgcn_s_waitcnt(0);
