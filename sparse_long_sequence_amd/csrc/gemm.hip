@@ -196,8 +196,12 @@ __device__ inline void wait_vm() {
 // are separate LDS objects and the K loop is unrolled by ST steps, so every access
 // names its stage statically: the compiler then knows that the loads in flight write
 // other stages and does not make the current step's LDS reads wait for them.
+//
+// Second problem (head-split epilogue only): workgroups from tiles0 on take the tiles
+// of g1, a GEMM of the same K and dtype, so a small GEMM rides in the idle slots of a
+// large one's last round of tiles instead of a launch of its own.
 template <typename T, int EPI, int TM, int TN, int WAVES, int WM, int WN, int KS, int ST>
-__global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs g) {
+__global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs g0, GemmArgs g1, int tiles0) {
   typedef typename GemmFrag<T>::type v8;
   constexpr int MI = WM / 32, NI = WN / 32;    // MFMA tiles per wave
   constexpr int WAVES_M = TM / WM;
@@ -229,13 +233,22 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs g) {
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int n = lane & 31, gq = lane >> 5;
+  const bool second = EPI == kEpiHeads && (int)blockIdx.x >= tiles0;
+  // the problem's arguments read in place from the kernel-argument segment (g0 at
+  // offset 0, g1 right after it): a select between the two parameters themselves
+  // would copy both to scratch memory
+  typedef __attribute__((address_space(4))) const GemmArgs* kargs_t;
+  const GemmArgs& g =
+      *(const GemmArgs*)((kargs_t)__builtin_amdgcn_kernarg_segment_ptr() + (second ? 1 : 0));
+  const int bx = second ? (int)blockIdx.x - tiles0 : (int)blockIdx.x;
 
   // tile order: per XCD a contiguous run of tile indices; within it, groups of
   // kGroupM m-tiles sweep all n-tiles, so a W tile is reused while it is in L2; with
-  // split-K the grid holds every tile once per split
+  // split-K the grid holds every tile once per split (the second problem's few tiles
+  // keep their order)
   const int tiles_n = g.N / TN;
   const int tiles_m = (g.M + TM - 1) / TM;
-  const int flat = xcd_chunk(blockIdx.x, tiles_m * tiles_n * g.splits);
+  const int flat = second ? bx : xcd_chunk(bx, tiles_m * tiles_n * g.splits);
   const int split = __builtin_amdgcn_readfirstlane(flat / (tiles_m * tiles_n));
   const int bid = flat - split * (tiles_m * tiles_n);
   const int per_group = kGroupM * tiles_n;
@@ -390,22 +403,25 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict_
 }
 
 template <typename T, int TM, int TN, int WAVES, int WM, int WN, int KS, int ST>
-hipError_t gemm_launch(const GemmArgs& g, int tiles, hipStream_t st) {
+hipError_t gemm_launch(const GemmArgs& g, int tiles, hipStream_t st, const GemmArgs* g2 = nullptr) {
+  // the second problem's tiles follow the first's (see gemm_kernel)
+  const int tiles2 = g2 ? ((g2->M + TM - 1) / TM) * (g2->N / TN) : 0;
+  const GemmArgs& h = g2 ? *g2 : g;
   switch (g.epi) {
     case kEpiHeads:
-      gemm_kernel<T, kEpiHeads, TM, TN, WAVES, WM, WN, KS, ST><<<tiles, 64 * WAVES, 0, st>>>(g);
+      gemm_kernel<T, kEpiHeads, TM, TN, WAVES, WM, WN, KS, ST><<<tiles + tiles2, 64 * WAVES, 0, st>>>(g, h, tiles);
       break;
     case kEpiGelu:
-      gemm_kernel<T, kEpiGelu, TM, TN, WAVES, WM, WN, KS, ST><<<tiles, 64 * WAVES, 0, st>>>(g);
+      gemm_kernel<T, kEpiGelu, TM, TN, WAVES, WM, WN, KS, ST><<<tiles + tiles2, 64 * WAVES, 0, st>>>(g, h, tiles);
       break;
     case kEpiResidT:
-      gemm_kernel<T, kEpiResidT, TM, TN, WAVES, WM, WN, KS, ST><<<tiles, 64 * WAVES, 0, st>>>(g);
+      gemm_kernel<T, kEpiResidT, TM, TN, WAVES, WM, WN, KS, ST><<<tiles + tiles2, 64 * WAVES, 0, st>>>(g, h, tiles);
       break;
     case kEpiResidF32:
-      gemm_kernel<T, kEpiResidF32, TM, TN, WAVES, WM, WN, KS, ST><<<tiles, 64 * WAVES, 0, st>>>(g);
+      gemm_kernel<T, kEpiResidF32, TM, TN, WAVES, WM, WN, KS, ST><<<tiles + tiles2, 64 * WAVES, 0, st>>>(g, h, tiles);
       break;
     case kEpiPartial:
-      gemm_kernel<T, kEpiPartial, TM, TN, WAVES, WM, WN, KS, ST><<<tiles, 64 * WAVES, 0, st>>>(g);
+      gemm_kernel<T, kEpiPartial, TM, TN, WAVES, WM, WN, KS, ST><<<tiles + tiles2, 64 * WAVES, 0, st>>>(g, h, tiles);
       break;
     default: return hipErrorInvalidValue;
   }
@@ -413,20 +429,20 @@ hipError_t gemm_launch(const GemmArgs& g, int tiles, hipStream_t st) {
 }
 
 template <typename T>
-hipError_t gemm_t(const GemmArgs& g, hipStream_t st) {
+hipError_t gemm_t(const GemmArgs& g, hipStream_t st, const GemmArgs* g2 = nullptr) {
   // 256 x 256 tiles when their grid still covers every CU at least once
   const int big_tiles = g.N % 256 == 0 ? ((g.M + 255) / 256) * (g.N / 256) : 0;
   constexpr int KS = 128 / (int)sizeof(T);   // 128-byte tile rows: 64 fp16 / bf16, 32 fp32
-  if (big_tiles >= 256 && g.splits == 1)
-    return gemm_launch<T, 256, 256, 8, 128, 64, KS, 2>(g, big_tiles, st);
+  if (big_tiles >= 256 && g.splits == 1 && (!g2 || g2->N % 256 == 0))
+    return gemm_launch<T, 256, 256, 8, 128, 64, KS, 2>(g, big_tiles, st, g2);
   // small grids (at most 320 tiles of 128 x 128, e.g. 1024 rows): 64 x 128 tiles,
   // three workgroups per CU (24 KB of LDS per stage), so more K steps are in flight
   // per CU than with 128 x 128 tiles at two per CU
   const int t128 = ((g.M + 127) / 128) * (g.N / 128) * g.splits;
   if (t128 <= 320)
     return gemm_launch<T, 64, 128, 4, 32, 64, KS, 2>(g, ((g.M + 63) / 64) * (g.N / 128) * g.splits,
-                                                     st);
-  return gemm_launch<T, 128, 128, 4, 64, 64, KS, 2>(g, t128, st);
+                                                     st, g2);
+  return gemm_launch<T, 128, 128, 4, 64, 64, KS, 2>(g, t128, st, g2);
 }
 
 // LayerNorm of z = sum_s part[s] + bias + resid, one row per wave (the split-K
@@ -502,36 +518,6 @@ __global__ __launch_bounds__(256) void layernorm_parts_kernel(
       *(v4*)(out_t + (size_t)row * N + col) = w;
     }
   }
-}
-
-// Head-split epilogue of a split-K GEMM: thread per 4 consecutive columns of a row.
-template <typename T>
-__global__ __launch_bounds__(256) void splitk_heads_kernel(GemmArgs g) {
-  typedef typename Elem<T>::vec4 v4;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int per_row = g.N / 4;
-  if (idx >= (int64_t)g.M * per_row) return;
-  const int m = (int)(idx / per_row), n = 4 * (int)(idx - (int64_t)m * per_row);
-  const size_t sstride = (size_t)g.M * g.N, at = (size_t)m * g.N + n;
-  // loads of four splits in flight at a time; the sum keeps the split order
-  f32x4 z = *(const f32x4*)(g.part + at);
-  int sp = 1;
-  for (; sp + 4 <= g.splits; sp += 4) {
-    f32x4 p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = *(const f32x4*)(g.part + (sp + i) * sstride + at);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) z += p[i];
-  }
-  for (; sp < g.splits; ++sp) z += *(const f32x4*)(g.part + sp * sstride + at);
-  const v4 bv = *(const v4*)((const T*)g.bias + n);
-  const int ti = n / g.D, nn = n - ti * g.D;
-  const int h = nn >> 6, d = nn & 63;
-  const int bb = m / g.rows, rr = m - bb * g.rows;
-  v4 w;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) w[e] = Elem<T>::from_f(z[e] + Elem<T>::to_f(bv[e]));
-  *(v4*)((T*)g.heads[ti] + (((size_t)bb * g.H + h) * g.rows + rr) * 64 + d) = w;
 }
 
 template <typename T, bool RESID_F32>
@@ -773,18 +759,6 @@ hipError_t launch_layernorm_parts(int dtype, const float* part, int splits, cons
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_splitk_heads(const GemmArgs& g, hipStream_t st) {
-  const int64_t n = (int64_t)g.M * (g.N / 4);
-  const unsigned grid = (unsigned)((n + 255) / 256);
-  switch (g.dtype) {
-    case 0: splitk_heads_kernel<float><<<grid, 256, 0, st>>>(g); break;
-    case 1: splitk_heads_kernel<f16><<<grid, 256, 0, st>>>(g); break;
-    case 2: splitk_heads_kernel<bf16><<<grid, 256, 0, st>>>(g); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
 bool layernorm_width_ok(int N) {
   const int c = N / 256;
   return N % 256 == 0 && (c == 1 || c == 2 || c == 3 || c == 4 || c == 8 || c == 16);
@@ -798,6 +772,19 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
     case 0: return gemm_t<float>(g, st);
     case 1: return gemm_t<f16>(g, st);
     case 2: return gemm_t<bf16>(g, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm_pair(const GemmArgs& g, const GemmArgs& g2, hipStream_t st) {
+  if (g.epi != kEpiHeads || g2.epi != kEpiHeads || g.splits != 1 || g2.splits != 1 ||
+      g2.dtype != g.dtype || g2.K != g.K)
+    return hipErrorInvalidValue;
+  if (!gemm_shape_ok(g.M, g.N, g.K) || !gemm_shape_ok(g2.M, g2.N, g2.K)) return hipErrorInvalidValue;
+  switch (g.dtype) {
+    case 0: return gemm_t<float>(g, st, &g2);
+    case 1: return gemm_t<f16>(g, st, &g2);
+    case 2: return gemm_t<bf16>(g, st, &g2);
   }
   return hipErrorInvalidValue;
 }

@@ -175,7 +175,7 @@ struct LayerWs {
   size_t act_bytes, qkv_off, qg_off, attn_off, z_off, h1f_off, h1t_off, u_off, part_off, total;
   size_t pidx_off, pcnt_off, pbias_off;   // masks preprocessed inside a layer call (fp32,
                                           // or global tokens anywhere): index, count, bias
-  int split_qg, split_o, split_ffn2;   // split-K factors of the GEMMs with small grids
+  int split_o, split_ffn2;   // split-K factors of the GEMMs with small grids
 };
 
 LayerWs layer_ws(int dtype, int B, int S, int hidden, int H, int ffn, int G) {
@@ -197,14 +197,11 @@ LayerWs layer_ws(int dtype, int B, int S, int hidden, int H, int ffn, int G) {
     L.u_off = off;
     off += u_bytes;
   }
-  // fp32 partial sums of the split-K GEMMs (global-query projection, output
-  // projection, FFN2), one at a time
-  L.split_qg = G > 0 ? lf::gemm_splits(B * G, hidden, hidden) : 1;
+  // fp32 partial sums of the split-K GEMMs (output projection, FFN2), one at a time
   L.split_o = lf::gemm_splits((int)M, hidden, hidden);
   L.split_ffn2 = lf::gemm_splits((int)M, hidden, ffn);
   size_t part = 0;
-  if (L.split_qg > 1) part = (size_t)L.split_qg * B * G * hidden * 4;
-  if (L.split_o > 1) part = std::max(part, (size_t)L.split_o * M * hidden * 4);
+  if (L.split_o > 1) part = (size_t)L.split_o * M * hidden * 4;
   if (L.split_ffn2 > 1) part = std::max(part, (size_t)L.split_ffn2 * M * hidden * 4);
   L.part_off = off;
   off += align256(part);
@@ -318,8 +315,8 @@ hipError_t run_ffn_two_gemm(int dtype, const void* h, const float* resid, const 
   return lf::launch_layernorm(dtype, z, ln_g, ln_b, ln_eps, M, D, nullptr, y, st);
 }
 
-// One encoder layer ([FT-LF] per-layer steps 1-6) as 8 launches on `st`; arguments
-// already validated.
+// One encoder layer ([FT-LF] per-layer steps 1-6) as 7 launches on `st` (8 when the
+// masks are preprocessed inside the call); arguments already validated.
 int run_layer(int dtype, const lf_layer_weights* w, const void* x, const LayerMasks& mk, int B,
               int S, int hidden, int H, int ffn, int W, int G, float attn_scale, float ln_eps,
               void* y, char* ws, const LayerWs& L, hipStream_t st) {
@@ -347,12 +344,6 @@ int run_layer(int dtype, const lf_layer_weights* w, const void* x, const LayerMa
   };
   float* part = (float*)(ws + L.part_off);
   hipError_t he;
-  // step 1: packed projections, split into heads ([B, H, S, 64] each)
-  {
-    lf::GemmArgs g = gemm(lf::kEpiHeads, x, D, 0, 0, w->w_proj, D, w->b_proj, M, 5 * D, D);
-    for (int i = 0; i < 5; ++i) g.heads[i] = qkv[i];
-    if ((he = lf::launch_gemm(g, st)) != hipSuccess) return hip_fail(he, "projection GEMM");
-  }
   // masks preprocessed inside this call: fp32 attention reads them, and with global
   // tokens anywhere the global queries and keys go through the index
   const int32_t* gidx = mk.gidx;
@@ -369,23 +360,22 @@ int run_layer(int dtype, const lf_layer_weights* w, const void* x, const LayerMa
     gcnt = pcnt;
     mbias = pbias;
   }
-  // the global queries: rows 0 .. G-1 of every sequence, or the rows at the global
-  // positions (the first G entries of the index)
-  if (G > 0) {
-    lf::GemmArgs g = gemm(lf::kEpiHeads, x, D, G, S, w->w_qg, D, w->b_qg, B * G, D, D);
-    g.heads[0] = qg;
-    g.rows = G;
-    if (mk.any) g.a_rows = gidx;
-    if (L.split_qg > 1) {
-      // B * G rows: a handful of tiles, so the K range is split and reduced after
-      g.epi = lf::kEpiPartial;
-      g.splits = L.split_qg;
-      g.part = part;
-      if ((he = lf::launch_gemm(g, st)) != hipSuccess) return hip_fail(he, "global-query GEMM");
-      if ((he = lf::launch_splitk_heads(g, st)) != hipSuccess)
-        return hip_fail(he, "global-query reduction");
+  // steps 1-2: packed projections split into heads ([B, H, S, 64] each), and the
+  // global queries (rows 0 .. G-1 of every sequence, or the rows at the global
+  // positions: the first G entries of the index) in the same launch, their few tiles
+  // after the projection's
+  {
+    lf::GemmArgs g = gemm(lf::kEpiHeads, x, D, 0, 0, w->w_proj, D, w->b_proj, M, 5 * D, D);
+    for (int i = 0; i < 5; ++i) g.heads[i] = qkv[i];
+    if (G > 0) {
+      lf::GemmArgs gq = gemm(lf::kEpiHeads, x, D, G, S, w->w_qg, D, w->b_qg, B * G, D, D);
+      gq.heads[0] = qg;
+      gq.rows = G;
+      if (mk.any) gq.a_rows = gidx;
+      if ((he = lf::launch_gemm_pair(g, gq, st)) != hipSuccess)
+        return hip_fail(he, "projection GEMMs");
     } else if ((he = lf::launch_gemm(g, st)) != hipSuccess) {
-      return hip_fail(he, "global-query GEMM");
+      return hip_fail(he, "projection GEMM");
     }
   }
   // steps 3-4: attention, heads joined ([B, S, H * 64])

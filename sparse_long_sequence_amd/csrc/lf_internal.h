@@ -68,7 +68,7 @@ enum GemmEpi {
   kEpiResidT = 2,    // out[m * ldo + n] = acc + bias + resid[m * ldr + n] (resid dtype), fp32
   kEpiResidF32 = 3,  // same with an fp32 residual
   kEpiPartial = 4,   // split-K: part[split][m * N + n] = acc (fp32, no bias); reduced by
-                     // launch_layernorm_parts / launch_splitk_heads
+                     // launch_layernorm_parts
 };
 
 struct GemmArgs {
@@ -102,15 +102,16 @@ int gemm_splits(int M, int N, int K);
 // Row widths the LayerNorm kernel takes (multiples of 256 up to 4096).
 bool layernorm_width_ok(int N);
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
+// Two head-split GEMMs (kEpiHeads, no split-K, same dtype and K) in one launch: the
+// tiles of g2 follow those of g in the grid (g's tile shape), so a small g2 fills
+// the idle slots of g's last round of tiles.
+hipError_t launch_gemm_pair(const GemmArgs& g, const GemmArgs& g2, hipStream_t st);
 // LayerNorm of z = sum_s part[s] + bias + resid (resid in the layer dtype, or fp32
 // when resid_f32): the reduction of a split-K GEMM fused into the row kernel.
 hipError_t launch_layernorm_parts(int dtype, const float* part, int splits, const void* bias,
                                   const void* resid, bool resid_f32, const void* gamma,
                                   const void* beta, float eps, int M, int N, float* out_f32,
                                   void* out_t, hipStream_t st);
-// Head-split epilogue of a split-K GEMM: heads[0] gets sum_s part[s] + bias in the
-// kEpiHeads layout (row m -> (m / rows, m % rows), column n -> head n / 64, dim n % 64).
-hipError_t launch_splitk_heads(const GemmArgs& g, hipStream_t st);
 // Fused FFN (gemm.hip): part[s][m][:] = GELU(x[m] W1^T + b1) W2^T over F slice s of
 // `splits` equal slices, the GELU output kept on chip; fp16 / bf16, D in
 // {256, 512, 768, 1024}, F a multiple of 32 * splits.
