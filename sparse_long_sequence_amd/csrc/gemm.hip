@@ -462,9 +462,21 @@ __global__ __launch_bounds__(256) void layernorm_parts_kernel(
   for (int c = 0; c < NPL; ++c) {
     const int col = 4 * (lane + 64 * c);
     const size_t at = (size_t)row * N + col;
-    f32x4 z = *(const f32x4*)(part + at);
-    int sp = 1;
-    for (; sp + 4 <= splits; sp += 4) {   // four loads in flight; the sum keeps the order
+    // four loads in flight at a time (the first four included); the sum keeps the
+    // split order
+    f32x4 z;
+    int sp;
+    if (splits >= 4) {
+      f32x4 p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = *(const f32x4*)(part + i * sstride + at);
+      z = ((p[0] + p[1]) + p[2]) + p[3];
+      sp = 4;
+    } else {
+      z = *(const f32x4*)(part + at);
+      sp = 1;
+    }
+    for (; sp + 4 <= splits; sp += 4) {
       f32x4 p[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) p[i] = *(const f32x4*)(part + (sp + i) * sstride + at);
