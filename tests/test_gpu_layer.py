@@ -57,7 +57,9 @@ def _run(lf, x, w, lm, gm, H, W, G):
     (1, 512, 256, 4, 512, 128, 8, None),
     (2, 384, 512, 8, 1024, 64, 0, (0.1, 0.25)),
     (1, 256, 256, 4, 384, 128, 64, None),
-], ids=["B1_S512_D256_G8", "B2_S384_D512_G0_pad", "B1_S256_D256_G64"])
+    # 200 global-query rows: four 64-row tiles after the projection's in one launch
+    (2, 512, 256, 4, 512, 256, 100, None),
+], ids=["B1_S512_D256_G8", "B2_S384_D512_G0_pad", "B1_S256_D256_G64", "B2_S512_D256_G100"])
 def test_layer_parity_small(lf, dtype, case):
     B, S, D, H, F, W, G, pad = case
     x, w, lm, gm = _inputs(11 + S + G, B, S, D, H, F, G, dtype, pad)
@@ -97,6 +99,23 @@ def test_layer_full_workload_sampled_rows(lf):
                    for s in [0, 1, wl.G - 1, wl.G, wl.G + 1, wl.W // 2, wl.S // 2, wl.S - 1]
                    + [int(v) for v in rng.integers(0, wl.S, 12)]})
     ref = oracle.encoder_layer(x, w, lm, gm, wl.H, wl.W, wl.G, rows=rows)
+    g_rows = np.stack([got[b, s].double().numpy() for (b, s) in rows])
+    err = np.abs(g_rows - ref).max()
+    assert err <= TOL["fp16"], f"max abs err {err:.3e} over {len(rows)} rows"
+
+
+def test_layer_mid_size_many_global_rows_sampled(lf):
+    # 2048 rows: the projection takes the 128 x 128 tiles; 2 x 200 global-query rows are
+    # four more 128-row tiles in the same launch
+    B, S, D, H, F, W, G = 2, 1024, 1024, 16, 1024, 512, 200
+    x, w, lm, gm = _inputs(23, B, S, D, H, F, G, "fp16", w_std=0.02)
+    y = _run(lf, x, w, lm, gm, H, W, G)
+    assert torch.isfinite(y).all()
+    got = y.cpu()
+    rng = np.random.default_rng(29)
+    rows = sorted({(b, s) for b in range(B)
+                   for s in [0, 127, 128, 199, 200, S - 1] + [int(v) for v in rng.integers(0, S, 6)]})
+    ref = oracle.encoder_layer(x, w, lm, gm, H, W, G, rows=rows)
     g_rows = np.stack([got[b, s].double().numpy() for (b, s) in rows])
     err = np.abs(g_rows - ref).max()
     assert err <= TOL["fp16"], f"max abs err {err:.3e} over {len(rows)} rows"
