@@ -457,44 +457,49 @@ __global__ __launch_bounds__(256) void layernorm_parts_kernel(
   const int lane = threadIdx.x & 63;
   if (row >= M) return;
   const size_t sstride = (size_t)M * N;
-  f32x4 x[NPL];
+  const size_t rbase = (size_t)row * N + 4 * lane;   // column chunk c adds 256 c
+  // bias and residual first, then the partials GS splits at a time: every load of a
+  // group (all column chunks) is issued before its first add.  A group's splits past
+  // `splits` read split 0 again and are not added; the sums keep the split order, then
+  // add the residual, then the bias.
+  constexpr int GS = NPL <= 4 ? 4 : NPL <= 8 ? 2 : 1;
+  f32x4 rv[NPL], bv[NPL];
 #pragma unroll
   for (int c = 0; c < NPL; ++c) {
-    const int col = 4 * (lane + 64 * c);
-    const size_t at = (size_t)row * N + col;
-    // four loads in flight at a time (the first four included); the sum keeps the
-    // split order
-    f32x4 z;
-    int sp;
-    if (splits >= 4) {
-      f32x4 p[4];
+    const v4 b4 = *(const v4*)(bias + 4 * lane + 256 * c);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = *(const f32x4*)(part + i * sstride + at);
-      z = ((p[0] + p[1]) + p[2]) + p[3];
-      sp = 4;
-    } else {
-      z = *(const f32x4*)(part + at);
-      sp = 1;
-    }
-    for (; sp + 4 <= splits; sp += 4) {
-      f32x4 p[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = *(const f32x4*)(part + (sp + i) * sstride + at);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) z += p[i];
-    }
-    for (; sp < splits; ++sp) z += *(const f32x4*)(part + sp * sstride + at);
-    const v4 bv = *(const v4*)(bias + col);
+    for (int e = 0; e < 4; ++e) bv[c][e] = Elem<T>::to_f(b4[e]);
     if (RESID_F32) {
-      z += *(const f32x4*)((const float*)resid + at);
+      rv[c] = *(const f32x4*)((const float*)resid + rbase + 256 * c);
     } else {
-      const v4 rv = *(const v4*)((const T*)resid + at);
+      const v4 r4 = *(const v4*)((const T*)resid + rbase + 256 * c);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) z[e] += Elem<T>::to_f(rv[e]);
+      for (int e = 0; e < 4; ++e) rv[c][e] = Elem<T>::to_f(r4[e]);
     }
+  }
+  f32x4 x[NPL];
+  for (int s0 = 0; s0 < splits; s0 += GS) {
+    f32x4 p[NPL][GS];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) z[e] += Elem<T>::to_f(bv[e]);
-    x[c] = z;
+    for (int c = 0; c < NPL; ++c)
+#pragma unroll
+      for (int i = 0; i < GS; ++i) {
+        const int sp = s0 + i < splits ? s0 + i : 0;
+        p[c][i] = *(const f32x4*)(part + sp * sstride + rbase + 256 * c);
+      }
+#pragma unroll
+    for (int c = 0; c < NPL; ++c) {
+      if (s0 == 0) x[c] = p[c][0];
+      else x[c] += p[c][0];
+#pragma unroll
+      for (int i = 1; i < GS; ++i)
+        if (s0 + i < splits) x[c] += p[c][i];
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < NPL; ++c) {
+    x[c] += rv[c];
+    x[c] += bv[c];
   }
   float s = 0.0f;
 #pragma unroll
