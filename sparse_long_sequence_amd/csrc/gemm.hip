@@ -65,51 +65,44 @@ __device__ inline float gelu(float x) {
   return 0.5f * x * (1.0f + erf_x);
 }
 
-// Epilogue of 4 consecutive output columns nb .. nb + 3 of row m (acc = the raw sums).
+// Residual operand of the residual epilogues (4 columns of one row, as stored).
+template <typename T, int EPI> struct ResidVec { typedef typename Elem<T>::vec4 type; };
+template <typename T> struct ResidVec<T, kEpiResidF32> { typedef f32x4 type; };
+
+// Epilogue of 4 consecutive output columns nb .. nb + 3 of row m (acc = the raw sums,
+// bv = their bias, rv = their residual; GELU and residual epilogues).
 template <typename T, int EPI>
-__device__ __forceinline__ void epilogue4(const GemmArgs& g, int m, int nb, const float acc[4]) {
+__device__ __forceinline__ void epilogue4(const GemmArgs& g, int m, int nb, const float acc[4],
+                                          const typename Elem<T>::vec4& bv,
+                                          const typename ResidVec<T, EPI>::type& rv) {
   typedef typename Elem<T>::vec4 v4;
-  const v4 bv = *(const v4*)((const T*)g.bias + nb);
   float r[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) r[e] = acc[e] + Elem<T>::to_f(bv[e]);
-  if (EPI == kEpiHeads) {
-    // n -> tensor n / D, head (n % D) / 64, dim n % 64; m -> (batch, row)
-    const int ti = nb / g.D, nn = nb - ti * g.D;
-    const int h = nn >> 6, d = nn & 63;
-    const int bb = m / g.rows, rr = m - bb * g.rows;
-    T* dst = (T*)g.heads[ti] + (((size_t)bb * g.H + h) * g.rows + rr) * 64 + d;
-    v4 w;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = Elem<T>::from_f(r[e]);
-    *(v4*)dst = w;
-  } else if (EPI == kEpiGelu) {
+  if (EPI == kEpiGelu) {
     v4 w;
 #pragma unroll
     for (int e = 0; e < 4; ++e) w[e] = Elem<T>::from_f(gelu(r[e]));
     *(v4*)((T*)g.out + (size_t)m * g.ldo + nb) = w;
   } else {
     f32x4 z;
-    if (EPI == kEpiResidF32) {
-      const f32x4 rv = *(const f32x4*)((const float*)g.resid + (size_t)m * g.ldr + nb);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) z[e] = r[e] + rv[e];
-    } else {
-      const v4 rv = *(const v4*)((const T*)g.resid + (size_t)m * g.ldr + nb);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) z[e] = r[e] + Elem<T>::to_f(rv[e]);
-    }
+    for (int e = 0; e < 4; ++e)
+      z[e] = r[e] + (EPI == kEpiResidF32 ? (float)rv[e] : Elem<T>::to_f(rv[e]));
     *(f32x4*)((float*)g.out + (size_t)m * g.ldo + nb) = z;
   }
 }
 
 // Epilogue of one 32 x 32 MFMA tile: the lane's 16 sums are columns cbase + 8 jj +
-// 4 gq .. + 3 (jj = 0..3) of output row m; cbase (a multiple of 32) is the same for
-// the whole wave, and D is a multiple of 64, so for the head split the tensor and
-// head come from cbase alone (one scalar division per tile, none per element).
+// 4 gq .. + 3 (jj = 0..3) of output row m, with their bias bv[jj] and residual
+// rv[jj] already in registers; cbase (a multiple of 32) is the same for the whole
+// wave, and D is a multiple of 64, so for the head split the tensor and head come
+// from cbase alone (one scalar division per tile, none per element).
 template <typename T, int EPI>
 __device__ __forceinline__ void epilogue_tile(const GemmArgs& g, int m, int cbase, int gq,
-                                              const f32x16& acc, int split) {
+                                              const f32x16& acc, int split,
+                                              const typename Elem<T>::vec4 bv[4],
+                                              const typename ResidVec<T, EPI>::type rv[4]) {
   typedef typename Elem<T>::vec4 v4;
   if (EPI == kEpiPartial) {
     float* dst = g.part + ((size_t)split * g.M + m) * g.N + cbase + 4 * gq;
@@ -123,13 +116,11 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& g, int m, int cbas
     const int h = nn >> 6, d0 = nn & 63;
     const int bb = m / g.rows, rr = m - bb * g.rows;
     T* dst = (T*)g.heads[ti] + (((size_t)bb * g.H + h) * g.rows + rr) * 64 + d0 + 4 * gq;
-    const T* bias = (const T*)g.bias + cbase + 4 * gq;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const v4 bv = *(const v4*)(bias + 8 * jj);
       v4 w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = Elem<T>::from_f(acc[4 * jj + e] + Elem<T>::to_f(bv[e]));
+      for (int e = 0; e < 4; ++e) w[e] = Elem<T>::from_f(acc[4 * jj + e] + Elem<T>::to_f(bv[jj][e]));
       *(v4*)(dst + 8 * jj) = w;
     }
     return;
@@ -137,7 +128,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& g, int m, int cbas
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
     const float r[4] = {acc[4 * jj], acc[4 * jj + 1], acc[4 * jj + 2], acc[4 * jj + 3]};
-    epilogue4<T, EPI>(g, m, cbase + 8 * jj + 4 * gq, r);
+    epilogue4<T, EPI>(g, m, cbase + 8 * jj + 4 * gq, r, bv[jj], rv[jj]);
   }
 }
 
@@ -338,14 +329,40 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs g0, GemmArgs 
   if (ks + 1 < nk) step(std::integral_constant<int, 1>{}, ks + 1);
   if constexpr (ST > 2) if (ks + 2 < nk) step(std::integral_constant<int, 2>{}, ks + 2);
 
-  // epilogue: lane holds, for output row m, columns nb .. nb + 3 of each group
+  // epilogue: lane holds, for output row m, columns nb .. nb + 3 of each group.  The
+  // bias of the wave's columns, and (residual epilogues) the residual of each 32-row
+  // group, are loaded before that group's stores: as far as the compiler knows the
+  // outputs may alias them, so a load placed after a store would wait on its own,
+  // one memory round trip per 4 columns
+  typedef typename Elem<T>::vec4 v4;
+  typedef typename ResidVec<T, EPI>::type rv_t;
+  typedef typename std::conditional<EPI == kEpiResidF32, float, T>::type r_t;
+  constexpr bool kRes = EPI == kEpiResidT || EPI == kEpiResidF32;
+  v4 bv[NI][4] = {};
+  if constexpr (EPI != kEpiPartial) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        bv[i][jj] = *(const v4*)((const T*)g.bias + n0 + wn + 32 * i + 8 * jj + 4 * gq);
+  }
 #pragma unroll
   for (int j = 0; j < MI; ++j) {
     const int m = m0 + wm + 32 * j + n;
+    rv_t rv[kRes ? NI : 1][4] = {};
+    if constexpr (kRes) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          if (m < g.M)
+            rv[i][jj] = *(const rv_t*)((const r_t*)g.resid + (size_t)m * g.ldr + n0 + wn + 32 * i +
+                                       8 * jj + 4 * gq);
+    }
     if (m >= g.M) continue;
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-      epilogue_tile<T, EPI>(g, m, n0 + wn + 32 * i, gq, acc[i][j], split);
+      epilogue_tile<T, EPI>(g, m, n0 + wn + 32 * i, gq, acc[i][j], split, bv[i], rv[kRes ? i : 0]);
   }
 }
 
