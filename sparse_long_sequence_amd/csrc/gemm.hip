@@ -366,6 +366,47 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs g0, GemmArgs 
   }
 }
 
+// LayerNorm gamma and beta of a lane's columns 4 (lane + 64 c) .. + 3, loaded with the
+// row (a load placed after the row's first store would wait on its own: the outputs
+// may alias gamma and beta as far as the compiler knows).
+template <typename T, int NPL>
+__device__ __forceinline__ void ln_load_affine(const T* __restrict__ gamma,
+                                               const T* __restrict__ beta, int lane,
+                                               typename Elem<T>::vec4 gv[NPL],
+                                               typename Elem<T>::vec4 bt[NPL]) {
+  typedef typename Elem<T>::vec4 v4;
+#pragma unroll
+  for (int c = 0; c < NPL; ++c) {
+    gv[c] = *(const v4*)(gamma + 4 * (lane + 64 * c));
+    bt[c] = *(const v4*)(beta + 4 * (lane + 64 * c));
+  }
+}
+
+// (x - mean) * inv * gamma + beta of one row, written as fp32 and / or in T.
+template <typename T, int NPL>
+__device__ __forceinline__ void ln_write_row(const f32x4 x[NPL], float mean, float inv,
+                                             const typename Elem<T>::vec4 gv[NPL],
+                                             const typename Elem<T>::vec4 bt[NPL], size_t rowoff,
+                                             int lane, float* __restrict__ out_f32,
+                                             T* __restrict__ out_t) {
+  typedef typename Elem<T>::vec4 v4;
+#pragma unroll
+  for (int c = 0; c < NPL; ++c) {
+    const int col = 4 * (lane + 64 * c);
+    f32x4 y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      y[e] = (x[c][e] - mean) * inv * Elem<T>::to_f(gv[c][e]) + Elem<T>::to_f(bt[c][e]);
+    if (out_f32) *(f32x4*)(out_f32 + rowoff + col) = y;
+    if (out_t) {
+      v4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = Elem<T>::from_f(y[e]);
+      *(v4*)(out_t + rowoff + col) = w;
+    }
+  }
+}
+
 // LayerNorm of one row per wave ([FT-LF] steps 5 and 6): mean, biased variance
 // (two passes over the row held in registers), (z - mean) / sqrt(var + eps) * gamma
 // + beta; written as fp32 (the residual stream) and / or in the layer dtype.
@@ -383,6 +424,8 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict_
   f32x4 x[NPL];
 #pragma unroll
   for (int c = 0; c < NPL; ++c) x[c] = *(const f32x4*)(zr + 4 * (lane + 64 * c));
+  v4 gv[NPL], bt[NPL];
+  ln_load_affine<T, NPL>(gamma, beta, lane, gv, bt);
   float s = 0.0f;
 #pragma unroll
   for (int c = 0; c < NPL; ++c) s += (x[c][0] + x[c][1]) + (x[c][2] + x[c][3]);
@@ -400,23 +443,7 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const float* __restrict_
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) q += __shfl_xor(q, d, 64);
   const float inv = 1.0f / sqrtf(q / (float)N + eps);
-#pragma unroll
-  for (int c = 0; c < NPL; ++c) {
-    const int col = 4 * (lane + 64 * c);
-    const v4 gv = *(const v4*)(gamma + col);
-    const v4 bv = *(const v4*)(beta + col);
-    f32x4 y;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      y[e] = (x[c][e] - mean) * inv * Elem<T>::to_f(gv[e]) + Elem<T>::to_f(bv[e]);
-    if (out_f32) *(f32x4*)(out_f32 + (size_t)row * N + col) = y;
-    if (out_t) {
-      v4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = Elem<T>::from_f(y[e]);
-      *(v4*)(out_t + (size_t)row * N + col) = w;
-    }
-  }
+  ln_write_row<T, NPL>(x, mean, inv, gv, bt, (size_t)row * N, lane, out_f32, out_t);
 }
 
 template <typename T, int TM, int TN, int WAVES, int WM, int WN, int KS, int ST>
@@ -480,6 +507,8 @@ __global__ __launch_bounds__(256) void layernorm_parts_kernel(
   // `splits` read split 0 again and are not added; the sums keep the split order, then
   // add the residual, then the bias.
   constexpr int GS = NPL <= 4 ? 4 : NPL <= 8 ? 2 : 1;
+  v4 gv[NPL], bt[NPL];
+  ln_load_affine<T, NPL>(gamma, beta, lane, gv, bt);
   f32x4 rv[NPL], bv[NPL];
 #pragma unroll
   for (int c = 0; c < NPL; ++c) {
@@ -535,23 +564,7 @@ __global__ __launch_bounds__(256) void layernorm_parts_kernel(
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) q += __shfl_xor(q, d, 64);
   const float inv = 1.0f / sqrtf(q / (float)N + eps);
-#pragma unroll
-  for (int c = 0; c < NPL; ++c) {
-    const int col = 4 * (lane + 64 * c);
-    const v4 gv = *(const v4*)(gamma + col);
-    const v4 bv = *(const v4*)(beta + col);
-    f32x4 y;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      y[e] = (x[c][e] - mean) * inv * Elem<T>::to_f(gv[e]) + Elem<T>::to_f(bv[e]);
-    if (out_f32) *(f32x4*)(out_f32 + (size_t)row * N + col) = y;
-    if (out_t) {
-      v4 w;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = Elem<T>::from_f(y[e]);
-      *(v4*)(out_t + (size_t)row * N + col) = w;
-    }
-  }
+  ln_write_row<T, NPL>(x, mean, inv, gv, bt, (size_t)row * N, lane, out_f32, out_t);
 }
 
 template <typename T, bool RESID_F32>
