@@ -566,6 +566,9 @@ __device__ void global_combine(const AttnArgs& a, const Ctx<T>& c) {
   T* outh = (T*)a.out + (size_t)c.b * a.out_sb + (size_t)c.h * a.out_sh;
   for (int idx = t; idx < nb * 16; idx += kThreads) {
     const int rl = idx >> 4, d4 = (idx & 15) * 4;
+    // the row's position and mask value first: their loads travel with the partials'
+    const int pos = RAW && !ANY ? rl : a.gidx[(size_t)c.b * c.S + rl];
+    const T mval = c.mask[pos];
     const int off_ml = rl * kPartPitch * 4, off_o = (rl * kPartPitch + 4 + d4) * 4;
     float M = kNegBig, L = 0.0f;
     f32x4 O = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -596,8 +599,7 @@ __device__ void global_combine(const AttnArgs& a, const Ctx<T>& c) {
         O += __builtin_bit_cast(f32x4, pv[j]) * w;
       }
     }
-    const int pos = RAW && !ANY ? rl : a.gidx[(size_t)c.b * c.S + rl];
-    const float inv = mask_live<RAW>(Elem<T>::to_f(c.mask[pos])) ? 1.0f / L : 0.0f;
+    const float inv = mask_live<RAW>(Elem<T>::to_f(mval)) ? 1.0f / L : 0.0f;
     typename Frag<T>::v4 w;
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = Elem<T>::from_f(O[i] * inv);
@@ -762,6 +764,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   v8 qf[4];
   const int srow = c.r0 + 64 * rg + 32 * sb + n;
   load_q<T>(qf, (const T*)a.q + head + (size_t)(srow < c.S ? srow : 0) * 64, srow < c.S);
+  // the row's mask value (and global flag) for the epilogue, loaded now so that no
+  // load sits between the band loop and the output stores
+  const int srow_c = srow < c.S ? srow : 0;
+  const T row_mask = c.mask[srow_c];
+  const unsigned short row_gflag = ANY ? c.gm[srow_c] : (unsigned short)0;
   __builtin_amdgcn_sched_barrier(0);
   static_assert(kDepth == 2, "steps run in pairs: entry e uses set e % 2");
   // after the band loop the ring holds list entries up to n_list + 1 and the register
@@ -812,9 +819,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     typedef typename Frag<T>::v4 v4;
     const float l_tot = cross_half_sum(l_run);
     // global rows are written by the combine
-    const bool local = srow < c.S && (ANY ? (c.gm[srow] & 0x7fff) != 0 : srow >= c.nb);
+    const bool local = srow < c.S && (ANY ? (row_gflag & 0x7fff) != 0 : srow >= c.nb);
     if (local) {
-      const bool live = mask_live<RAW>(Elem<T>::to_f(c.mask[srow]));
+      const bool live = mask_live<RAW>(Elem<T>::to_f(row_mask));
       const float inv = live ? 1.0f / l_tot : 0.0f;
       T* dst = (T*)a.out + (size_t)c.b * a.out_sb + (size_t)c.h * a.out_sh + (size_t)srow * a.out_ss;
 #pragma unroll
