@@ -225,9 +225,10 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs g0, GemmArgs 
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int n = lane & 31, gq = lane >> 5;
   const bool second = EPI == kEpiHeads && (int)blockIdx.x >= tiles0;
-  // the problem's arguments read in place from the kernel-argument segment (g0 at
-  // offset 0, g1 right after it): a select between the two parameters themselves
-  // would copy both to scratch memory
+  // the problem's arguments read in place from the kernel-argument segment: the
+  // AMDGPU kernel ABI lays the arguments out in order, each at its natural alignment,
+  // so g0 sits at offset 0 and g1 at sizeof(GemmArgs) (a multiple of its alignment).
+  // A select between the two parameters themselves would copy both to scratch memory.
   typedef __attribute__((address_space(4))) const GemmArgs* kargs_t;
   const GemmArgs& g =
       *(const GemmArgs*)((kargs_t)__builtin_amdgcn_kernarg_segment_ptr() + (second ? 1 : 0));
