@@ -441,7 +441,9 @@ __device__ inline void store_entry(Slot<T>& sl, const Stage<T>& s, const Ctx<T>&
 // ANY is unused in the body: it gives each kernel instantiation a copy of its own
 // (with one copy shared by the two raw-mask kernels, the compiler allocated the
 // leading-globals kernel's prologue registers worse: 14 spilled VGPRs instead of 1).
-template <typename T, bool RAW, bool ANY>
+// PRE: the first round of the first query block is already in the ring (the band
+// loop staged it); else every round loads its entries.
+template <typename T, bool RAW, bool ANY, bool PRE>
 __device__ void global_split_run(const AttnArgs& a, const Ctx<T>& c, int sp, Slot<T>* ring,
                                  int slot0, const typename Frag<T>::v8 qf0[4]) {
   typedef typename Frag<T>::v8 v8;
@@ -470,7 +472,7 @@ __device__ void global_split_run(const AttnArgs& a, const Ctx<T>& c, int sp, Slo
     float m_run = kNegBig, l_run = 0.0f;
     for (int u = 0; u < n_rounds; ++u) {
       const int base = k_lo + kBlk * kWaves * u;
-      const bool staged = qb == 0 && u == 0;
+      const bool staged = PRE && qb == 0 && u == 0;
       if (!staged) {
         Stage<T> st[kSplitEnt];
 #pragma unroll
@@ -656,6 +658,48 @@ __device__ inline int count_globals(const AttnArgs& a, int b, int first) {
   return __builtin_amdgcn_readfirstlane(cnt);
 }
 
+// Global rows of one (b, h) in a workgroup of their own (GWG mode, used when the
+// band tiles leave CUs idle): one split over every key, its partial merged by the
+// same workgroup; it runs beside the band tiles, which then skip the split, the
+// ticket and the combine.
+template <typename T, bool RAW, bool ANY>
+__device__ void global_rows_wg(const AttnArgs& a, Slot<T>* ring, int bh) {
+  typedef typename Frag<T>::v8 v8;
+  Ctx<T> c;
+  c.bh = bh;
+  c.b = __builtin_amdgcn_readfirstlane(bh / a.H);
+  c.h = __builtin_amdgcn_readfirstlane(bh % a.H);
+  c.S = a.S;
+  c.W = a.W;
+  c.G = a.G;
+  c.ngp = (a.G + kEnt - 1) / kEnt;
+  c.tile = 0;
+  c.r0 = 0;
+  c.kbase = 0;
+  c.n_list = 0;
+  c.mask = (const T*)(RAW ? a.local_mask : a.bias) + (size_t)c.b * c.S;
+  c.gi = ANY ? a.gidx + (size_t)c.b * c.S : nullptr;
+  c.gm = ANY ? (const unsigned short*)a.global_mask + (size_t)c.b * c.S : nullptr;
+  c.split = true;
+  c.sp_lo = 0;
+  c.sp_hi = c.S;
+  const size_t head = (size_t)bh * c.S * 64;
+  c.kh = (const T*)a.k + head;
+  c.vh = (const T*)a.v + head;
+  c.kgh = (const T*)a.kg + head;
+  c.vgh = (const T*)a.vg + head;
+  const int first = count_load<T, RAW, ANY>(a, c.b);
+  c.nb = count_globals<T, RAW, ANY>(a, c.b, first);
+  if (c.nb == 0) return;
+  const int n = lane_id() & 31;
+  v8 qg0[4];
+  load_q<T>(qg0, (const T*)a.qg + ((size_t)bh * a.G + (n < a.G ? n : 0)) * 64, n < a.G);
+  global_split_run<T, RAW, ANY, false>(a, c, 0, ring, 0, qg0);
+  __builtin_amdgcn_s_waitcnt(0);   // the partial's write-through stores are complete
+  __syncthreads();
+  global_combine<T, RAW, ANY>(a, c);
+}
+
 // One step t of a wave: the two 32-key blocks of its entry.  LDS reads first
 // (K, V^T and per-key terms of both blocks), then QK^T, the band mask on edge
 // steps only, one running-max update for the 64 keys, P, PV, then the staging of
@@ -702,8 +746,9 @@ __device__ __forceinline__ void band_step(const Ctx<T>& c, Slot<T>* ring, int tt
 }
 
 // RAW: read the raw masks (else global_count and the shifted mask); ANY (with RAW):
-// global tokens at any positions, through global_idx / global_count.
-template <typename T, bool RAW, bool ANY>
+// global tokens at any positions, through global_idx / global_count; GWG: workgroups
+// past the band tiles compute the global rows, and the band tiles run no split.
+template <typename T, bool RAW, bool ANY, bool GWG>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_mfma_kernel(AttnArgs a, int n_tiles) {
   __shared__ __attribute__((aligned(16))) Slot<T> ring[kRing];
   typedef typename Frag<T>::v8 v8;
@@ -712,6 +757,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int rg = wave & 3, sb = wave >> 2;
   const int n = lane & 31, g = lane >> 5;
   const int n_wg = a.B * a.H * n_tiles;
+  if constexpr (GWG) {
+    if ((int)blockIdx.x >= n_wg) {   // uniform: the whole workgroup
+      global_rows_wg<T, RAW, ANY>(a, ring, (int)blockIdx.x - n_wg);
+      return;
+    }
+  }
   // the integer divides below run on the vector ALU; readfirstlane keeps their
   // (uniform) results, and everything derived from them, in scalar registers
   const int li = __builtin_amdgcn_readfirstlane(xcd_remap(blockIdx.x, n_wg));
@@ -738,7 +789,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   c.gi = ANY ? a.gidx + (size_t)c.b * c.S : nullptr;
   c.gm = ANY ? (const unsigned short*)a.global_mask + (size_t)c.b * c.S : nullptr;
   const float c2 = a.scale * kLog2e;
-  const bool split = a.G > 0 && c.tile < a.n_split;
+  const bool split = !GWG && a.G > 0 && c.tile < a.n_split;
   c.split = split;
   c.sp_lo = split ? c.tile * a.split_len : 0;
   c.sp_hi = split ? min(c.S, c.sp_lo + a.split_len) : 0;
@@ -852,7 +903,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
       store_entry<T, RAW, ANY, true>(ring[(e2 + 1) % kRing], st[0], c, e2 + 1);
     }
     __syncthreads();
-    global_split_run<T, RAW, ANY>(a, c, c.tile, ring, c.n_list % kRing, qg0);
+    global_split_run<T, RAW, ANY, true>(a, c, c.tile, ring, c.n_list % kRing, qg0);
     const int ticket = take_ticket<T>(a, c);
     __shared__ int s_last;
     if (threadIdx.x == 0) s_last = ticket == a.n_split - 1;
@@ -861,10 +912,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 }
 
+#ifndef LF_ATTN_GWG_TU
+// Compute units of the current device (cached per device).
+int cu_count() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) return cache[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) cache[dev] = n;
+  return n;
+}
+
 template <typename T>
-hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
-  const int n_tiles = (a.S + kTile - 1) / kTile;
-  const int64_t grid = (int64_t)a.B * a.H * n_tiles;
+hipError_t launch_t(const AttnArgs& args, hipStream_t st) {
+  const int n_tiles = (args.S + kTile - 1) / kTile;
+  const int64_t band = (int64_t)args.B * args.H * n_tiles;
+  // band tiles that leave CUs idle: the global rows of each (b, h) get a workgroup of
+  // their own (one split over all keys) that runs beside them
+  AttnArgs a = args;
+  const bool gwg = a.G > 0 && band + (int64_t)a.B * a.H <= cu_count();
+  if (gwg) {
+    a.n_split = 1;
+    a.split_len = (a.S + kBlk * kWaves - 1) / (kBlk * kWaves) * (kBlk * kWaves);
+  }
+  const int64_t grid = band + (gwg ? (int64_t)a.B * a.H : 0);
   if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (a.G > 0 && (a.split_len % (kBlk * kWaves) != 0 || a.n_split > n_tiles))
     return hipErrorInvalidConfiguration;
@@ -873,20 +946,38 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t st) {
     hipError_t e0 = hipEventRecord(a.ev_begin, st);
     if (e0 != hipSuccess) return e0;
   }
-  if (a.raw && a.any_pos)
-    attn_mfma_kernel<T, true, true><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles);
-  else if (a.raw)
-    attn_mfma_kernel<T, true, false><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles);
-  else
-    attn_mfma_kernel<T, false, false><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles);
+  if (gwg) {
+    // instantiated in a translation unit of its own (attn_mfma_gwg.hip), so that the
+    // code of the kernels below does not change with it
+    const hipError_t eg = launch_attention_gwg(a, n_tiles, (unsigned)grid, st);
+    if (eg != hipSuccess) return eg;
+  } else if (a.raw && a.any_pos) {
+    attn_mfma_kernel<T, true, true, false><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles);
+  } else if (a.raw) {
+    attn_mfma_kernel<T, true, false, false><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles);
+  } else {
+    attn_mfma_kernel<T, false, false, false><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.ev_end) e = hipEventRecord(a.ev_end, st);
   return e;
 }
+#else
+template <typename T>
+void launch_gwg_t(const AttnArgs& a, int n_tiles, unsigned grid, hipStream_t st) {
+  if (a.raw && a.any_pos)
+    attn_mfma_kernel<T, true, true, true><<<grid, kThreads, 0, st>>>(a, n_tiles);
+  else if (a.raw)
+    attn_mfma_kernel<T, true, false, true><<<grid, kThreads, 0, st>>>(a, n_tiles);
+  else
+    attn_mfma_kernel<T, false, false, true><<<grid, kThreads, 0, st>>>(a, n_tiles);
+}
+#endif
 
 }  // namespace
 
+#ifndef LF_ATTN_GWG_TU
 void attn_split_plan(int S, int* n_split, int* split_len) {
   // one split per 256-row tile, at most 32 splits per (b, h); splits are whole
   // rounds of 8 x 32 keys
@@ -906,5 +997,15 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   }
   return hipErrorInvalidValue;
 }
+
+#else
+hipError_t launch_attention_gwg(const AttnArgs& a, int n_tiles, unsigned grid, hipStream_t st) {
+  switch (a.dtype) {
+    case 1: launch_gwg_t<f16>(a, n_tiles, grid, st); return hipGetLastError();
+    case 2: launch_gwg_t<bf16>(a, n_tiles, grid, st); return hipGetLastError();
+  }
+  return hipErrorInvalidValue;
+}
+#endif
 
 }  // namespace lf

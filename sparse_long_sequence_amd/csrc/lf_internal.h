@@ -49,6 +49,9 @@ hipError_t launch_prep(int dtype, const void* global_mask, const void* local_mas
 hipError_t launch_mask_shift(int dtype, const void* local_mask, int64_t n, void* bias,
                              hipStream_t st);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
+// The attention kernel with one extra workgroup per (b, h) for the global rows (grid =
+// band tiles + B * H; a.n_split == 1): attn_mfma_gwg.hip.
+hipError_t launch_attention_gwg(const AttnArgs& a, int n_tiles, unsigned grid, hipStream_t st);
 hipError_t launch_attention_fp32(const AttnArgs& a, hipStream_t st);
 
 // Mask precondition check: writes 4 ints to `flags` (device): bad local value,
