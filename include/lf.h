@@ -33,6 +33,11 @@
  *    sequence; masks hold only the values above.  lf_check_masks verifies them,
  *    and setting the environment variable LF_DEBUG_CHECK=1 makes lf_attn_forward
  *    call it first.
+ *  - Work split (fp16 / bf16): when the band tiles (B * H * ceil(S / 256) workgroups)
+ *    plus B * H leave none of the device's CUs short, the global rows of each (b, h)
+ *    run in a workgroup of their own; otherwise they are split over the band tiles'
+ *    workgroups and merged by the last one.  The two differ only in rounding order.
+ *    LF_ATTN_NO_GWG=1 (read on every call) selects the second on every grid.
  *  - Return value: an lf_status.  LF_ERR_HIP means a HIP call failed while
  *    enqueuing; lf_last_error() (thread-local) holds the message.
  */

@@ -52,6 +52,8 @@
 // (coherent across XCDs without cache maintenance).  Then the workgroup takes an
 // atomic ticket; the one whose ticket completed the (b, h) reads all partials with
 // coherent loads, writes the global rows and resets the ticket.
+#include <cstdlib>
+
 #include "lf_device.h"
 #include "lf_internal.h"
 
@@ -932,7 +934,10 @@ hipError_t launch_t(const AttnArgs& args, hipStream_t st) {
   // band tiles that leave CUs idle: the global rows of each (b, h) get a workgroup of
   // their own (one split over all keys) that runs beside them
   AttnArgs a = args;
-  const bool gwg = a.G > 0 && band + (int64_t)a.B * a.H <= cu_count();
+  // LF_ATTN_NO_GWG=1 (read on every call) keeps the split path on small grids too
+  const char* no_gwg = getenv("LF_ATTN_NO_GWG");
+  const bool gwg = a.G > 0 && band + (int64_t)a.B * a.H <= cu_count() &&
+                   !(no_gwg && no_gwg[0] == '1');
   if (gwg) {
     a.n_split = 1;
     a.split_len = (a.S + kBlk * kWaves - 1) / (kBlk * kWaves) * (kBlk * kWaves);

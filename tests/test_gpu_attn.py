@@ -96,6 +96,18 @@ def test_attention_parity_mid(lf, dtype, case):
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}H{c[1]}S{c[2]}W{c[3]}G{c[4]}" for c in CASES])
+def test_attention_parity_mid_split_path(lf, dtype, case, monkeypatch):
+    # these grids leave CUs idle, so by default the global rows run in workgroups of
+    # their own; LF_ATTN_NO_GWG=1 sends them through the key-split path instead
+    monkeypatch.setenv("LF_ATTN_NO_GWG", "1")
+    B, H, S, W, G, pad, ng = case
+    inp = workloads.random_attention_inputs(zlib.crc32(repr(case).encode()) % 100000, B, H, S, W, G, dtype,
+                                            pad_frac=pad, n_global=ng)
+    _full_compare(lf, inp, W, G, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("std", [1.0, 2.0])
 def test_attention_stress_inputs(lf, dtype, std):
     # larger scores exercise the running-max updates and rescaling
