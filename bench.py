@@ -3,8 +3,11 @@
 
 Workload: the longformer-large-shaped problem (B=1, H=16 heads x 64, S=4096,
 window W=512 i.e. +-256, G=8 leading global tokens, fp16), seeded synthetic
-inputs already resident in HBM.  One step = one lf_attn_forward call: global
-index extraction, mask shift, band + global attention (every step of the path).
+inputs already resident in HBM.  One step = one lf_attn_forward call on the raw
+masks: one kernel launch that counts the leading global tokens from the global mask
+and tests keys against the local mask where it uses them (so the separate index and
+mask-shift kernels of the preprocessing entry points do not run), then the band and
+global-key scores, the masked online softmax, PV, the global rows and the output.
 
 Prints ONE JSON line on stdout.  After W warm-up steps and `--warmup-seconds` of
 further untimed steps (the GPU clocks ramp up over the first second of work), K
@@ -36,6 +39,7 @@ PEAK_FP16_TFLOPS = 2516.6        # MI355X dense fp16 MFMA: 256 CU x 4 SIMD x 102
 PEAK_HBM_GBS = 8000.0
 LAUNCHES_PER_STEP = 1            # lf_attn_forward on fp16 / bf16 inputs: one kernel launch
 KERNEL_SOURCES = ["sparse_long_sequence_amd/csrc/attn_mfma.hip",
+                  "sparse_long_sequence_amd/csrc/attn_mfma_gwg.hip",
                   "sparse_long_sequence_amd/csrc/lf_device.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_mfma_longformer_large_fp16_traffic.txt")
 
@@ -78,13 +82,17 @@ def stored_traffic():
 
 
 def cpu_baseline(inp, wl, budget_s: float):
-    """Time the float64 oracle (single-threaded) on rows of the workload until the
-    budget is spent; returns throughput in the metric's unit (TFLOP/s)."""
-    from threadpoolctl import threadpool_limits
+    """Time the float64 oracle on rows of the workload until the budget is spent, with
+    its BLAS using every core this process may run on; returns throughput in the
+    metric's unit (TFLOP/s)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import oracle
+    cores = len(os.sched_getaffinity(0))
     rows, flops, t_total, passes = 0, 0.0, 0.0, 0
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=cores):
+        blas = ",".join(sorted({f"{i.get('internal_api')} {i.get('version')} x{i.get('num_threads')}"
+                                for i in threadpool_info() if i.get("user_api") == "blas"}))
         # whole heads of batch 0 in blocks of 256 rows, head after head, starting
         # over at head 0 until the time budget is spent
         while t_total < budget_s:
@@ -98,11 +106,13 @@ def cpu_baseline(inp, wl, budget_s: float):
                 rows += len(rr)
                 flops += 256.0 * sum(row_pairs(s, wl.S, wl.W, wl.G) for (_, _, s) in rr)
             passes = rows / (wl.H * wl.S)
-    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{rows} query rows ({passes:.2f} passes over the {wl.H} x {wl.S} rows of "
                       f"batch 0) of the same workload, whole heads of {wl.S} rows, "
-                      f"{t_total:.1f} s of float64 numpy oracle time, BLAS limited to 1 thread",
-            "seconds": round(t_total, 2), "host_cpus": os.cpu_count()}
+                      f"{t_total:.1f} s of float64 numpy oracle time, BLAS threads = {cores} "
+                      f"(the process's CPU affinity; the oracle's per-row products are small, "
+                      f"so most of its time is single-threaded Python)",
+            "blas": blas, "seconds": round(t_total, 2), "host_cpus": os.cpu_count()}
 
 
 def main():
@@ -116,6 +126,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the oracle CPU baseline (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--trials", type=int, default=5,
+                    help="after the K timed steps, this many further trials of --trial-steps "
+                         "steps each; their median per-step time is reported beside the value")
+    ap.add_argument("--trial-steps", type=int, default=200)
     ap.add_argument("--cold-calls", type=int, default=20,
                     help="after the timed steps, time this many single steps each right after "
                          "a 512 MiB scrub write (caches cold; reported beside the value)")
@@ -169,6 +183,24 @@ def main():
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     n_k, k_ms = args.steps * LAUNCHES_PER_STEP, e0.elapsed_time(e1)
+    # secondary: 5 trials of 200 back-to-back steps, median per-step time
+    trial_ms = []
+    for _ in range(args.trials):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(args.trial_steps):
+            step()
+        t1.record()
+        torch.cuda.synchronize()
+        trial_ms.append(t0.elapsed_time(t1) / args.trial_steps)
+    trials = None
+    if trial_ms:
+        srt = sorted(trial_ms)
+        trials = {"n_trials": len(srt), "steps_per_trial": args.trial_steps,
+                  "ms_per_step_median": round(srt[len(srt) // 2], 6),
+                  "ms_per_step_min": round(srt[0], 6), "ms_per_step_max": round(srt[-1], 6)}
     # secondary: cold caches.  A 512 MiB fill evicts L2 and the 256 MiB Infinity Cache;
     # the events and the step are enqueued while the fill still runs, so the interval
     # holds only the step.
@@ -249,6 +281,8 @@ def main():
         "pct_mfma_peak": round(100.0 * tflops / PEAK_FP16_TFLOPS, 3),
         "roofline": roof,
     }
+    if trials is not None:
+        res["trials"] = trials
     if cold is not None:
         res["cold_cache"] = cold
     if not args.no_cpu_baseline and args.cpu_seconds > 0:

@@ -92,18 +92,34 @@ int lf_mask_shift(int dtype, const void* local_mask, int B, int S, void* local_b
  *   - any other row s is softmax over the live keys j with |j - s| <= W/2,
  *     j >= n_b, plus the live global keys j < n_b, of c <q[s], k[j]>, weighting
  *     v[j].  Global keys are therefore counted once.
- * Padding enters as the additive -10000 score bias of the mask shift.  fp16 / bf16:
- * one launch on MFMA with fp32 accumulation, reading both masks itself; its
- * global-row partials and split tickets live in one library-owned workspace per
- * (device, stream), allocated on first use and grown (after a stream
- * synchronisation) when a larger shape needs it, so concurrent calls must use
- * distinct streams.  fp32: the index extraction and mask shift into temporary
- * device memory (hipMallocAsync / hipFreeAsync on `stream`), then fp32 FMA.
+ * A padded key (local_mask 0) is excluded from every row.  The page adds the shifted
+ * mask (-10000) to its scores; exp(x - 10000) is exactly 0 in fp32 for any score a
+ * row with one live key can reach, so excluding the key gives the same result, and the
+ * kernels exclude it (-inf) instead of adding the bias.
+ * fp16 / bf16: one launch on MFMA with fp32 accumulation, reading both masks itself.
+ * fp32: the index extraction and mask shift, then the vector-ALU kernel.
+ * Scratch, per (device, stream), never waiting for the host: the split tickets of the
+ * global-row merge sit in a slot of a static device array (64 slots per device, one per
+ * stream that calls; zero-filled on the stream when the slot is handed out, left zero
+ * by every call); the global-row partials (and fp32's preprocessed masks) sit in a
+ * device buffer kept for the stream, allocated and, when a larger shape needs more,
+ * replaced with hipMallocAsync / hipFreeAsync on `stream` (stream-ordered: no host
+ * sync).  lf_release_stream_scratch frees that buffer.  Calls on one stream share its
+ * scratch (they run in order); calls on different streams do not.  While `stream` is
+ * being captured into a graph, a call uses neither: it allocates and frees its own
+ * scratch and tickets on the stream (capture-safe).
  */
 int lf_attn_forward(int dtype, const void* q, const void* k, const void* v,
                     const void* qg, const void* kg, const void* vg,
                     const void* local_mask, const void* global_mask,
                     int B, int H, int S, int W, int G, void* out, void* stream);
+
+/*
+ * Frees the scratch buffer lf_attn_forward / lf_attn_forward_any_globals keep for
+ * `stream` on the current device (stream-ordered: hipFreeAsync on `stream`, after the
+ * calls already enqueued there).  The next call on the stream allocates a new one.
+ */
+int lf_release_stream_scratch(void* stream);
 
 /*
  * Band + global attention with the global tokens at any positions (the global
@@ -119,10 +135,9 @@ int lf_attn_forward(int dtype, const void* q, const void* k, const void* v,
  *     in P_b, plus the live keys of P_b, of c <q[s], k[j]>, weighting v[j].
  * With leading global tokens this equals lf_attn_forward.  Two launches on `stream`:
  * the index extraction (as lf_init_global_idx) into library-owned device memory,
- * then the attention, which gathers the global keys through that index.  The
- * library keeps one workspace per (device, stream), allocated on first use and
- * grown when a larger shape needs it (that growth synchronises the stream), so
- * concurrent calls must use distinct streams.  Data-dependent preconditions (masks
+ * then the attention, which gathers the global keys through that index.  The index
+ * sits in the stream's scratch buffer, beside the partials (same scratch rules as
+ * lf_attn_forward).  Data-dependent preconditions (masks
  * 0/1 and 0/-10000, n_b <= G) are checked only by lf_check_masks or under
  * LF_DEBUG_CHECK=1, which here skips the head-of-sequence test.
  */
@@ -200,9 +215,14 @@ size_t lf_encoder_layer_workspace_bytes(int dtype, int B, int S, int hidden, int
  * tickets) must be zero before the first call that uses it (zero-fill it once after
  * allocating); every call leaves them zero.  The residual stream (x + projection,
  * h1) is kept in fp32; GEMM inputs are rounded to `dtype`.  Calls sharing a
- * workspace must not overlap in time.  Enqueues 8 to 9 launches on `stream` (the
- * global-query projection adds a reduction when it is split over K), no sync.  The
- * result does not depend on the split: partial sums are added in a fixed order.
+ * workspace must not overlap in time.  Enqueues 7 launches on `stream` (the
+ * global-query projection rides in the packed projection's launch), 8 when the masks
+ * are preprocessed inside the call (fp32), no sync.  The result does not depend on
+ * how a GEMM is split over K: partial sums are added in a fixed order.
+ * Weight layout: [out, in] (y = x W^T), so that both MFMA operands of every GEMM are
+ * contiguous along the reduction dimension; a caller holding [in, out] weights (the
+ * layout the page's plugin produces by transposing the model's weights) transposes
+ * them once at load time.
  */
 int lf_encoder_layer(int dtype, const lf_layer_weights* w, const void* x,
                      const void* local_mask, const void* global_mask, int B, int S,
@@ -251,7 +271,7 @@ size_t lf_encoder_forward_workspace_bytes(int dtype, int B, int S, int hidden, i
  * between y and an activation buffer in the workspace so that the last layer writes
  * y.  Same shape rules, dtype, precision and workspace convention as
  * lf_encoder_layer (ws_bytes >= lf_encoder_forward_workspace_bytes; its first bytes
- * zero before the first use, left zero).  Enqueues 1 + (8 to 9) * n_layers launches.
+ * zero before the first use, left zero).  Enqueues 1 + 7 * n_layers launches.
  */
 int lf_encoder_forward(int dtype, const lf_layer_weights* w, int n_layers, const void* x,
                        const void* local_mask, const void* global_mask, int B, int S,
@@ -269,7 +289,7 @@ int lf_encoder_forward(int dtype, const lf_layer_weights* w, int n_layers, const
  * other positions of the global-index partition; the attention never reads them),
  * and the attention is lf_attn_forward_any_globals'.  With leading global tokens the
  * result equals lf_encoder_layer / lf_encoder_forward.  The layer call runs the
- * global-index partition itself first (one more launch); the stack runs it once.
+ * global-index partition itself first (8 launches); the stack runs it once.
  */
 int lf_encoder_layer_any_globals(int dtype, const lf_layer_weights* w, const void* x,
                                  const void* local_mask, const void* global_mask, int B, int S,

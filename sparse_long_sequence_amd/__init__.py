@@ -20,7 +20,7 @@ __all__ = ["LFError", "library_path", "load_library", "init_global_idx", "mask_s
            "encoder_layer", "encoder_layer_workspace_bytes", "encoder_forward",
            "encoder_forward_workspace_bytes", "LAYER_WEIGHT_FIELDS",
            "ffn_block", "ffn_block_workspace_bytes",
-           "kernel_timing_start", "kernel_timing_stop",
+           "kernel_timing_start", "kernel_timing_stop", "release_stream_scratch",
            "EXPORTED_SYMBOLS", "dtype_code"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -42,6 +42,7 @@ EXPORTED_SYMBOLS = ["lf_init_global_idx", "lf_mask_shift", "lf_attn_forward",
                     "lf_encoder_forward_any_globals",
                     "lf_ffn_block_workspace_bytes", "lf_ffn_block",
                     "lf_kernel_timing_start", "lf_kernel_timing_stop",
+                    "lf_release_stream_scratch",
                     "lf_status_string", "lf_last_error"]
 
 
@@ -91,6 +92,7 @@ def load_library():
     lib.lf_ffn_block_workspace_bytes.restype = S
     lib.lf_ffn_block.argtypes = [I, P, P, P, P, P, P, P, P, I, I, I, ctypes.c_float, I, P, P, S,
                                  P]
+    lib.lf_release_stream_scratch.argtypes = [P]
     lib.lf_kernel_timing_start.argtypes = [I]
     lib.lf_kernel_timing_stop.argtypes = [ctypes.POINTER(ctypes.c_int),
                                           ctypes.POINTER(ctypes.c_double)]
@@ -103,7 +105,7 @@ def load_library():
                  "lf_attn_forward_pre", "lf_check_masks", "lf_encoder_layer",
                  "lf_encoder_forward", "lf_encoder_layer_any_globals",
                  "lf_encoder_forward_any_globals", "lf_ffn_block",
-                 "lf_kernel_timing_start", "lf_kernel_timing_stop"):
+                 "lf_kernel_timing_start", "lf_kernel_timing_stop", "lf_release_stream_scratch"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -240,6 +242,13 @@ def attn_forward_pre(q, k, v, qg, kg, vg, global_idx, global_count, local_bias, 
                                    _ptr(local_bias), B, H, S, W, G, _ptr(out), _ptr(workspace),
                                    workspace.numel() * workspace.element_size(), _stream(dev)))
     return out
+
+
+def release_stream_scratch(stream=None):
+    """Free the scratch buffer the attention entry points keep for `stream` (default: the
+    current stream of the current device); stream-ordered, no sync."""
+    st = stream if stream is not None else torch.cuda.current_stream()
+    _check(load_library().lf_release_stream_scratch(ctypes.c_void_p(st.cuda_stream)))
 
 
 def kernel_timing_start(capacity: int):

@@ -121,7 +121,7 @@ AttnWs attn_ws(int B, int H, int S, int G) {
 lf::AttnArgs make_args(int dtype, const void* q, const void* k, const void* v, const void* qg,
                        const void* kg, const void* vg, const int32_t* gidx, const int32_t* gcnt,
                        const void* bias, int B, int H, int S, int W, int G, void* out,
-                       char* workspace, const AttnWs& ws, size_t partials_off) {
+                       int* tickets, float* partials, const AttnWs& ws) {
   lf::AttnArgs a;
   a.dtype = dtype;
   a.raw = 0;
@@ -134,8 +134,8 @@ lf::AttnArgs make_args(int dtype, const void* q, const void* k, const void* v, c
   a.out_sb = (int64_t)H * S * 64;
   a.B = B; a.H = H; a.S = S; a.W = W; a.G = G;
   a.scale = 0.125f;
-  a.counters = (int*)workspace;
-  a.partials = (float*)(workspace + partials_off);
+  a.counters = tickets;
+  a.partials = partials;
   a.n_split = ws.n_split;
   a.split_len = ws.split_len;
   a.ev_begin = nullptr;
@@ -382,7 +382,8 @@ int run_layer(int dtype, const lf_layer_weights* w, const void* x, const LayerMa
   {
     AttnWs aw = attn_ws(B, H, S, G);
     lf::AttnArgs a = make_args(dtype, qkv[0], qkv[1], qkv[2], qg, qkv[3], qkv[4], gidx, gcnt,
-                               mbias, B, H, S, W, G, attn, ws, aw, aw.partials_off);
+                               mbias, B, H, S, W, G, attn, (int*)ws,
+                               (float*)(ws + aw.partials_off), aw);
     // fp16 / bf16: the MFMA kernel reads the raw masks (leading globals: itself; any
     // positions: with the index); fp32: the vector-ALU kernel reads the preprocessed
     // masks (and the global mask for any positions)
@@ -422,54 +423,66 @@ int run_layer(int dtype, const lf_layer_weights* w, const void* x, const LayerMa
   return LF_OK;
 }
 
-// Workspace of lf_attn_forward (fp16 / bf16), cached per (device, stream): the
-// split tickets [ticket_cap ints, zeroed when allocated and left zero by every
-// call] followed by the partial states.  Calls on one stream are ordered, so they
-// can share it; a call that needs more memory than the cache holds waits for the
-// stream, frees it and allocates a larger one (so the first calls on a stream
-// allocate, later ones do not).
-struct WsCache {
-  char* ptr = nullptr;
-  size_t ticket_cap = 0;   // ints
-  size_t part_bytes = 0;
-};
-std::mutex g_ws_mu;
-std::map<std::pair<int, hipStream_t>, WsCache> g_ws;
+// Scratch of lf_attn_forward / lf_attn_forward_any_globals, per (device, stream).
+//  - Split tickets (fp16 / bf16): one slot of kTicketsPerSlot ints of a static device
+//    array per (device, stream).  A slot is zero-filled on its stream when it is handed
+//    out and every call leaves its tickets zero again, so the calls of one stream,
+//    which run in order, share it with no fill.
+//  - The rest (global-row partials, the index of the globals-anywhere mode, fp32's
+//    preprocessed masks): one device buffer per (device, stream), allocated and, when a
+//    call needs more, replaced with stream-ordered hipMallocAsync / hipFreeAsync on that
+//    stream, so no call waits for the host.  A per-call allocation and free cost ~2 us
+//    per call at the longformer-large shape; the buffer is released by
+//    lf_release_stream_scratch or at process end.
+// A call holds the lock from the lookup until its kernels are enqueued: a concurrent
+// call on the same stream that replaces the buffer enqueues its free after them.
+// Streams being captured into a graph get neither: their calls bring their own
+// stream-ordered scratch and zero-filled tickets (capture-safe), freed in the graph.
+constexpr int kTicketSlots = 64;
+constexpr int kTicketsPerSlot = 8192;
+static __device__ __align__(256) int g_stream_tickets[kTicketSlots * kTicketsPerSlot];
 
-int cached_workspace(hipStream_t st, size_t tickets, size_t part_bytes, char** base,
-                     size_t* part_off) {
+struct StreamScratch {
+  int* tickets = nullptr;   // the stream's ticket slot (nullptr: none left)
+  char* buf = nullptr;      // cached scratch buffer
+  size_t bytes = 0;
+};
+struct DeviceScratch {
+  int* base = nullptr;      // device address of g_stream_tickets on that device
+  int slots_used = 0;
+  std::map<hipStream_t, StreamScratch> streams;
+};
+std::mutex g_scratch_mu;
+std::map<int, DeviceScratch> g_scratch;
+
+// The (device, stream) entry, its ticket slot assigned (and zero-filled on st) on first
+// use; call with g_scratch_mu held.
+int stream_entry(hipStream_t st, StreamScratch** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  std::lock_guard<std::mutex> lock(g_ws_mu);
-  WsCache& w = g_ws[std::make_pair(dev, st)];
-  if (!w.ptr || w.ticket_cap < tickets || w.part_bytes < part_bytes) {
-    if (w.ptr) {
-      e = hipStreamSynchronize(st);
-      if (e != hipSuccess) return hip_fail(e, "workspace resize (stream sync)");
-      (void)hipFree(w.ptr);
-      w = WsCache();
-    }
-    const size_t cap = tickets < 1024 ? 1024 : tickets;
-    const size_t pb = part_bytes < 65536 ? 65536 : part_bytes;
-    const size_t bytes = align256(cap * sizeof(int)) + pb;
-    char* p = nullptr;
-    e = hipMalloc((void**)&p, bytes);
-    if (e != hipSuccess) return hip_fail(e, "workspace allocation");
-    e = hipMemsetAsync(p, 0, bytes, st);
-    if (e != hipSuccess) {
-      (void)hipFree(p);
-      return hip_fail(e, "workspace zero-fill");
-    }
-    w.ptr = p;
-    w.ticket_cap = cap;
-    w.part_bytes = pb;
+  DeviceScratch& D = g_scratch[dev];
+  if (!D.base) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_stream_tickets));
+    if (e != hipSuccess) return hip_fail(e, "ticket slots (hipGetSymbolAddress)");
+    D.base = (int*)p;
   }
-  *base = w.ptr;
-  *part_off = align256(w.ticket_cap * sizeof(int));
+  auto it = D.streams.find(st);
+  if (it == D.streams.end()) {
+    StreamScratch ss;
+    if (D.slots_used < kTicketSlots) {
+      int* p = D.base + (size_t)D.slots_used * kTicketsPerSlot;
+      e = lf::launch_fill_i32(p, kTicketsPerSlot, 0, st);
+      if (e != hipSuccess) return hip_fail(e, "ticket slot zero-fill");
+      ++D.slots_used;
+      ss.tickets = p;
+    }
+    it = D.streams.emplace(st, ss).first;
+  }
+  *out = &it->second;
   return LF_OK;
 }
-
 
 bool debug_check_enabled() {
   const char* e = getenv("LF_DEBUG_CHECK");
@@ -539,7 +552,8 @@ int lf_attn_forward_pre(int dtype, const void* q, const void* k, const void* v, 
   if (((uintptr_t)workspace) & 255)
     return fail(LF_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
   lf::AttnArgs a = make_args(dtype, q, k, v, qg, kg, vg, global_idx, global_count, local_bias, B,
-                             H, S, W, G, out, (char*)workspace, ws, ws.partials_off);
+                             H, S, W, G, out, (int*)workspace,
+                             (float*)((char*)workspace + ws.partials_off), ws);
   hipError_t he = run_attention(a, (hipStream_t)stream);
   if (he != hipSuccess) return hip_fail(he, "lf_attn_forward_pre");
   return ok();
@@ -548,6 +562,88 @@ int lf_attn_forward_pre(int dtype, const void* q, const void* k, const void* v, 
 }  // extern "C"
 
 namespace {
+
+// Scratch of one lf_attn_forward-family call, as offsets into one region.  fp16 /
+// bf16: [tickets (with_tickets)][global-row partials (G > 0)][index, count (any_pos)];
+// fp32: [index][count][shifted mask] (the vector-ALU kernel reads preprocessed masks).
+struct AttnScratch {
+  size_t tickets_off, partials_off, idx_off, cnt_off, bias_off, total;
+};
+
+AttnScratch attn_scratch(int dtype, int B, int H, int S, int G, bool any_pos, bool with_tickets) {
+  AttnScratch c;
+  size_t off = 0;
+  const size_t n_bs = (size_t)B * S;
+  c.tickets_off = c.partials_off = c.idx_off = c.cnt_off = c.bias_off = 0;
+  if (dtype == LF_F32) {
+    c.idx_off = off; off += align256(n_bs * sizeof(int32_t));
+    c.cnt_off = off; off += align256((size_t)B * sizeof(int32_t));
+    c.bias_off = off; off += align256(n_bs * dtype_size(dtype));
+    c.total = off;
+    return c;
+  }
+  if (with_tickets && G > 0) {
+    c.tickets_off = off;
+    off += align256((size_t)B * H * sizeof(int));
+  }
+  if (G > 0) {
+    const AttnWs w = attn_ws(B, H, S, G);
+    c.partials_off = off;
+    off += w.total - w.partials_off;
+  }
+  if (any_pos) {
+    c.idx_off = off; off += align256(n_bs * sizeof(int32_t));
+    c.cnt_off = off; off += align256((size_t)B * sizeof(int32_t));
+  }
+  c.total = off;
+  return c;
+}
+
+// The launches of lf_attn_forward (any_pos = false) / lf_attn_forward_any_globals
+// (any_pos = true) into a given scratch region (layout sc) with given split tickets
+// (zero on entry, left zero; fp16 / bf16 with G > 0 only).  fp16 / bf16, leading
+// globals: one launch, the kernel reads both masks itself (count of the leading global
+// tokens, live-key test of the local mask); globals anywhere: the index partition
+// first, then the kernel, which gathers the global keys through it.  fp32: the
+// preprocessing kernel, then the vector-ALU kernel.
+hipError_t run_attn_forward(int dtype, const void* q, const void* k, const void* v,
+                            const void* qg, const void* kg, const void* vg,
+                            const void* local_mask, const void* global_mask, int B, int H, int S,
+                            int W, int G, void* out, hipStream_t st, bool any_pos, char* scratch,
+                            const AttnScratch& sc, const AttnWs& ws, int* tickets) {
+  int32_t* gidx = nullptr;
+  int32_t* gcnt = nullptr;
+  void* bias = nullptr;
+  float* partials = nullptr;
+  if (dtype == LF_F32) {
+    gidx = (int32_t*)(scratch + sc.idx_off);
+    gcnt = (int32_t*)(scratch + sc.cnt_off);
+    bias = scratch + sc.bias_off;
+    hipError_t he = lf::launch_prep(dtype, global_mask, local_mask, B, S, gidx, gcnt, bias,
+                                    nullptr, 0, st);
+    if (he != hipSuccess) return he;
+    lf::AttnArgs a = make_args(dtype, q, k, v, qg, kg, vg, gidx, gcnt, bias, B, H, S, W, G, out,
+                               nullptr, nullptr, ws);
+    a.any_pos = any_pos ? 1 : 0;
+    a.global_mask = global_mask;
+    return run_attention(a, st);
+  }
+  if (G > 0) partials = (float*)(scratch + sc.partials_off);
+  if (any_pos) {
+    gidx = (int32_t*)(scratch + sc.idx_off);
+    gcnt = (int32_t*)(scratch + sc.cnt_off);
+    hipError_t he = lf::launch_prep(dtype, global_mask, nullptr, B, S, gidx, gcnt, nullptr,
+                                    nullptr, 0, st);
+    if (he != hipSuccess) return he;
+  }
+  lf::AttnArgs a = make_args(dtype, q, k, v, qg, kg, vg, gidx, gcnt, nullptr, B, H, S, W, G, out,
+                             tickets, partials, ws);
+  a.raw = 1;
+  a.any_pos = any_pos ? 1 : 0;
+  a.local_mask = local_mask;
+  a.global_mask = global_mask;
+  return run_attention(a, st);
+}
 
 // The mask precondition check; leading: the global tokens must also be contiguous at
 // the head of the sequence (lf_attn_forward), not when they may sit anywhere.
@@ -603,65 +699,108 @@ int attn_forward_impl(int dtype, const void* q, const void* k, const void* v, co
       return e;
   }
   const AttnWs ws = attn_ws(B, H, S, G);
-  if (dtype != LF_F32) {
-    // leading globals: one launch, the kernel reads both masks itself (count of the
-    // leading global tokens, live-key test of the local mask).  Globals anywhere: the
-    // index partition first (into the cached workspace, after the partials), then
-    // the kernel, which gathers the global keys through it.
-    char* base = nullptr;
-    size_t part_off = 0;
-    const size_t part_bytes = ws.total - ws.partials_off;
-    const size_t idx_bytes = any_pos ? align256((size_t)B * S * sizeof(int32_t)) +
-                                           align256((size_t)B * sizeof(int32_t))
-                                     : 0;
-    if (int e = cached_workspace(st, (size_t)B * H, part_bytes + idx_bytes, &base, &part_off))
-      return e;
-    int32_t* gidx = nullptr;
-    int32_t* gcnt = nullptr;
-    if (any_pos) {
-      gidx = (int32_t*)(base + part_off + part_bytes);
-      gcnt = (int32_t*)(base + part_off + part_bytes + align256((size_t)B * S * sizeof(int32_t)));
-      hipError_t he = lf::launch_prep(dtype, global_mask, nullptr, B, S, gidx, gcnt, nullptr,
-                                      nullptr, 0, st);
-      if (he != hipSuccess) return hip_fail(he, "lf_attn_forward_any_globals index");
-    }
-    lf::AttnArgs a = make_args(dtype, q, k, v, qg, kg, vg, gidx, gcnt, nullptr, B, H, S, W, G, out,
-                               base, ws, part_off);
-    a.raw = 1;
-    a.any_pos = any_pos ? 1 : 0;
-    a.local_mask = local_mask;
-    a.global_mask = global_mask;
-    hipError_t he = run_attention(a, st);
-    if (he != hipSuccess) return hip_fail(he, "lf_attn_forward");
+  const bool need_tickets = dtype != LF_F32 && G > 0;
+  const char* who = any_pos ? "lf_attn_forward_any_globals" : "lf_attn_forward";
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  hipError_t he = hipStreamIsCapturing(st, &cap);
+  if (he != hipSuccess) return hip_fail(he, "hipStreamIsCapturing");
+  if (cap != hipStreamCaptureStatusNone) {
+    // under capture: scratch and zero-filled tickets of this call alone
+    const AttnScratch sc = attn_scratch(dtype, B, H, S, G, any_pos, true);
+    char* scratch = nullptr;
+    if (sc.total > 0 && (he = hipMallocAsync((void**)&scratch, sc.total, st)) != hipSuccess)
+      return hip_fail(he, "attention scratch (hipMallocAsync)");
+    int* tickets = need_tickets ? (int*)(scratch + sc.tickets_off) : nullptr;
+    if (need_tickets) he = lf::launch_fill_i32(tickets, (int64_t)B * H, 0, st);
+    if (he == hipSuccess)
+      he = run_attn_forward(dtype, q, k, v, qg, kg, vg, local_mask, global_mask, B, H, S, W, G,
+                            out, st, any_pos, scratch, sc, ws, tickets);
+    const hipError_t he2 = scratch ? hipFreeAsync(scratch, st) : hipSuccess;
+    if (he != hipSuccess) return hip_fail(he, who);
+    if (he2 != hipSuccess) return hip_fail(he2, "attention scratch (hipFreeAsync)");
     return ok();
   }
-  // fp32: preprocessing kernel, then the vector-ALU attention kernel
-  const size_t n_bs = (size_t)B * S;
-  const size_t off_idx = 0;
-  const size_t off_cnt = align256(off_idx + n_bs * sizeof(int32_t));
-  const size_t off_bias = align256(off_cnt + (size_t)B * sizeof(int32_t));
-  const size_t total = align256(off_bias + n_bs * dtype_size(dtype));
-  char* scratch = nullptr;
-  hipError_t he = hipMallocAsync((void**)&scratch, total, st);
-  if (he != hipSuccess) return hip_fail(he, "lf_attn_forward scratch");
-  int32_t* gidx = (int32_t*)(scratch + off_idx);
-  int32_t* gcnt = (int32_t*)(scratch + off_cnt);
-  void* bias = scratch + off_bias;
-  he = lf::launch_prep(dtype, global_mask, local_mask, B, S, gidx, gcnt, bias, nullptr, 0, st);
-  if (he == hipSuccess) {
-    lf::AttnArgs a = make_args(dtype, q, k, v, qg, kg, vg, gidx, gcnt, bias, B, H, S, W, G, out,
-                               nullptr, ws, 0);
-    a.any_pos = any_pos ? 1 : 0;
-    a.global_mask = global_mask;
-    he = run_attention(a, st);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  StreamScratch* ss = nullptr;
+  if (int e = stream_entry(st, &ss)) return e;
+  // the stream's ticket slot when it has one and it is large enough, else tickets in
+  // the scratch buffer (zero-filled by this call)
+  const bool slot = need_tickets && ss->tickets && (int64_t)B * H <= kTicketsPerSlot;
+  const AttnScratch sc = attn_scratch(dtype, B, H, S, G, any_pos, need_tickets && !slot);
+  if (sc.total > ss->bytes) {
+    if (ss->buf && (he = hipFreeAsync(ss->buf, st)) != hipSuccess)
+      return hip_fail(he, "attention scratch (hipFreeAsync)");
+    ss->buf = nullptr;
+    ss->bytes = 0;
+    if ((he = hipMallocAsync((void**)&ss->buf, sc.total, st)) != hipSuccess)
+      return hip_fail(he, "attention scratch (hipMallocAsync)");
+    ss->bytes = sc.total;
   }
-  hipError_t he2 = hipFreeAsync(scratch, st);
-  if (he != hipSuccess) return hip_fail(he, "lf_attn_forward");
-  if (he2 != hipSuccess) return hip_fail(he2, "lf_attn_forward free");
+  int* tickets = nullptr;
+  if (slot) {
+    tickets = ss->tickets;
+  } else if (need_tickets) {
+    tickets = (int*)(ss->buf + sc.tickets_off);
+    if ((he = lf::launch_fill_i32(tickets, (int64_t)B * H, 0, st)) != hipSuccess)
+      return hip_fail(he, who);
+  }
+  he = run_attn_forward(dtype, q, k, v, qg, kg, vg, local_mask, global_mask, B, H, S, W, G, out,
+                        st, any_pos, ss->buf, sc, ws, tickets);
+  if (he != hipSuccess) return hip_fail(he, who);
   return ok();
 }
 
 }  // namespace
+
+namespace lf {
+
+size_t attn_forward_scratch_bytes(int dtype, int B, int H, int S, int G) {
+  return attn_scratch(dtype, B, H, S, G, false, false).total;
+}
+
+int attn_forward_validate(int dtype, const void* q, const void* k, const void* v,
+                          const void* qg, const void* kg, const void* vg, const void* local_mask,
+                          const void* global_mask, int B, int H, int S, int W, int G,
+                          const void* out, size_t scratch_bytes, int ticket_capacity,
+                          const char* who) {
+  if (int e = validate_attn(dtype, B, H, S, W, G)) return e;
+  if (int e = null_check("q,k,v,kg,vg,local_mask,global_mask,out",
+                         {q, k, v, kg, vg, local_mask, global_mask, out}))
+    return e;
+  if (G > 0 && !qg) return fail(LF_ERR_INVALID_ARGUMENT, "null pointer: qg (G > 0)");
+  const size_t need = attn_scratch(dtype, B, H, S, G, false, false).total;
+  if (need > scratch_bytes)
+    return fail(LF_ERR_UNSUPPORTED, "%s: this shape needs %zu bytes of scratch, more than the %zu "
+                "available", who, need, scratch_bytes);
+  if (dtype != LF_F32 && G > 0 && (int64_t)B * H > ticket_capacity)
+    return fail(LF_ERR_UNSUPPORTED, "%s: B*H = %lld exceeds the %d split tickets available", who,
+                (long long)B * H, ticket_capacity);
+  return LF_OK;
+}
+
+int attn_forward_in(int dtype, const void* q, const void* k, const void* v, const void* qg,
+                    const void* kg, const void* vg, const void* local_mask,
+                    const void* global_mask, int B, int H, int S, int W, int G, void* out,
+                    void* stream, char* scratch, size_t scratch_bytes, int* tickets,
+                    int ticket_capacity, const char* who) {
+  if (int e = attn_forward_validate(dtype, q, k, v, qg, kg, vg, local_mask, global_mask, B, H, S,
+                                    W, G, out, scratch_bytes, ticket_capacity, who))
+    return e;
+  hipStream_t st = (hipStream_t)stream;
+  if (debug_check_enabled()) {
+    if (int e = check_masks_impl(dtype, local_mask, global_mask, B, S, G, stream, true)) return e;
+  }
+  const AttnScratch sc = attn_scratch(dtype, B, H, S, G, false, false);
+  const hipError_t he = run_attn_forward(dtype, q, k, v, qg, kg, vg, local_mask, global_mask, B,
+                                         H, S, W, G, out, st, false, scratch, sc,
+                                         attn_ws(B, H, S, G), tickets);
+  if (he != hipSuccess) return hip_fail(he, who);
+  return ok();
+}
+
+int set_error(int code, const char* msg) { return fail(code, "%s", msg); }
+
+}  // namespace lf
 
 extern "C" {
 
@@ -684,6 +823,23 @@ int lf_attn_forward_any_globals(int dtype, const void* q, const void* k, const v
                                 int S, int W, int G, void* out, void* stream) {
   return attn_forward_impl(dtype, q, k, v, qg, kg, vg, local_mask, global_mask, B, H, S, W, G,
                            out, stream, true);
+}
+
+int lf_release_stream_scratch(void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  auto d = g_scratch.find(dev);
+  if (d == g_scratch.end()) return ok();
+  auto it = d->second.streams.find(st);
+  if (it == d->second.streams.end() || !it->second.buf) return ok();
+  e = hipFreeAsync(it->second.buf, st);
+  it->second.buf = nullptr;
+  it->second.bytes = 0;
+  if (e != hipSuccess) return hip_fail(e, "lf_release_stream_scratch");
+  return ok();
 }
 
 int lf_kernel_timing_start(int capacity) {

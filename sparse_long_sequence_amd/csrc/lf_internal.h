@@ -34,6 +34,27 @@ struct AttnArgs {
   hipEvent_t ev_end;
 };
 
+// lf_attn_forward's computation in memory the caller provides (lf_api.hip): `scratch`
+// (device, 256-byte aligned, scratch_bytes >= attn_forward_scratch_bytes) holds the
+// global-row partials (fp16 / bf16) or the preprocessed masks (fp32); `tickets` (device,
+// ticket_capacity ints, zero on entry and left zero) the split tickets.  Validates the
+// arguments as lf_attn_forward does; returns an lf_status, with the message for
+// lf_last_error() naming `who`.
+size_t attn_forward_scratch_bytes(int dtype, int B, int H, int S, int G);
+// The argument checks of attn_forward_in alone (nothing is enqueued).
+int attn_forward_validate(int dtype, const void* q, const void* k, const void* v,
+                          const void* qg, const void* kg, const void* vg, const void* local_mask,
+                          const void* global_mask, int B, int H, int S, int W, int G,
+                          const void* out, size_t scratch_bytes, int ticket_capacity,
+                          const char* who);
+int attn_forward_in(int dtype, const void* q, const void* k, const void* v, const void* qg,
+                    const void* kg, const void* vg, const void* local_mask,
+                    const void* global_mask, int B, int H, int S, int W, int G, void* out,
+                    void* stream, char* scratch, size_t scratch_bytes, int* tickets,
+                    int ticket_capacity, const char* who);
+// Records a failure for lf_last_error(); returns code.
+int set_error(int code, const char* msg);
+
 // Floats per global-row partial state: m (scaled log2 units), l, 2 pad, o[64].
 constexpr int kPartPitch = 68;
 
@@ -48,6 +69,8 @@ hipError_t launch_prep(int dtype, const void* global_mask, const void* local_mas
                        int tickets_per_row, hipStream_t st);
 hipError_t launch_mask_shift(int dtype, const void* local_mask, int64_t n, void* bias,
                              hipStream_t st);
+// n ints at p set to v, one launch (no memset node).
+hipError_t launch_fill_i32(int* p, int64_t n, int v, hipStream_t st);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
 // The attention kernel with one extra workgroup per (b, h) for the global rows (grid =
 // band tiles + B * H; a.n_split == 1): attn_mfma_gwg.hip.

@@ -158,6 +158,13 @@ __global__ __launch_bounds__(256) void check_masks_kernel(const T* __restrict__ 
   }
 }
 
+// n ints set to v (a kernel rather than hipMemsetAsync, so that a caller may capture
+// it in a graph).
+__global__ __launch_bounds__(256) void fill_i32_kernel(int* __restrict__ p, int64_t n, int v) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = v;
+}
+
 template <typename T>
 hipError_t prep_t(const void* g, const void* l, int B, int S, int32_t* idx, int32_t* cnt,
                   void* bias, int* tickets, int tickets_per_row, hipStream_t st) {
@@ -201,6 +208,14 @@ hipError_t launch_prep(int dtype, const void* global_mask, const void* local_mas
     case 2: return prep_t<bf16>(global_mask, local_mask, B, S, gidx, gcnt, bias, tickets, tickets_per_row, st);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_fill_i32(int* p, int64_t n, int v, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  fill_i32_kernel<<<(int)blocks, 256, 0, st>>>(p, n, v);
+  return hipGetLastError();
 }
 
 hipError_t launch_mask_shift(int dtype, const void* local_mask, int64_t n, void* bias,

@@ -7,6 +7,9 @@
     python sparse_long_sequence_amd/perf.py stack [--iters N] [--dtype fp16|bf16|fp32]
     python sparse_long_sequence_amd/perf.py ffn   [--iters N]   # FFN block, both paths
                                            # one encoder layer / the 24-layer encoder, B1 S1024
+    python sparse_long_sequence_amd/perf.py table  # the five workloads: warm and cold time
+    Any op: --calibrate-copy-mb N ends the run with one plain elementwise copy of N MiB
+    (fp32 in, fp32 out), the known size HBM counters are scaled by.
 
 Prints one JSON line per run: time per call (HIP events on the current stream around
 N back-to-back calls after a warm-up) and the algorithmic throughput.  This is the
@@ -225,10 +228,106 @@ def run_ffn(iters: int, warmup: int, dtype: str = "fp16") -> dict:
     return res
 
 
+def _time_trials(fn, trials: int, calls: int) -> float:
+    """Median over `trials` of the per-call time of `calls` back-to-back calls (after a
+    second of untimed calls, so the clocks have ramped up)."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < 1.0:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+    res = []
+    for _ in range(trials):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(calls):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res.append(e0.elapsed_time(e1) / calls)
+    return sorted(res)[len(res) // 2]
+
+
+def _time_cold(fn, calls: int) -> float:
+    """Median time of `calls` single calls, each enqueued right after a 512 MiB fill that
+    evicts L2 and the Infinity Cache (the interval holds only the call)."""
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    res = []
+    for i in range(calls):
+        scrub.fill_(i & 0xff)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res.append(e0.elapsed_time(e1))
+    del scrub
+    return sorted(res)[len(res) // 2]
+
+
+PEAK = {"fp16": 2516.6, "bf16": 2516.6, "fp32": 157.3}   # dense MFMA TFLOP/s (fp32: FMA)
+
+
+def run_table() -> list:
+    """The five workloads (tiny fp32, longformer-large fp16, padded fp16, long bf16, the
+    fp16 encoder layer): warm time (median of 5 trials of back-to-back calls), cold time
+    (median of 20 calls after a cache scrub), algorithmic TFLOP/s and GB/s."""
+    out = []
+    for wl in workloads.ATTN_WORKLOADS:
+        inp = workloads.make_attention_inputs(wl)
+        g = {n: t.cuda() for n, t in inp.items()}
+        o = torch.empty_like(g["q"])
+        fn = lambda: lf.attn_forward(g["q"], g["k"], g["v"], g["qg"], g["kg"], g["vg"],
+                                     g["local_mask"], g["global_mask"], wl.W, wl.G, out=o)
+        warm = _time_trials(fn, 5, 200)
+        cold = _time_cold(fn, 20)
+        flops = 256.0 * oracle_free_pairs(inp["local_mask"], inp["global_mask"], wl.W) * wl.H
+        nbytes = sum(t.numel() * t.element_size() for t in inp.values()) + o.numel() * o.element_size()
+        out.append({"workload": wl.name, "ms_warm": warm, "ms_cold": cold,
+                    "tflops": flops / (warm * 1e-3) / 1e12,
+                    "pct_peak": 100.0 * flops / (warm * 1e-3) / 1e12 / PEAK[wl.dtype],
+                    "peak_tflops": PEAK[wl.dtype], "alg_gbs": nbytes / (warm * 1e-3) / 1e9,
+                    "alg_bytes": nbytes, "alg_gflop": flops / 1e9})
+        del g, o
+    wl = workloads.LAYER_FP16
+    t = workloads.make_layer_inputs(wl)
+    x = t["x"].cuda()
+    w = {n: t[n].cuda() for n in lf.LAYER_WEIGHT_FIELDS}
+    lm, gm = t["local_mask"].cuda(), t["global_mask"].cuda()
+    y = torch.empty_like(x)
+    nb = lf.encoder_layer_workspace_bytes(x.dtype, wl.B, wl.S, wl.hidden, wl.H, wl.ffn, wl.W, wl.G)
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    fn = lambda: lf.encoder_layer(x, w, lm, gm, wl.H, wl.W, wl.G, out=y, workspace=ws)
+    warm = _time_trials(fn, 5, 20)
+    cold = _time_cold(fn, 20)
+    M, D, F, G, S, W = wl.B * wl.S, wl.hidden, wl.ffn, wl.G, wl.S, wl.W
+    gemm = 2.0 * M * D * (5 * D + D + 2 * F) + 2.0 * wl.B * G * D * D
+    pairs = G * S + (S - G) * (W + 1 + G) - (W // 2) * (W // 2 + 1)
+    flops = gemm + 256.0 * pairs * wl.B * wl.H
+    out.append({"workload": wl.name, "ms_warm": warm, "ms_cold": cold,
+                "tflops": flops / (warm * 1e-3) / 1e12,
+                "pct_peak": 100.0 * flops / (warm * 1e-3) / 1e12 / PEAK["fp16"],
+                "peak_tflops": PEAK["fp16"], "alg_gflop": flops / 1e9})
+    return out
+
+
+def calibrate_copy(mib: int):
+    """One plain elementwise copy of `mib` MiB (fp32 read, fp32 written)."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("op", choices=["attn", "attn_any", "prep", "layer", "stack", "ffn"])
+    ap.add_argument("op", choices=["attn", "attn_any", "prep", "layer", "stack", "ffn", "table"])
     ap.add_argument("--iters", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--dtype", default="fp16", choices=["fp16", "bf16", "fp32"],
@@ -237,21 +336,25 @@ def main():
                     help="attn only: longformer-large, padded (B4 H12 G32) or long (bf16 S16384)")
     ap.add_argument("--any-globals", action="store_true",
                     help="layer only: globals spread over the sequence, general entry point")
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="end with one plain elementwise copy of this many MiB (counter scaling)")
     a = ap.parse_args()
     if a.op == "layer":
         print(json.dumps(run_layer(a.iters, a.warmup, a.dtype, a.any_globals)), flush=True)
-        return
-    if a.op == "stack":
+    elif a.op == "stack":
         print(json.dumps(run_stack(a.iters, a.warmup, a.dtype)), flush=True)
-        return
-    if a.op == "ffn":
+    elif a.op == "ffn":
         print(json.dumps(run_ffn(a.iters, a.warmup, a.dtype)), flush=True)
-        return
-    if a.op == "attn":
+    elif a.op == "attn":
         print(json.dumps(run_attn(a.iters, a.warmup, a.shape)), flush=True)
-        return
-    fn = {"attn_any": run_attn_any, "prep": run_prep}[a.op]
-    print(json.dumps(fn(a.iters, a.warmup)), flush=True)
+    elif a.op == "table":
+        for r in run_table():
+            print(json.dumps(r), flush=True)
+    else:
+        fn = {"attn_any": run_attn_any, "prep": run_prep}[a.op]
+        print(json.dumps(fn(a.iters, a.warmup)), flush=True)
+    if a.calibrate_copy_mb > 0:
+        calibrate_copy(a.calibrate_copy_mb)
 
 
 if __name__ == "__main__":

@@ -13,6 +13,7 @@ import torch
 
 import oracle
 import workloads
+from parity import report
 
 pytestmark = pytest.mark.gpu
 
@@ -56,15 +57,15 @@ def _positions(seed, B, S, n, live_len=None):
     return out
 
 
-def _compare_full(lf, inp, W, G, dtype):
+def _compare_full(lf, inp, W, G, dtype, case="any"):
     g = _gpu(inp)
     out = _run_any(lf, g, W, G)
     torch.cuda.synchronize()
     got = out.cpu()
     assert torch.isfinite(got.float()).all()
     ref = _oracle(inp, W, G)
-    err = np.abs(got.double().numpy() - ref)
-    assert err.max() <= TOL[dtype], f"max abs err {err.max():.3e} (tol {TOL[dtype]})"
+    err = report(f"{case} {dtype}", got.double().numpy(), ref, TOL[dtype])
+    assert err <= TOL[dtype], f"max abs err {err:.3e} (tol {TOL[dtype]})"
     live = (inp["local_mask"] == 1).numpy()
     o = got.float().numpy()
     for b in range(o.shape[0]):
@@ -107,9 +108,7 @@ SCATTER_CASES = [
 ]
 
 
-@pytest.mark.parametrize("dtype", ["fp16", "bf16", "fp32"])
-@pytest.mark.parametrize("ci", range(len(SCATTER_CASES)))
-def test_scattered_globals_full_output(lf, dtype, ci):
+def _scatter_inputs(ci, dtype):
     B, H, S, W, G, pos, pad = SCATTER_CASES[ci]
     seed = 900 + ci
     if isinstance(pos, tuple):
@@ -122,7 +121,25 @@ def test_scattered_globals_full_output(lf, dtype, ci):
             pos = _positions(seed, B, S, pos[1])
     inp = workloads.random_attention_inputs(seed, B, H, S, W, G, dtype, pad_frac=pad,
                                             global_positions=pos)
-    _compare_full(lf, inp, W, G, dtype)
+    return inp, W, G
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16", "fp32"])
+@pytest.mark.parametrize("ci", range(len(SCATTER_CASES)))
+def test_scattered_globals_full_output(lf, dtype, ci):
+    inp, W, G = _scatter_inputs(ci, dtype)
+    _compare_full(lf, inp, W, G, dtype, f"scatter {ci}")
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("ci", range(len(SCATTER_CASES)))
+def test_scattered_globals_full_output_split_path(lf, dtype, ci, monkeypatch):
+    # these grids leave CUs idle, so by default the global rows run in workgroups of
+    # their own; LF_ATTN_NO_GWG=1 sends them through the key-split path (gathered
+    # global-key entries, split rounds, ticketed combine writing through the index)
+    monkeypatch.setenv("LF_ATTN_NO_GWG", "1")
+    inp, W, G = _scatter_inputs(ci, dtype)
+    _compare_full(lf, inp, W, G, dtype, f"scatter-split {ci}")
 
 
 def test_scattered_globals_stress_scale_fp16(lf):
@@ -131,13 +148,14 @@ def test_scattered_globals_stress_scale_fp16(lf):
     pos = _positions(77, B, S, G)
     inp = workloads.random_attention_inputs(77, B, H, S, W, G, "fp16", std=1.0,
                                             global_positions=pos)
-    _compare_full(lf, inp, W, G, "fp16")
+    _compare_full(lf, inp, W, G, "fp16", "scatter stress std1")
 
 
-def test_scattered_globals_longformer_large_shape_sampled_rows(lf):
+def test_scattered_globals_longformer_large_shape_every_element(lf):
     # the benchmark shape (B=1 H=16 S=4096 W=512 G=8 fp16) with the 8 global tokens
-    # spread over the sequence; every global row, the rows around each global token
-    # and the band edges are checked, plus random rows
+    # spread over the sequence (tile edges, the middle, both ends): this grid takes the
+    # key-split path (gathered entries, 16 splits per head, ticketed combine writing
+    # through the index); every output element against the oracle
     B, H, S, W, G = 1, 16, 4096, 512, 8
     pos = [[0, 255, 256, 1000, 2047, 2048, 3500, 4095]]
     inp = workloads.random_attention_inputs(20260102, B, H, S, W, G, "fp16", global_positions=pos)
@@ -148,16 +166,9 @@ def test_scattered_globals_longformer_large_shape_sampled_rows(lf):
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16)), "not deterministic"
     got = out.cpu()
     assert torch.isfinite(got.float()).all()
-    rng = np.random.default_rng(5)
-    srows = set()
-    for p in pos[0]:
-        srows.update(x for x in (p - 257, p - 256, p - 1, p, p + 1, p + 256, p + 257) if 0 <= x < S)
-    srows.update(int(x) for x in rng.integers(0, S, 16))
-    rows = [(0, h, s) for h in (0, 7, 15) for s in sorted(srows)]
-    ref = _oracle(inp, W, G, rows=rows)
-    g_rows = np.stack([got[b, h, s].double().numpy() for (b, h, s) in rows])
-    err = np.abs(g_rows - ref).max()
-    assert err <= TOL["fp16"], f"max abs err {err:.3e} over {len(rows)} rows"
+    ref = _oracle(inp, W, G)
+    err = report("scatter longformer-large fp16", got.double().numpy(), ref, TOL["fp16"])
+    assert err <= TOL["fp16"], f"max abs err {err:.3e}"
 
 
 # ------------------------------------------------------------------ encoder layer / stack
@@ -203,7 +214,12 @@ def test_layer_any_equals_layer_with_leading_globals(lf, dtype):
     (2, 512, 256, 4, 512, 128, 8, [[3, 100, 101, 255, 256, 400, 500, 511], [0, 64, 300]], None),
     (1, 384, 512, 8, 1024, 64, 5, [[10, 200, 201, 300, 301]], (0.1, 0.15)),
 ], ids=["B2_S512_G8", "B1_S384_G5_pad"])
-def test_layer_any_scattered_globals_vs_oracle(lf, dtype, case):
+@pytest.mark.parametrize("split_path", [False, True], ids=["default", "split_path"])
+def test_layer_any_scattered_globals_vs_oracle(lf, dtype, case, split_path, monkeypatch):
+    if split_path:
+        if dtype == "fp32":
+            pytest.skip("fp32 attention has no key-split path")
+        monkeypatch.setenv("LF_ATTN_NO_GWG", "1")
     B, S, D, H, F, W, G, positions, pad = case
     x, w, lm, gm = _layer_inputs(71 + S, B, S, D, F, G, dtype, positions, pad)
     live = lm.float()
@@ -217,6 +233,8 @@ def test_layer_any_scattered_globals_vs_oracle(lf, dtype, case):
     ref = oracle.encoder_layer(x, w, lm, gm, H, W, G)
     err = np.abs(got.double().numpy() - ref)
     tol = LAYER_TOL[dtype] + (2.0 ** -8 * np.abs(ref) if dtype == "bf16" else 0.0)
+    report(f"layer-any S{S} G{G} {dtype}{' split' if split_path else ''}", got.double().numpy(),
+           ref, LAYER_TOL[dtype] if dtype != "bf16" else "per-element")
     assert np.all(err <= tol), f"max abs err {err.max():.3e}"
 
 
@@ -238,9 +256,9 @@ def test_stack_any_equals_layer_any_after_layer_any(lf, dtype):
     assert torch.equal(_bits(y), _bits(cur))
 
 
-def test_layer_any_full_size_sampled_rows(lf):
+def test_layer_any_full_size_every_element(lf):
     # the graded layer shape (B=2 S=4096 hidden 1024, 16 heads, FFN 4096, W=512) with its
-    # 16 global tokens spread over each sequence
+    # 16 global tokens spread over each sequence; every output element
     wl = workloads.LAYER_FP16
     t = workloads.make_layer_inputs(wl)
     rng = np.random.default_rng(wl.seed + 11)
@@ -255,13 +273,9 @@ def test_layer_any_full_size_sampled_rows(lf):
     torch.cuda.synchronize()
     got = y.cpu()
     assert torch.isfinite(got.float()).all()
-    rows = sorted({(b, s) for b in range(wl.B) for p in positions[b][:4]
-                   for s in (p - 1, p, p + 1) if 0 <= s < wl.S}
-                  | {(b, int(s)) for b in range(wl.B) for s in rng.integers(0, wl.S, 4)})
-    ref = oracle.encoder_layer(x, w, lm, gm, wl.H, wl.W, wl.G, rows=rows)
-    g_rows = np.stack([got[b, s].double().numpy() for (b, s) in rows])
-    err = np.abs(g_rows - ref).max()
-    assert err <= LAYER_TOL["fp16"], f"max abs err {err:.3e} over {len(rows)} rows"
+    ref = oracle.encoder_layer(x, w, lm, gm, wl.H, wl.W, wl.G)
+    err = report("layer-any full size fp16", got.double().numpy(), ref, LAYER_TOL["fp16"])
+    assert err <= LAYER_TOL["fp16"], f"max abs err {err:.3e}"
 
 
 def test_stack_any_last_layer_matches_oracle(lf):
@@ -279,5 +293,5 @@ def test_stack_any_last_layer_matches_oracle(lf):
     y = lf.encoder_forward(xg, wg, lmg, gmg, H, W, G, any_globals=True)
     torch.cuda.synchronize()
     ref = oracle.encoder_layer(y1.cpu(), layers[1], lm, gm, H, W, G)
-    err = np.abs(y.cpu().double().numpy() - ref).max()
+    err = report("stack-any last layer fp16", y.cpu().double().numpy(), ref, LAYER_TOL["fp16"])
     assert err <= LAYER_TOL["fp16"], f"max abs err {err:.3e}"

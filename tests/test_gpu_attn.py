@@ -1,11 +1,11 @@
 """GPU parity of band + global attention against the float64 oracle.
 
 [FT-LF] computation flow, per-layer steps 3-4.  Tolerances (max abs error on the
-outputs): fp32 1e-5, fp16 3e-3, bf16 1e-2.  Small and mid-size problems are
-compared element by element over the whole output; the full-size workloads, in
-the launch configuration the benchmark times, are compared on sampled rows the
-oracle computes one by one, plus properties that hold at any size (padded rows
-exactly +0.0, finite outputs, determinism)."""
+outputs): fp32 1e-5, fp16 3e-3, bf16 1e-2.  Every problem, the full-size
+workloads included (in the launch configuration the benchmark times), is compared
+element by element over the whole output, plus properties that hold at any size
+(padded rows exactly +0.0, finite outputs, determinism).  Each comparison prints
+its max abs error and max abs error / max |ref| (tests/parity.py)."""
 import zlib
 
 import numpy as np
@@ -14,6 +14,7 @@ import torch
 
 import oracle
 import workloads
+from parity import report
 
 pytestmark = pytest.mark.gpu
 
@@ -50,15 +51,15 @@ def _check_padded_zero(out_cpu, lm):
         assert np.all(pad == 0.0) and not np.any(np.signbit(pad)), "padded rows must be +0.0"
 
 
-def _full_compare(lf, inp, W, G, dtype):
+def _full_compare(lf, inp, W, G, dtype, case="attn"):
     g = _gpu(inp)
     out = _run(lf, g, W, G)
     torch.cuda.synchronize()
     got = out.cpu()
     ref = _oracle(inp, W, G)
-    err = np.abs(got.double().numpy() - ref)
     assert np.isfinite(got.float().numpy()).all()
-    assert err.max() <= TOL[dtype], f"max abs err {err.max():.3e} (tol {TOL[dtype]})"
+    err = report(f"{case} {dtype}", got.double().numpy(), ref, TOL[dtype])
+    assert err <= TOL[dtype], f"max abs err {err:.3e} (tol {TOL[dtype]})"
     _check_padded_zero(got, inp["local_mask"])
     return got, ref
 
@@ -67,7 +68,7 @@ def _full_compare(lf, inp, W, G, dtype):
 def test_tiny_fp32_workload(lf):
     wl = workloads.TINY_FP32
     inp = workloads.make_attention_inputs(wl)
-    _full_compare(lf, inp, wl.W, wl.G, "fp32")
+    _full_compare(lf, inp, wl.W, wl.G, "fp32", wl.name)
 
 
 # ---------------------------------------------------------------- mid-size, every element
@@ -92,7 +93,7 @@ def test_attention_parity_mid(lf, dtype, case):
     B, H, S, W, G, pad, ng = case
     inp = workloads.random_attention_inputs(zlib.crc32(repr(case).encode()) % 100000, B, H, S, W, G, dtype,
                                             pad_frac=pad, n_global=ng)
-    _full_compare(lf, inp, W, G, dtype)
+    _full_compare(lf, inp, W, G, dtype, f"mid B{B}H{H}S{S}W{W}G{G}")
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
@@ -104,22 +105,48 @@ def test_attention_parity_mid_split_path(lf, dtype, case, monkeypatch):
     B, H, S, W, G, pad, ng = case
     inp = workloads.random_attention_inputs(zlib.crc32(repr(case).encode()) % 100000, B, H, S, W, G, dtype,
                                             pad_frac=pad, n_global=ng)
-    _full_compare(lf, inp, W, G, dtype)
+    _full_compare(lf, inp, W, G, dtype, f"mid-split B{B}H{H}S{S}W{W}G{G}")
+
+
+# unit roundoff of the output / probability type
+UNIT = {"fp16": 2.0 ** -11, "bf16": 2.0 ** -8}
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
-@pytest.mark.parametrize("std", [1.0, 2.0])
-def test_attention_stress_inputs(lf, dtype, std):
-    # larger scores exercise the running-max updates and rescaling
+def test_attention_stress_inputs_std1(lf, dtype):
+    # N(0,1) inputs: scores of std ~1 exercise the running-max updates and rescaling;
+    # the outputs stay below ~2 in magnitude, so the stated tolerance applies as is
     B, H, S, W, G = 2, 2, 1024, 256, 12
-    inp = workloads.random_attention_inputs(77, B, H, S, W, G, dtype, std=std,
+    inp = workloads.random_attention_inputs(77, B, H, S, W, G, dtype, std=1.0,
+                                            pad_frac=(0.1, 0.2))
+    _full_compare(lf, inp, W, G, dtype, "stress std1")
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_attention_stress_inputs_std2(lf, dtype):
+    """N(0,4) inputs: scores of std ~4, so a row's softmax is dominated by a few keys
+    and |out| reaches ~8, where one rounding of the output to fp16 is already up to
+    2^-11 * 8 ~ 4e-3 (bf16: 3e-2), beyond the absolute tolerance.  The bound is the
+    arithmetic's: with u the unit roundoff of the type (fp16 2^-11, bf16 2^-8),
+      - the stored output is rounded once:                  <= u |out|;
+      - P is rounded to the type before P V, and the row sum is taken from the
+        rounded values, so the result is an exact convex combination of the allowed
+        v rows whose weights carry a relative error <= 2u / (1 - u):
+                                                            <= 2.001 u max|v|;
+      - the fp32 accumulations (<= 1e-6 relative) fit in the absolute tolerance.
+    Per element: |err| <= TOL + u |ref| + 2.001 u max(|v|, |vg|) of its (b, h)."""
+    B, H, S, W, G = 2, 2, 1024, 256, 12
+    inp = workloads.random_attention_inputs(78, B, H, S, W, G, dtype, std=2.0,
                                             pad_frac=(0.1, 0.2))
     g = _gpu(inp)
     got = _run(lf, g, W, G).cpu().double().numpy()
     ref = _oracle(inp, W, G)
-    # the tolerance scales with the output magnitude (values ~ std)
-    err = np.abs(got - ref).max()
-    assert err <= TOL[dtype] * max(1.0, 2 * std), f"max abs err {err:.3e}"
+    u = UNIT[dtype]
+    vmax = np.maximum(inp["v"].double().abs().amax(dim=(2, 3)).numpy(),
+                      inp["vg"].double().abs().amax(dim=(2, 3)).numpy())[:, :, None, None]
+    bound = TOL[dtype] + u * np.abs(ref) + 2.001 * u * vmax
+    report(f"stress std2 {dtype}", got, ref, "per-element")
+    assert np.all(np.abs(got - ref) <= bound), "error beyond the derived per-element bound"
 
 
 # ---------------------------------------------------------------- structure
@@ -211,36 +238,20 @@ def test_check_masks_detects_violations(lf):
 
 
 # ---------------------------------------------------------------- full-size workloads
-def _sample_rows(wl, lm, rng, n_random=48):
-    rows = set()
-    live = (lm == 1).numpy()
-    for b in range(wl.B):
-        n_live = int(live[b].sum())
-        cand = list(range(min(wl.G + 2, wl.S)))                         # globals + first locals
-        cand += [wl.S - 1, wl.S - 2, n_live - 1, n_live, min(n_live + 1, wl.S - 1)]
-        cand += [127, 128, 255, 256, wl.W // 2, wl.W // 2 + wl.G, wl.W, wl.S // 2]
-        for s in cand:
-            if 0 <= s < wl.S:
-                rows.add((b, int(rng.integers(wl.H)), int(s)))
-        for _ in range(n_random):
-            rows.add((b, int(rng.integers(wl.H)), int(rng.integers(wl.S))))
-    return sorted(rows)
-
-
 @pytest.mark.parametrize("wl", workloads.ATTN_WORKLOADS[1:], ids=lambda w: w.name)
-def test_full_workload_sampled_rows(lf, wl):
+def test_full_workload_every_element(lf, wl):
+    # the longformer-large, padded and long workloads, in the launch configuration the
+    # benchmark times, against the oracle over every output element
     inp = workloads.make_attention_inputs(wl)
     g = _gpu(inp)
     out = _run(lf, g, wl.W, wl.G)
     out2 = _run(lf, g, wl.W, wl.G)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16)), "not deterministic"
-    assert torch.isfinite(out).all()
     got = out.cpu()
+    assert torch.isfinite(got.float()).all()
     _check_padded_zero(got, inp["local_mask"])
-    rng = np.random.default_rng(wl.seed + 1)
-    rows = _sample_rows(wl, inp["local_mask"], rng)
-    ref = _oracle(inp, wl.W, wl.G, rows=rows)
-    g_rows = np.stack([got[b, h, s].double().numpy() for (b, h, s) in rows])
-    err = np.abs(g_rows - ref).max()
-    assert err <= TOL[wl.dtype], f"{wl.name}: max abs err {err:.3e} over {len(rows)} rows"
+    del g, out, out2
+    ref = _oracle(inp, wl.W, wl.G)
+    err = report(wl.name, got.double().numpy(), ref, TOL[wl.dtype])
+    assert err <= TOL[wl.dtype], f"{wl.name}: max abs err {err:.3e}"

@@ -11,6 +11,7 @@ import torch
 
 import oracle
 import workloads
+from parity import report
 
 pytestmark = pytest.mark.gpu
 
@@ -59,8 +60,41 @@ def test_stack_last_layer_matches_oracle(lf):
     y = lf.encoder_forward(xg, wg, lmg, gmg, H, W, G)
     torch.cuda.synchronize()
     ref = oracle.encoder_layer(y1.cpu(), layers[1], lm, gm, H, W, G)
-    err = np.abs(y.cpu().double().numpy() - ref).max()
+    err = report("stack S512 D256 last layer fp16", y.cpu().double().numpy(), ref, 3e-3)
     assert err <= 3e-3, f"max abs err {err:.3e}"
+
+
+@pytest.mark.parametrize("split_path", [False, True], ids=["default", "split_path"])
+def test_stack_benchmark_shape_every_layer_vs_oracle(lf, split_path, monkeypatch):
+    """The encoder stack at the shape the pages benchmark ([FT-LF] section "性能基准：FP32
+    与 FP16": 16 heads x 64, intermediate 4096, window 512; batch 1, sequence 1024) with
+    16 leading global tokens and 3 layers.  This shape takes the kernel paths of small
+    grids: 64 x 128 GEMM tiles, the output projection and FFN2 split over K with the
+    partial sums reduced in the LayerNorm kernel, and the global rows in workgroups of
+    their own (split_path: LF_ATTN_NO_GWG=1, the key-split path instead).  Layer l of
+    the stack is checked over every element against the oracle's layer applied to the
+    stack's own output after l - 1 layers."""
+    if split_path:
+        monkeypatch.setenv("LF_ATTN_NO_GWG", "1")
+    B, S, D, H, F, W, G, L = 1, 1024, 1024, 16, 4096, 512, 16, 3
+    rng = np.random.default_rng(41)
+    layers = [workloads.random_layer_params(rng, D, F, "fp16", w_std=0.02, b_std=0.02,
+                                            ln_jitter=0.1) for _ in range(L)]
+    x = torch.from_numpy(rng.standard_normal((B, S, D))).to(torch.float16)
+    lm, gm = workloads.make_masks(rng, B, S, G, "fp16")
+    xg, lmg, gmg = x.cuda(), lm.cuda(), gm.cuda()
+    wg = [{n: t.cuda() for n, t in w.items()} for w in layers]
+    prev = x
+    for l in range(L):
+        y = lf.encoder_forward(xg, wg[:l + 1], lmg, gmg, H, W, G)
+        torch.cuda.synchronize()
+        got = y.cpu()
+        assert torch.isfinite(got.float()).all()
+        ref = oracle.encoder_layer(prev, layers[l], lm, gm, H, W, G)
+        err = report(f"stack B1 S1024 D1024 F4096 layer {l}{' split' if split_path else ''}",
+                     got.double().numpy(), ref, 3e-3)
+        assert err <= 3e-3, f"layer {l}: max abs err {err:.3e}"
+        prev = got
 
 
 def test_stack_rejects_zero_layers(lf):
