@@ -115,6 +115,27 @@ int lf_attn_forward(int dtype, const void* q, const void* k, const void* v,
                     int B, int H, int S, int W, int G, void* out, void* stream);
 
 /*
+ * lf_attn_forward for callers that cannot allocate device memory: code under stream
+ * capture, tight serving loops, harnesses that forbid allocation.  Same arguments,
+ * computation, work split and results (bit for bit) as lf_attn_forward.  It calls no
+ * allocator: its split tickets and global-row partials (fp32: the preprocessed masks)
+ * live in one static device array per device, 32 MiB, held until the process ends
+ * (lf_attn_forward_noalloc_max_scratch() bytes of it for partials, the rest for 16384
+ * tickets).  The array's device address is looked up once per device (on the first
+ * call there, which also zero-fills the tickets with a kernel on `stream`); every call
+ * leaves the tickets zero.  Every call on a device shares that device's array, which
+ * keeps the last call's contents: calls that overlap in time on one device (on
+ * different streams or threads) race and must not be made.  A shape whose scratch
+ * exceeds the array (partials of B*H*n_split*G*272 bytes, n_split <= 32), or with
+ * B*H > 16384 and G > 0, returns LF_ERR_UNSUPPORTED with nothing enqueued.
+ */
+size_t lf_attn_forward_noalloc_max_scratch(void);
+int lf_attn_forward_noalloc(int dtype, const void* q, const void* k, const void* v,
+                            const void* qg, const void* kg, const void* vg,
+                            const void* local_mask, const void* global_mask,
+                            int B, int H, int S, int W, int G, void* out, void* stream);
+
+/*
  * Frees the scratch buffer lf_attn_forward / lf_attn_forward_any_globals keep for
  * `stream` on the current device (stream-ordered: hipFreeAsync on `stream`, after the
  * calls already enqueued there).  The next call on the stream allocates a new one.

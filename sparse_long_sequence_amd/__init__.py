@@ -16,6 +16,7 @@ import torch
 
 __all__ = ["LFError", "library_path", "load_library", "init_global_idx", "mask_shift",
            "attn_forward", "attn_forward_any_globals", "attn_forward_pre", "attn_workspace_bytes",
+           "attn_forward_noalloc",
            "check_masks",
            "encoder_layer", "encoder_layer_workspace_bytes", "encoder_forward",
            "encoder_forward_workspace_bytes", "LAYER_WEIGHT_FIELDS",
@@ -34,6 +35,7 @@ LAYER_WEIGHT_FIELDS = ["w_proj", "b_proj", "w_qg", "b_qg", "w_o", "b_o", "ln1_g"
                        "w_ffn1", "b_ffn1", "w_ffn2", "b_ffn2", "ln2_g", "ln2_b"]
 
 EXPORTED_SYMBOLS = ["lf_init_global_idx", "lf_mask_shift", "lf_attn_forward",
+                    "lf_attn_forward_noalloc", "lf_attn_forward_noalloc_max_scratch",
                     "lf_attn_forward_any_globals",
                     "lf_attn_workspace_bytes", "lf_attn_forward_pre", "lf_check_masks",
                     "lf_encoder_layer_workspace_bytes", "lf_encoder_layer",
@@ -74,6 +76,9 @@ def load_library():
     lib.lf_mask_shift.argtypes = [I, P, I, I, P, P]
     lib.lf_attn_forward.argtypes = [I, P, P, P, P, P, P, P, P, I, I, I, I, I, P, P]
     lib.lf_attn_forward_any_globals.argtypes = [I, P, P, P, P, P, P, P, P, I, I, I, I, I, P, P]
+    lib.lf_attn_forward_noalloc.argtypes = [I, P, P, P, P, P, P, P, P, I, I, I, I, I, P, P]
+    lib.lf_attn_forward_noalloc_max_scratch.argtypes = []
+    lib.lf_attn_forward_noalloc_max_scratch.restype = S
     lib.lf_attn_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.lf_attn_workspace_bytes.restype = S
     lib.lf_attn_forward_pre.argtypes = [I, P, P, P, P, P, P, P, P, P, I, I, I, I, I, P, P, S, P]
@@ -101,7 +106,7 @@ def load_library():
     lib.lf_last_error.argtypes = []
     lib.lf_last_error.restype = ctypes.c_char_p
     for name in ("lf_init_global_idx", "lf_mask_shift", "lf_attn_forward",
-                 "lf_attn_forward_any_globals",
+                 "lf_attn_forward_any_globals", "lf_attn_forward_noalloc",
                  "lf_attn_forward_pre", "lf_check_masks", "lf_encoder_layer",
                  "lf_encoder_forward", "lf_encoder_layer_any_globals",
                  "lf_encoder_forward_any_globals", "lf_ffn_block",
@@ -217,6 +222,18 @@ def attn_forward_any_globals(q, k, v, qg, kg, vg, local_mask, global_mask, W: in
                                            _ptr(qg), _ptr(kg), _ptr(vg), _ptr(local_mask),
                                            _ptr(global_mask), B, H, S, W, G, _ptr(out),
                                            _stream(dev)))
+    return out
+
+
+def attn_forward_noalloc(q, k, v, qg, kg, vg, local_mask, global_mask, W: int, G: int, out):
+    """lf_attn_forward_noalloc: the attention with its scratch in the library's static
+    device array (no allocation inside the library; `out` must be given)."""
+    lib = load_library()
+    dev = _dev(q, k, v, qg, kg, vg, local_mask, global_mask, out)
+    B, H, S = _attn_shapes(q, qg, W, G)
+    _check(lib.lf_attn_forward_noalloc(dtype_code(q.dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(qg),
+                                       _ptr(kg), _ptr(vg), _ptr(local_mask), _ptr(global_mask),
+                                       B, H, S, W, G, _ptr(out), _stream(dev)))
     return out
 
 
