@@ -35,13 +35,17 @@ import sparse_long_sequence_amd as lf  # noqa: E402
 import workloads  # noqa: E402
 
 
+WARMUP_SECONDS = 1.0   # --warmup-seconds
+
+
 def _time(fn, iters: int, warmup: int) -> float:
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    # one second of untimed calls: the clocks ramp up over the first second of work
+    # untimed calls (one second by default): the clocks ramp up over the first second
+    # of work
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 < 1.0:
+    while time.perf_counter() - t0 < WARMUP_SECONDS:
         for _ in range(20):
             fn()
         torch.cuda.synchronize()
@@ -338,7 +342,11 @@ def main():
                     help="layer only: globals spread over the sequence, general entry point")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="end with one plain elementwise copy of this many MiB (counter scaling)")
+    ap.add_argument("--warmup-seconds", type=float, default=1.0,
+                    help="untimed calls before timing (0 under a counter profiler)")
     a = ap.parse_args()
+    global WARMUP_SECONDS
+    WARMUP_SECONDS = a.warmup_seconds
     if a.op == "layer":
         print(json.dumps(run_layer(a.iters, a.warmup, a.dtype, a.any_globals)), flush=True)
     elif a.op == "stack":

@@ -13,7 +13,9 @@ found below it.  Kernels are selected by a substring of their (mangled or demang
 name.  ``traffic`` turns the per-dispatch FETCH_SIZE and WRITE_SIZE counters (KiB) of
 two runs into bytes per launch, each scaled by what the same counter reads for the
 plain elementwise copy (``torch.mul(src, 1.0, out=dst)``) of known size the measured
-program ran at its end (``--calibrate-copy-mb``).  ``--sources`` lists the files the
+program ran at its end (``--calibrate-copy-mb``); with ``--trace DIR`` (a kernel-trace
+run of the same program) it also gives each kernel's mean duration and the counted
+bytes per second.  ``--sources`` lists the files the
 measured kernels are built from; their sha256 (first 16 hex digits) is written into the
 summary, so a reader (bench.py's ``stored_traffic``) can tell whether it still matches
 the sources.  The summary goes to stdout.
@@ -29,7 +31,7 @@ import statistics
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-COPY_KERNEL = "elementwise"     # torch's elementwise kernel of the calibration copy
+COPY_KERNEL = "AUnaryFunctor"   # torch's elementwise kernel of the calibration copy (x * 1.0)
 
 
 def source_hash(paths) -> str:
@@ -94,6 +96,7 @@ def cmd_traffic(a):
             f"#   FETCH_SIZE of that kernel: {fetch_copy[0]:.1f} KiB -> scale {f_scale:.4f}",
             f"#   WRITE_SIZE of that kernel: {write_copy[0]:.1f} KiB -> scale {w_scale:.4f}", "#"]
     total = None
+    trace = _rows(a.trace, "kernel_trace.csv") if a.trace else None
     for k in a.kernel:
         fm = counter_means(a.fetch, k).get("FETCH_SIZE")
         wm = counter_means(a.write, k).get("WRITE_SIZE")
@@ -105,6 +108,14 @@ def cmd_traffic(a):
         out += [f"# {k}: {len(names)} instantiation(s), {fm[1]} / {wm[1]} dispatches",
                 f"#   FETCH_SIZE {fm[0]:.1f} KiB raw -> {fb / 1e6:.4f} MB scaled",
                 f"#   WRITE_SIZE {wm[0]:.1f} KiB raw -> {wb / 1e6:.4f} MB scaled"]
+        if trace is not None:
+            d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in trace
+                 if _match(r["Kernel_Name"], k)]
+            if d:
+                mean = statistics.fmean(d)
+                out += [f"#   duration (kernel trace, {len(d)} dispatches): mean {mean:.0f} ns "
+                        f"-> {(fb + wb) / mean:.1f} GB/s counted ({100.0 * (fb + wb) / mean / 8000.0:.1f} % "
+                        f"of 8 TB/s)"]
         if total is None:
             total = (k, fb, wb)
     k, fb, wb = total
@@ -170,6 +181,7 @@ def main(argv=None):
             p.add_argument("--calib-mib", type=float, required=True)
             p.add_argument("--alg-bytes", type=float, default=0.0)
             p.add_argument("--workload", default="")
+            p.add_argument("--trace", default="")
         else:
             p.add_argument("--dir", required=True)
         if name == "trace":
