@@ -131,9 +131,17 @@ def run_prep(iters: int, warmup: int) -> dict:
     es = gm.element_size()
     idx_bytes = B * S * (es + 4) + B * 4
     shift_bytes = 2 * B * S * es
+    # the headline masks (B=1, S=4096) as well
+    wl1 = workloads.LARGE_FP16
+    inp1 = workloads.make_attention_inputs(wl1)
+    gm1 = inp1["global_mask"].cuda()
+    idx1 = torch.empty(gm1.shape, dtype=torch.int32, device="cuda")
+    cnt1 = torch.empty(gm1.shape[0], dtype=torch.int32, device="cuda")
+    ms_idx1 = _time(lambda: lf.init_global_idx(gm1, idx1, cnt1), iters, warmup)
     return {"op": "prep", "workload": f"masks of {wl.name}", "ms_init_global_idx": ms_idx,
             "gbs_init_global_idx": idx_bytes / (ms_idx * 1e-3) / 1e9, "ms_mask_shift": ms_shift,
-            "gbs_mask_shift": shift_bytes / (ms_shift * 1e-3) / 1e9}
+            "gbs_mask_shift": shift_bytes / (ms_shift * 1e-3) / 1e9,
+            "ms_init_global_idx_" + wl1.name: ms_idx1}
 
 
 def run_layer(iters: int, warmup: int, dtype: str = "fp16", any_globals: bool = False) -> dict:

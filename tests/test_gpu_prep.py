@@ -44,8 +44,11 @@ def test_partition_golden(lf, dtype):
 
 @pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
 @pytest.mark.parametrize("B,S", [(1, 1), (3, 7), (2, 1000), (2, 4096), (3, 4097), (2, 16384),
-                                 (1, 70000)])
+                                 (1, 70000), (2, 300001)])
 def test_partition_random_bit_exact(lf, dtype, B, S):
+    # S = 4097 and 300001: rows that start off a 16-byte boundary (the count of
+    # earlier flags takes narrow loads); 70000 and 300001: several passes per
+    # workgroup, 300001: more than 64 chunks of 1024 positions
     rng = np.random.default_rng(B * 100003 + S)
     dens = rng.uniform(0, 1, size=(B, 1))
     flags = rng.uniform(size=(B, S)) < dens
