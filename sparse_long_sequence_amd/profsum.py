@@ -10,7 +10,7 @@
 
 DIR is a rocprofv3 output directory (``-d DIR --output-format csv``); the CSV files are
 found below it.  Kernels are selected by a substring of their (mangled or demangled)
-name.  ``traffic`` turns the per-dispatch FETCH_SIZE and WRITE_SIZE counters (KiB) of
+name; ``--note`` adds lines of explanation to the header.  ``traffic`` turns the per-dispatch FETCH_SIZE and WRITE_SIZE counters (KiB) of
 two runs into bytes per launch, each scaled by what the same counter reads for the
 plain elementwise copy (``torch.mul(src, 1.0, out=dst)``) of known size the measured
 program ran at its end (``--calibrate-copy-mb``); with ``--trace DIR`` (a kernel-trace
@@ -73,17 +73,19 @@ def kernel_names(d: str, suffix: str, sub: str):
     return sorted({r["Kernel_Name"] for r in _rows(d, suffix) if _match(r["Kernel_Name"], sub)})
 
 
-def _header(title: str, cmds, sources):
+def _header(title: str, cmds, sources, notes=()):
     lines = [f"# {title}", "#", "# Commands (each a run of its own, from /tmp with TMPDIR=/tmp; "
              "R = repository root):"]
     lines += [f"#   {c}" for c in cmds]
     if sources:
         lines += ["#", f"# kernel sources: {' '.join(sources)}"]
+    if notes:
+        lines += ["#"] + [f"# {n}" for n in notes]
     return lines
 
 
 def cmd_traffic(a):
-    out = _header(a.title, a.cmd, a.sources)
+    out = _header(a.title, a.cmd, a.sources, a.note)
     fetch_copy = counter_means(a.fetch, COPY_KERNEL).get("FETCH_SIZE")
     write_copy = counter_means(a.write, COPY_KERNEL).get("WRITE_SIZE")
     if not fetch_copy or not write_copy:
@@ -131,7 +133,7 @@ def cmd_traffic(a):
 
 
 def cmd_counters(a):
-    out = _header(a.title, a.cmd, a.sources)
+    out = _header(a.title, a.cmd, a.sources, a.note)
     for k in a.kernel:
         m = counter_means(a.dir, k)
         if not m:
@@ -145,7 +147,7 @@ def cmd_counters(a):
 
 
 def cmd_trace(a):
-    out = _header(a.title, a.cmd, a.sources)
+    out = _header(a.title, a.cmd, a.sources, a.note)
     rows = _rows(a.dir, "kernel_trace.csv")
     for k in a.kernel:
         d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows
@@ -175,6 +177,8 @@ def main(argv=None):
         p.add_argument("--title", required=True)
         p.add_argument("--cmd", action="append", default=[])
         p.add_argument("--sources", nargs="*", default=[])
+        p.add_argument("--note", action="append", default=[],
+                       help="a line of explanation for the summary's header (repeatable)")
         if name == "traffic":
             p.add_argument("--fetch", required=True)
             p.add_argument("--write", required=True)
