@@ -115,6 +115,35 @@ def cpu_baseline(inp, wl, budget_s: float):
             "blas": blas, "seconds": round(t_total, 2), "host_cpus": os.cpu_count()}
 
 
+def oracle_table():
+    """The float64 oracle over the whole output of each graded configuration (the same
+    calls the full-output parity tests make), BLAS threads = this process's CPU
+    affinity; one JSON line per configuration.  CPU only: no GPU work."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    import workloads
+    cores = len(os.sched_getaffinity(0))
+    with threadpool_limits(limits=cores):
+        for wl in workloads.ATTN_WORKLOADS:
+            inp = workloads.make_attention_inputs(wl)
+            t0 = time.perf_counter()
+            oracle.attention(inp["q"], inp["k"], inp["v"], inp["qg"], inp["kg"], inp["vg"],
+                             inp["local_mask"], inp["global_mask"], wl.W, wl.G)
+            dt = time.perf_counter() - t0
+            print(json.dumps({"workload": wl.name, "oracle_s": round(dt, 3), "cores": cores,
+                              "rows": wl.B * wl.H * wl.S}), flush=True)
+        wl = workloads.LAYER_FP16
+        t = workloads.make_layer_inputs(wl)
+        w = {n: t[n] for n in ["w_proj", "b_proj", "w_qg", "b_qg", "w_o", "b_o", "ln1_g", "ln1_b",
+                               "w_ffn1", "b_ffn1", "w_ffn2", "b_ffn2", "ln2_g", "ln2_b"]}
+        t0 = time.perf_counter()
+        oracle.encoder_layer(t["x"], w, t["local_mask"], t["global_mask"], wl.H, wl.W, wl.G)
+        dt = time.perf_counter() - t0
+        print(json.dumps({"workload": wl.name, "oracle_s": round(dt, 3), "cores": cores,
+                          "rows": wl.B * wl.S}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,7 +165,13 @@ def main():
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="after the timed loop, run one plain elementwise copy of this many MiB "
                          "(fp32 in, fp32 out) so HBM counters can be scaled by a known size")
+    ap.add_argument("--oracle-table", action="store_true",
+                    help="only time the float64 oracle over the whole output of each graded "
+                         "configuration on this host's cores (CPU only), one JSON line each")
     args = ap.parse_args()
+    if args.oracle_table:
+        oracle_table()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the library has no multi-GPU path "
               f"(--gpus {args.gpus} requested). The (batch, head) pairs of the attention are "
