@@ -16,23 +16,29 @@
 // it reads global_count / the shifted mask produced by the preprocessing entry
 // points.
 //
-// Band workgroup: 8 waves = 256 query rows of one (b, h), two waves per SIMD (one
-// wave's vector work overlaps the other's matrix work).  Wave w owns the 32 rows
-// r0 + 64 (w % 4) + 32 (w / 4) ..: row group w % 4, sub-block w / 4.  Keys move in
-// entries of 64 (two 32-key blocks; K row-major, V transposed, plus a per-key
-// 0 / -inf term) through an 8-slot LDS ring.  The entry list of a workgroup is
-//     [ceil(G/64) global-key entries][band entries 0 .. npb+2]
+// Band workgroup, two layouts (one per translation unit):
+//   8 waves = 256 query rows of one (b, h), two waves per SIMD, an 8-slot LDS ring
+//     (146 KB: one workgroup per CU); sequences below 8192 tokens;
+//   4 waves = 128 rows, a 4-slot ring (73 KB: two workgroups per CU, one wave of
+//     each per SIMD); long sequences, where one workgroup's memory round trips
+//     overlap the other's band work.
+// Wave w owns the 32 rows r0 + 64 (w % R) + 32 (w / R) .. (R = waves / 2 row groups
+// of 64 rows): row group w % R, sub-block w / R.  Keys move in entries of 64 (two
+// 32-key blocks; K row-major, V transposed, plus a per-key 0 / -inf term) through the
+// ring.  The entry list of a workgroup is
+//     [ceil(G/64) global-key entries][band entries 0 .. npb + R - 2]
 // where band entry j holds keys r0 - W/2 + 64j ..; row group rg needs band blocks
 // 2rg .. 2rg + nband (nband = (W + 63) / 32), i.e. band entries rg .. rg + npb - 1.
 // At step t every wave reads entry t (global phase) or t + rg (band phase: the row
-// groups walk the band on a diagonal, so none of them idles); entry t + 5 is written
-// into the ring from registers and the loads of entry t + 7 are issued.  Steps run
-// in pairs with one barrier per pair: an entry written at step t is first read at
-// step t + 2, after the barrier that ends the pair, and the slot it overwrites (that
-// of entry t - 3) was last read before the previous barrier.  Writing only two
-// entries ahead of the read window keeps the workgroups' first loads small (entries
-// 0..4 and Q), so the HBM traffic spreads over the loop instead of arriving as one
-// burst at the start.
+// groups walk the band on a diagonal, so none of them idles); entry t + kAhead is
+// written into the ring from registers and the loads of entry t + kAhead + 2 are
+// issued.  8 waves: kAhead = 5, steps in pairs with one barrier per pair (an entry
+// written at step t is first read at step t + 2, after the barrier that ends the pair,
+// and the slot it overwrites, entry t - 3's, was last read before the previous
+// barrier).  4 waves: kAhead = 2, a barrier after every step (written at t, read from
+// t + 1; the slot it overwrites, entry t - 2's, was last read at step t - 2).  Writing
+// only a few entries ahead of the read window keeps the workgroups' first loads small,
+// so the HBM traffic spreads over the loop instead of arriving as one burst.
 //
 // Per 32-key block and wave: S^T = K Q^T (4 x v_mfma_f32_32x32x16, accumulator
 // initialised with the per-key term, so dead keys cost no vector work), so each
@@ -44,11 +50,13 @@
 //
 // Global rows (r < n_b) attend to all live keys through kg / vg.  The first
 // n_split tiles of each (b, h) also take one key split of those rows (split_len
-// keys, 32 per wave per round) after their band work.  The split's first-round
+// keys, 32 per wave per round), after their band work.  The split's first-round
 // entries continue the ring's entry list, so the band loop's last steps stage them
 // like band entries: their kg / vg loads stream while the loop computes instead of
-// joining the launch's first burst of loads.  The eight wave states are merged in
-// LDS and one partial (m, l, o[64]) per row is published with write-through stores
+// joining the launch's first burst of loads.  (4 waves: every other dispatch
+// generation runs its split before the band loop instead, so that the two
+// workgroups on a CU are in different phases.)  The wave states are merged in LDS
+// and one partial (m, l, o[64]) per row is published with write-through stores
 // (coherent across XCDs without cache maintenance).  Then the workgroup takes an
 // atomic ticket; the one whose ticket completed the (b, h) reads all partials with
 // coherent loads, writes the global rows and resets the ticket.
@@ -61,7 +69,17 @@ namespace lf {
 
 namespace {
 
-constexpr int kWaves = 8;
+// Two layouts of the band workgroup, one per translation unit (LF_ATTN_WAVES): 8 waves
+// = 256 query rows with an 8-slot ring (one workgroup per CU; the default), or 4 waves
+// = 128 rows with a 4-slot ring of 75 KB, so that two workgroups share a CU and one's
+// memory round trips overlap the other's band work (long sequences).
+#ifndef LF_ATTN_WAVES
+#define LF_ATTN_WAVES 8
+#endif
+constexpr int kWaves = LF_ATTN_WAVES;
+static_assert(kWaves == 8 || kWaves == 4, "8- or 4-wave layout");
+constexpr int kRowGroups = kWaves / 2;   // 64-row groups per workgroup (two sub-blocks each)
+constexpr bool kPairs = kWaves == 8;     // one barrier per pair of steps (else per step)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsW = 32;           // query rows per wave
 constexpr int kTile = kRowsW * kWaves;  // query rows per workgroup
@@ -69,11 +87,11 @@ constexpr int kBlk = 32;             // keys per MFMA block
 constexpr int kEnt = 64;             // keys per ring entry (two blocks)
 constexpr int kKld = 72;             // LDS row pitch of K (elements): 144 B, conflict-free reads
 constexpr int kVld = 72;             // LDS row pitch of V^T (elements): 144 B, conflict-free reads
-constexpr int kRing = 8;             // LDS entry slots (the global-row split merges 8 wave states)
-constexpr int kAhead = 5;            // entry t + kAhead is written at step t
+constexpr int kRing = kWaves == 8 ? 8 : 4;    // LDS entry slots
+constexpr int kAhead = kWaves == 8 ? 5 : 2;   // entry t + kAhead is written at step t
 constexpr int kDepth = 2;            // register sets of loads in flight
 constexpr int kSplitEnt = kWaves * kBlk / kEnt;   // entries per round of the global-row split
-constexpr int kStPitch = 67;         // floats per row of a wave state in LDS: m, l, o[64], pad
+constexpr int kStPitch = 68;         // floats per row of a wave state in LDS: m, l, pad[2], o[64]
 constexpr int kMaxSplit = 32;        // at most this many key splits per (b, h)
 constexpr int kSc1 = 16;             // cache-policy bit of coherent (write-through / bypass) access
 constexpr float kLog2e = 1.4426950408889634f;
@@ -87,8 +105,8 @@ struct Slot {
   float bias2[kEnt];    // 0 for a live key, -inf for an empty / excluded / padded slot
 };
 
-static_assert(32 * kStPitch * 4 <= sizeof(Slot<_Float16>), "a wave state fits in one slot");
-static_assert(kRing >= kWaves, "the split merges one wave state per slot");
+static_assert(2 * 32 * kStPitch * 4 <= sizeof(Slot<_Float16>), "two wave states fit in one slot");
+static_assert(kRing >= kSplitEnt + kWaves / 2, "the split's entries and its wave states fit in the ring");
 
 template <typename T>
 struct Frag {
@@ -114,18 +132,20 @@ __device__ inline bool mask_live(float x) {
   return RAW ? x == 1.0f : x == 0.0f;
 }
 
-// Thread t stages 16 B of K row t/8 (column 8*(t%8)), dims 4*(t%16) .. +3 of the key
-// pair 2*(t/16), 2*(t/16)+1 of V (8 B each) and, for t < 64, the mask value of key
-// slot t.  Every thread does the same work; no branch.
+// An entry is staged as 512 parts, kParts per thread: part u = t + kThreads h is
+// 16 B of K row u/8 (column 8*(u%8)) and dims 4*(u%16) .. +3 of the key pair
+// 2*(u/16), 2*(u/16)+1 of V (8 B each); threads t < 64 also take the mask value of
+// key slot t.  Every thread does the same work; no branch.
+constexpr int kParts = 512 / kThreads;   // staging parts per thread
 template <typename T>
 struct Stage {
-  u32x4 k;
-  u32x2 v0, v1;
+  u32x4 k[kParts];
+  u32x2 v0[kParts], v1[kParts];
   unsigned short mask_bits;
   unsigned short gflag_bits;   // globals-anywhere mode, band entries: global-mask value
 };
 
-// Entry of keys base .. base + 63.  Every thread issues the same four loads, so the
+// Entry of keys base .. base + 63.  Every thread issues the same loads, so the
 // compiler can keep later entries in flight while it waits for this one.  K / V
 // rows are loaded for every in-range key (a dead key's score is masked to -inf, so
 // its data never matters).
@@ -133,10 +153,14 @@ template <typename T>
 __device__ inline void stage_load(Stage<T>& s, rsrc_t rk, rsrc_t rv, rsrc_t rm, int base) {
   const int t = threadIdx.x;
   const int b128 = base * 128;
-  const int voff = (t >> 4) * 256 + 8 * (t & 15);
-  s.k = __builtin_amdgcn_raw_buffer_load_b128(rk, b128 + (t >> 3) * 128 + 16 * (t & 7), 0, 0);
-  s.v0 = __builtin_amdgcn_raw_buffer_load_b64(rv, b128 + voff, 0, 0);
-  s.v1 = __builtin_amdgcn_raw_buffer_load_b64(rv, b128 + voff + 128, 0, 0);
+#pragma unroll
+  for (int h = 0; h < kParts; ++h) {
+    const int u = t + kThreads * h;
+    const int voff = (u >> 4) * 256 + 8 * (u & 15);
+    s.k[h] = __builtin_amdgcn_raw_buffer_load_b128(rk, b128 + (u >> 3) * 128 + 16 * (u & 7), 0, 0);
+    s.v0[h] = __builtin_amdgcn_raw_buffer_load_b64(rv, b128 + voff, 0, 0);
+    s.v1[h] = __builtin_amdgcn_raw_buffer_load_b64(rv, b128 + voff + 128, 0, 0);
+  }
   s.mask_bits = __builtin_amdgcn_raw_buffer_load_b16(rm, t < kEnt ? 2 * (base + t) : -1, 0, 0);
 }
 
@@ -144,19 +168,24 @@ __device__ inline void stage_load(Stage<T>& s, rsrc_t rk, rsrc_t rv, rsrc_t rm, 
 // position gi[r].  Slots below G load (the index holds S positions per row, G <= S);
 // slots from n_b on hold ordinary positions and are marked dead when the entry is
 // stored (the loads are issued before n_b is known), slots from G on read position
-// S, out of range, so their loads return zeros.  Same thread mapping as stage_load.
+// S, out of range, so their loads return zeros.  Same part mapping as stage_load.
 template <typename T>
 __device__ inline void stage_gather(Stage<T>& s, rsrc_t rk, rsrc_t rv, rsrc_t rm,
                                    const int32_t* __restrict__ gi, int slot0, int G, int S) {
   const int t = threadIdx.x;
-  const int sk = slot0 + (t >> 3), sv = slot0 + 2 * (t >> 4), sm = slot0 + (t & 63);
-  const int pk = sk < G ? gi[sk] : S;
-  const int pv0 = sv < G ? gi[sv] : S;
-  const int pv1 = sv + 1 < G ? gi[sv + 1] : S;
+#pragma unroll
+  for (int h = 0; h < kParts; ++h) {
+    const int u = t + kThreads * h;
+    const int sk = slot0 + (u >> 3), sv = slot0 + 2 * (u >> 4);
+    const int pk = sk < G ? gi[sk] : S;
+    const int pv0 = sv < G ? gi[sv] : S;
+    const int pv1 = sv + 1 < G ? gi[sv + 1] : S;
+    s.k[h] = __builtin_amdgcn_raw_buffer_load_b128(rk, pk * 128 + 16 * (u & 7), 0, 0);
+    s.v0[h] = __builtin_amdgcn_raw_buffer_load_b64(rv, pv0 * 128 + 8 * (u & 15), 0, 0);
+    s.v1[h] = __builtin_amdgcn_raw_buffer_load_b64(rv, pv1 * 128 + 8 * (u & 15), 0, 0);
+  }
+  const int sm = slot0 + (t & 63);
   const int pm = sm < G ? gi[sm] : S;
-  s.k = __builtin_amdgcn_raw_buffer_load_b128(rk, pk * 128 + 16 * (t & 7), 0, 0);
-  s.v0 = __builtin_amdgcn_raw_buffer_load_b64(rv, pv0 * 128 + 8 * (t & 15), 0, 0);
-  s.v1 = __builtin_amdgcn_raw_buffer_load_b64(rv, pv1 * 128 + 8 * (t & 15), 0, 0);
   s.mask_bits = __builtin_amdgcn_raw_buffer_load_b16(rm, t < kEnt ? 2 * pm : -1, 0, 0);
 }
 
@@ -174,16 +203,20 @@ template <typename T, bool RAW>
 __device__ inline void stage_store(Slot<T>& sl, const Stage<T>& s, int base, int lo, int hi,
                                    bool excl_glob = false) {
   const int t = threadIdx.x;
-  *(u32x4*)&sl.k[(t >> 3) * kKld + 8 * (t & 7)] = s.k;
-  // dims 4c .. 4c+3 of keys 2vp, 2vp+1 -> V^T rows 4c .. 4c+3, one dword (a key pair)
-  // each
-  const int vp = t >> 4, cc = t & 15;
-  uint32_t* vt = (uint32_t*)sl.vt + vt_pos(2 * vp) / 2;
-  constexpr int P = kVld / 2;   // pitch in dwords
-  vt[(4 * cc + 0) * P] = __builtin_amdgcn_perm(s.v1[0], s.v0[0], 0x05040100u);
-  vt[(4 * cc + 1) * P] = __builtin_amdgcn_perm(s.v1[0], s.v0[0], 0x07060302u);
-  vt[(4 * cc + 2) * P] = __builtin_amdgcn_perm(s.v1[1], s.v0[1], 0x05040100u);
-  vt[(4 * cc + 3) * P] = __builtin_amdgcn_perm(s.v1[1], s.v0[1], 0x07060302u);
+#pragma unroll
+  for (int h = 0; h < kParts; ++h) {
+    const int u = t + kThreads * h;
+    *(u32x4*)&sl.k[(u >> 3) * kKld + 8 * (u & 7)] = s.k[h];
+    // dims 4c .. 4c+3 of keys 2vp, 2vp+1 -> V^T rows 4c .. 4c+3, one dword (a key
+    // pair) each
+    const int vp = u >> 4, cc = u & 15;
+    uint32_t* vt = (uint32_t*)sl.vt + vt_pos(2 * vp) / 2;
+    constexpr int P = kVld / 2;   // pitch in dwords
+    vt[(4 * cc + 0) * P] = __builtin_amdgcn_perm(s.v1[h][0], s.v0[h][0], 0x05040100u);
+    vt[(4 * cc + 1) * P] = __builtin_amdgcn_perm(s.v1[h][0], s.v0[h][0], 0x07060302u);
+    vt[(4 * cc + 2) * P] = __builtin_amdgcn_perm(s.v1[h][1], s.v0[h][1], 0x05040100u);
+    vt[(4 * cc + 3) * P] = __builtin_amdgcn_perm(s.v1[h][1], s.v0[h][1], 0x07060302u);
+  }
   if (wave_id() == 0) {
     const int lane = lane_id();
     const int key = base + lane;
@@ -374,6 +407,7 @@ template <typename T>
 struct Ctx {
   int b, h, bh, tile, S, W, G, nb, ngp, r0, kbase, n_list;
   bool split;                // this tile runs a key split of the global rows
+  bool split_tail;           // ... after its band work (its first round staged by the band loop)
   int sp_lo, sp_hi;          // key range of the split
   const T *kh, *vh;          // k, v of this head
   const T *kgh, *vgh;        // kg, vg of this head (split tiles; else k, v)
@@ -396,7 +430,7 @@ __device__ inline int entry_base(const Ctx<T>& c, int i) {
   const int ngp = c.ngp, n_list = c.n_list, S = c.S;
   const int base = i < ngp ? kEnt * i : c.kbase + kEnt * (i - ngp);
   const int e = i - n_list;
-  const int past = PAST && c.split && e < kSplitEnt ? c.sp_lo + kEnt * e : S;
+  const int past = PAST && c.split_tail && e < kSplitEnt ? c.sp_lo + kEnt * e : S;
   return i < n_list ? base : past;
 }
 
@@ -433,6 +467,14 @@ __device__ inline void store_entry(Slot<T>& sl, const Stage<T>& s, const Ctx<T>&
 }
 
 // ------------------------------------------------------------------ global rows
+// Row q of wave w's state during the split's merge: the slots after the round's
+// kSplitEnt entries hold two wave states each.
+template <typename T>
+__device__ inline float* state_row(Slot<T>* ring, int ebase, int w, int q) {
+  unsigned char* sl = (unsigned char*)&ring[(ebase + kSplitEnt + (w >> 1)) % kRing];
+  return (float*)(sl + (w & 1) * (32 * kStPitch * 4)) + q * kStPitch;
+}
+
 // Key split `sp` of the global rows of (b, h), run after the band work: rounds of
 // kWaves blocks (one per wave, four entries), then the wave states are merged in
 // LDS and one partial (m, l, o[64]) per row is published with write-through
@@ -461,6 +503,9 @@ __device__ void global_split_run(const AttnArgs& a, const Ctx<T>& c, int sp, Slo
   float* part = a.partials + ((size_t)c.bh * a.n_split + sp) * (size_t)G * kPartPitch;
   const rsrc_t rpart = make_rsrc(part, (uint32_t)G * kPartPitch * 4u);
 
+  // ring slot of the round's first entry: the staged round sits at slot0, the rounds
+  // this function loads at slot 0
+  int ebase = PRE ? slot0 : 0;
   for (int qb = 0; qb * 32 < nb; ++qb) {
     v8 qf[4];
     const int r = 32 * qb + n;
@@ -476,6 +521,7 @@ __device__ void global_split_run(const AttnArgs& a, const Ctx<T>& c, int sp, Slo
       const int base = k_lo + kBlk * kWaves * u;
       const bool staged = PRE && qb == 0 && u == 0;
       if (!staged) {
+        ebase = 0;
         Stage<T> st[kSplitEnt];
 #pragma unroll
         for (int e = 0; e < kSplitEnt; ++e)
@@ -488,55 +534,59 @@ __device__ void global_split_run(const AttnArgs& a, const Ctx<T>& c, int sp, Slo
           stage_store<T, RAW>(ring[e], st[e], base + kEnt * e, k_lo, k_hi);
       }
       __syncthreads();
-      block_step<T>(ring[staged ? (slot0 + (wave >> 1)) % kRing : wave >> 1], wave & 1, qf, o,
-                    m_run, l_run, c2);
+      block_step<T>(ring[(ebase + (wave >> 1)) % kRing], wave & 1, qf, o, m_run, l_run, c2);
     }
-    __syncthreads();   // every wave is done with its block before the states go in
-    float* stp = (float*)&ring[wave];
+    // the wave states go into the slots the round's entries do not use (two states per
+    // slot), so no wave waits for the others before writing its own; only rows below
+    // n_b are written and merged
+    const int r_valid = min(32, nb - 32 * qb);   // rows of this query block published
     const float l_tot = cross_half_sum(l_run);
+    if (n < r_valid) {
+      float* stp = state_row(ring, ebase, wave, n);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-        stp[n * kStPitch + 2 + 32 * mb + 8 * (v >> 2) + 4 * g + (v & 3)] = o[mb][v];
-    if (g == 0) {
-      stp[n * kStPitch + 0] = m_run;
-      stp[n * kStPitch + 1] = l_tot;
+        for (int jj = 0; jj < 4; ++jj)
+          *(f32x4*)&stp[4 + 32 * mb + 8 * jj + 4 * g] =
+              f32x4{o[mb][4 * jj], o[mb][4 * jj + 1], o[mb][4 * jj + 2], o[mb][4 * jj + 3]};
+      if (g == 0) {
+        stp[0] = m_run;
+        stp[1] = l_tot;
+      }
     }
     __syncthreads();
-    // merge the wave states: thread -> (query q, 8 dims); publish with
-    // write-through stores (coherent across XCDs)
-    if (t < 32 * 8) {
-      const int q = t >> 3, d0 = (t & 7) * 8;
-      const int rr = 32 * qb + q;
+    // merge the wave states: thread -> (query q, 8 dims) (threads from 256 on idle);
+    // publish with write-through stores (coherent across XCDs)
+    constexpr int kTpr = 8, kDpt = 64 / kTpr;   // threads per row, dims each
+    const int q = t / kTpr, d0 = (t % kTpr) * kDpt;
+    if (q < r_valid) {
       float mw[kWaves], M = kNegBig;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        mw[w] = ((const float*)&ring[w])[q * kStPitch];
+        mw[w] = state_row(ring, ebase, w, q)[0];
         M = fmaxf(M, mw[w]);
       }
-      float L = 0.0f, acc[8];
+      float L = 0.0f;
+      f32x4 acc[kDpt / 4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+      for (int i = 0; i < kDpt / 4; ++i) acc[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const float* sw = (const float*)&ring[w] + q * kStPitch;
+        const float* sw = state_row(ring, ebase, w, q);
         const float f = fast_exp2(mw[w] - M);
         L += sw[1] * f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += sw[2 + d0 + i] * f;
+        for (int i = 0; i < kDpt / 4; ++i) acc[i] += *(const f32x4*)&sw[4 + d0 + 4 * i] * f;
       }
-      if (rr < nb) {
-        // write-through (sc1) stores: visible to every XCD once complete
-        const int off = (rr * kPartPitch + 4 + d0) * 4;
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{acc[0], acc[1], acc[2], acc[3]}),
-                                               rpart, off, 0, kSc1);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f32x4{acc[4], acc[5], acc[6], acc[7]}),
-                                               rpart, off + 16, 0, kSc1);
-        if ((t & 7) == 0) {
-          const u32x2 ml = {__float_as_uint(M), __float_as_uint(L)};
-          __builtin_amdgcn_raw_buffer_store_b64(ml, rpart, rr * kPartPitch * 4, 0, kSc1);
-        }
+      const int rr = 32 * qb + q;
+      const int off = (rr * kPartPitch + 4 + d0) * 4;
+#pragma unroll
+      for (int i = 0; i < kDpt / 4; ++i)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[i]), rpart, off + 16 * i,
+                                               0, kSc1);
+      if (d0 == 0) {
+        const u32x2 ml = {__float_as_uint(M), __float_as_uint(L)};
+        __builtin_amdgcn_raw_buffer_store_b64(ml, rpart, rr * kPartPitch * 4, 0, kSc1);
       }
     }
     __syncthreads();   // slots free again
@@ -756,7 +806,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   typedef typename Frag<T>::v8 v8;
   const int lane = lane_id();
   const int wave = wave_id();   // uniform: index math on the scalar unit
-  const int rg = wave & 3, sb = wave >> 2;
+  const int rg = wave % kRowGroups, sb = wave / kRowGroups;
   const int n = lane & 31, g = lane >> 5;
   const int n_wg = a.B * a.H * n_tiles;
   if constexpr (GWG) {
@@ -781,18 +831,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   c.r0 = c.tile * kTile;
   c.kbase = c.r0 - (a.W >> 1);
   // a row group needs nband + 1 band blocks (its second sub-block starts one block
-  // later): npb entries
+  // later): npb entries; the row groups' windows together span npb + kRowGroups - 1
   const int nband = (c.W + 2 * kBlk - 1) / kBlk;
   const int npb = (nband + 2) / 2;
   const int n_steps = c.ngp + npb;
-  c.n_list = c.ngp + npb + 3;
+  c.n_list = c.ngp + npb + kRowGroups - 1;
   const size_t head = (size_t)c.bh * c.S * 64;
   c.mask = (const T*)(RAW ? a.local_mask : a.bias) + (size_t)c.b * c.S;
   c.gi = ANY ? a.gidx + (size_t)c.b * c.S : nullptr;
   c.gm = ANY ? (const unsigned short*)a.global_mask + (size_t)c.b * c.S : nullptr;
   const float c2 = a.scale * kLog2e;
   const bool split = !GWG && a.G > 0 && c.tile < a.n_split;
+  // 4-wave layout: two workgroups share a CU, and the dispatcher places one on every
+  // CU before it places a second, so workgroups of consecutive dispatch generations
+  // (wg_per_gen workgroups each) pair up.  Odd generations run their split before the
+  // band loop, even ones after it: one workgroup's memory round trips overlap the
+  // other's band work.  (8 waves: one workgroup per CU, the split always runs last.)
+  const bool sfirst = kWaves == 4 && split && a.wg_per_gen > 0 &&
+                      (((int)blockIdx.x / a.wg_per_gen) & 1);
   c.split = split;
+  c.split_tail = split && !sfirst;
   c.sp_lo = split ? c.tile * a.split_len : 0;
   c.sp_hi = split ? min(c.S, c.sp_lo + a.split_len) : 0;
   c.kh = (const T*)a.k + head;
@@ -801,13 +859,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   c.vgh = split ? (const T*)a.vg + head : c.vh;
 
   // every load the prologue needs is issued before anything waits: the global-mask
-  // values, the first ring entries, Q, the register sets.  Only wave 0 counts the
-  // global tokens: it alone writes the per-key terms, the one use of the count before
-  // the band loop, and hands the count to the other waves at the prologue barrier.
-  // (Every workgroup of a batch row reads the same mask values: one request per
-  // workgroup instead of one per wave keeps that cache line from becoming a hot spot.)
+  // values, (split-first) the split's first round and its queries, the first ring
+  // entries, Q, the register sets.  Only wave 0 counts the global tokens and hands
+  // the count to the other waves at the prologue barrier.  (Every workgroup of a
+  // batch row reads the same mask values: one request per workgroup instead of one
+  // per wave keeps that cache line from becoming a hot spot.)
   const bool counter = wave == 0;
   const int gfirst = counter ? count_load<T, RAW, ANY>(a, c.b) : 0;
+  __builtin_amdgcn_sched_barrier(0);
+  Stage<T> spl[kSplitEnt];
+  v8 qg0[4];
+  if (sfirst) {
+    const uint32_t bytes = (uint32_t)c.S * 128u;
+    const rsrc_t rkg = make_rsrc(c.kgh, bytes), rvg = make_rsrc(c.vgh, bytes);
+    const rsrc_t rm = make_rsrc(c.mask, (uint32_t)c.S * 2u);
+#pragma unroll
+    for (int e = 0; e < kSplitEnt; ++e) stage_load<T>(spl[e], rkg, rvg, rm, c.sp_lo + kEnt * e);
+    load_q<T>(qg0, (const T*)a.qg + ((size_t)c.bh * a.G + (n < a.G ? n : 0)) * 64, n < a.G);
+  }
   __builtin_amdgcn_sched_barrier(0);
   Stage<T> pro[kAhead];
 #pragma unroll
@@ -824,9 +893,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const unsigned short row_gflag = ANY ? c.gm[srow_c] : (unsigned short)0;
   __builtin_amdgcn_sched_barrier(0);
   static_assert(kDepth == 2, "steps run in pairs: entry e uses set e % 2");
-  // after the band loop the ring holds list entries up to n_list + 1 and the register
-  // sets n_list + 2, n_list + 3: the split's first round
-  static_assert(kAhead - 3 + kDepth == kSplitEnt, "split round = two staged + two in registers");
+  // after the band loop the ring holds list entries up to n_list + kStaged - 1 and the
+  // register sets the next kDepth: the split's first round is n_list .. n_list +
+  // kSplitEnt - 1, its last kSplitEnt - kStaged entries still in registers
+  constexpr int kStaged = kAhead - (kRowGroups - 1);
+  static_assert(kStaged >= 1 && kSplitEnt - kStaged >= 1 && kSplitEnt - kStaged <= kDepth,
+                "split round = entries staged by the band loop + entries in the register sets");
   Stage<T> st[kDepth];
 #pragma unroll
   for (int u = 0; u < kDepth; ++u) {
@@ -834,37 +906,63 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     __builtin_amdgcn_sched_barrier(0);
   }
   c.nb = counter ? count_globals<T, RAW, ANY>(a, c.b, gfirst) : 0;
-
-#pragma unroll
-  for (int i = 0; i < kAhead; ++i) store_entry<T, RAW, ANY, true>(ring[i], pro[i], c, i);
   __shared__ int s_nb;
-  if (counter && lane == 0) s_nb = c.nb;
-  __syncthreads();
-  c.nb = __builtin_amdgcn_readfirstlane(s_nb);
+  int ticket = 0;
+  if constexpr (kWaves == 8) {
+    // the first entries are written before the prologue barrier (wave 0 alone writes
+    // the per-key terms, with its own count)
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) store_entry<T, RAW, ANY, true>(ring[i], pro[i], c, i);
+    if (counter && lane == 0) s_nb = c.nb;
+    __syncthreads();
+    c.nb = __builtin_amdgcn_readfirstlane(s_nb);
+  } else {
+    if (counter && lane == 0) s_nb = c.nb;
+    __syncthreads();
+    c.nb = __builtin_amdgcn_readfirstlane(s_nb);
+    // split first: its round is in the ring's slots 0 .. kSplitEnt - 1 (its wave
+    // states in the others), then the partial is published and the ticket taken; the
+    // band entries go in afterwards
+    if (sfirst && c.nb > 0) {
+#pragma unroll
+      for (int e = 0; e < kSplitEnt; ++e)
+        stage_store<T, RAW>(ring[e], spl[e], c.sp_lo + kEnt * e, c.sp_lo, c.sp_hi);
+      global_split_run<T, RAW, ANY, true>(a, c, c.tile, ring, 0, qg0);
+      ticket = take_ticket<T>(a, c);
+    }
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) store_entry<T, RAW, ANY, true>(ring[i], pro[i], c, i);
+    __syncthreads();
+  }
+  const bool do_split = split && c.nb > 0;
 
   f32x16 o[2] = {f32x16{}, f32x16{}};
   float m_run = kNegBig, l_run = 0.0f;
   constexpr int s0i = kAhead % kDepth, s1i = (kAhead + 1) % kDepth;
-  // steps t < n_steps - 4 stage and load entries of the list only; on split tiles
-  // the last four reach past it (the split's entries)
-  const int n_plain = split ? n_steps - 4 : n_steps;
+  // Barriers: 8 waves, one per pair of steps (an entry written at step t is read from
+  // step t + 2 on; the slot it overwrites, entry t - 3's, was last read before the
+  // previous barrier); 4 waves, one per step (written at t, read from t + 1; the slot
+  // it overwrites, entry t - 2's, was last read at step t - 2).  Steps t < n_plain
+  // stage and load entries of the list only; on split-last tiles the later ones reach
+  // past it (the split's first round)
+  constexpr bool kBar0 = !kPairs;
+  const int n_plain = c.split_tail ? c.n_list - kAhead - kDepth : n_steps;
   int t0 = 0;
   for (; t0 + 2 <= n_plain; t0 += 2) {
-    band_step<T, RAW, ANY, false, false>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
+    band_step<T, RAW, ANY, false, kBar0>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
     band_step<T, RAW, ANY, false, true>(c, ring, t0 + 1, rg, sb, c2, st[s1i], qf, o, m_run, l_run);
   }
   for (; t0 + 2 <= n_steps; t0 += 2) {
-    band_step<T, RAW, ANY, true, false>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
+    band_step<T, RAW, ANY, true, kBar0>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
     band_step<T, RAW, ANY, true, true>(c, ring, t0 + 1, rg, sb, c2, st[s1i], qf, o, m_run, l_run);
   }
   if (t0 < n_steps)
-    band_step<T, RAW, ANY, true, false>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
+    band_step<T, RAW, ANY, true, kBar0>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
 
   // the split's queries (rows 0 .. 31 below G; rows from n_b on are computed but not
   // published) go out before the epilogue, which hides their latency
-  const bool do_split = split && c.nb > 0;
-  v8 qg0[4];
-  if (do_split)
+  const bool tail = do_split && !sfirst;
+  if (tail)
     load_q<T>(qg0, (const T*)a.qg + ((size_t)c.bh * a.G + (n < a.G ? n : 0)) * 64, n < a.G);
 
   // epilogue: normalise and store the local rows
@@ -890,23 +988,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   }
 
-  // the global-row split: list entries n_list, n_list + 1 are in the ring,
-  // n_list + 2, n_list + 3 in the register sets; then the ticket
-  if (do_split) {
+  // split last: list entries n_list .. n_list + kStaged - 1 are in the ring, the
+  // rest of the round in the register sets
+  if (tail) {
     __syncthreads();   // band reads done
     // entry e sits in set e % 2: a uniform branch keeps the set index static (an
     // index known only at run time would put the sets in scratch memory)
-    const int e2 = c.n_list + 2;
-    if ((e2 & 1) == 0) {
-      store_entry<T, RAW, ANY, true>(ring[e2 % kRing], st[0], c, e2);
-      store_entry<T, RAW, ANY, true>(ring[(e2 + 1) % kRing], st[1], c, e2 + 1);
+    const int ef = c.n_list + kStaged;
+    if constexpr (kSplitEnt - kStaged == 2) {
+      if ((ef & 1) == 0) {
+        store_entry<T, RAW, ANY, true>(ring[ef % kRing], st[0], c, ef);
+        store_entry<T, RAW, ANY, true>(ring[(ef + 1) % kRing], st[1], c, ef + 1);
+      } else {
+        store_entry<T, RAW, ANY, true>(ring[ef % kRing], st[1], c, ef);
+        store_entry<T, RAW, ANY, true>(ring[(ef + 1) % kRing], st[0], c, ef + 1);
+      }
     } else {
-      store_entry<T, RAW, ANY, true>(ring[e2 % kRing], st[1], c, e2);
-      store_entry<T, RAW, ANY, true>(ring[(e2 + 1) % kRing], st[0], c, e2 + 1);
+      if ((ef & 1) == 0)
+        store_entry<T, RAW, ANY, true>(ring[ef % kRing], st[0], c, ef);
+      else
+        store_entry<T, RAW, ANY, true>(ring[ef % kRing], st[1], c, ef);
     }
     __syncthreads();
     global_split_run<T, RAW, ANY, true>(a, c, c.tile, ring, c.n_list % kRing, qg0);
-    const int ticket = take_ticket<T>(a, c);
+    ticket = take_ticket<T>(a, c);
+  }
+  // the workgroup whose ticket completed the (b, h) merges the partials
+  if (do_split) {
     __shared__ int s_last;
     if (threadIdx.x == 0) s_last = ticket == a.n_split - 1;
     __syncthreads();
@@ -914,7 +1022,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   }
 }
 
-#ifndef LF_ATTN_GWG_TU
+#if !defined(LF_ATTN_GWG_TU) && !defined(LF_ATTN_W4_TU)
+static_assert(kWaves == 8, "the main translation unit holds the 8-wave layout");
+
 // Compute units of the current device (cached per device).
 int cu_count() {
   static int cache[64];
@@ -925,6 +1035,17 @@ int cu_count() {
   if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   if (dev >= 0 && dev < 64) cache[dev] = n;
   return n;
+}
+
+// The 4-wave layout for sequences of at least 8192 tokens, where its overlap of two
+// workgroups per CU gains more than its extra band-halo staging costs (measured: 3 to
+// 21 % faster from S = 8192 on, up to 20 % slower at S = 4096).  LF_ATTN_WAVES=4 or 8
+// (read on every call) forces a layout.
+bool layout_w4(int S) {
+  const char* f = getenv("LF_ATTN_WAVES");
+  if (f && f[0] == '4' && f[1] == 0) return true;
+  if (f && f[0] == '8' && f[1] == 0) return false;
+  return S >= 8192;
 }
 
 template <typename T>
@@ -938,20 +1059,29 @@ hipError_t launch_t(const AttnArgs& args, hipStream_t st) {
   const char* no_gwg = getenv("LF_ATTN_NO_GWG");
   const bool gwg = a.G > 0 && band + (int64_t)a.B * a.H <= cu_count() &&
                    !(no_gwg && no_gwg[0] == '1');
+  const bool w4 = !gwg && layout_w4(a.S);
   if (gwg) {
     a.n_split = 1;
     a.split_len = (a.S + kBlk * kWaves - 1) / (kBlk * kWaves) * (kBlk * kWaves);
   }
+  a.wg_per_gen = cu_count();
   const int64_t grid = band + (gwg ? (int64_t)a.B * a.H : 0);
-  if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  if (a.G > 0 && (a.split_len % (kBlk * kWaves) != 0 || a.n_split > n_tiles))
-    return hipErrorInvalidConfiguration;
+  if (!w4) {
+    if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (a.G > 0 && (a.split_len % (kBlk * kWaves) != 0 || a.n_split > n_tiles))
+      return hipErrorInvalidConfiguration;
+  }
   if ((int64_t)a.S * 128 > 0x7fffffff) return hipErrorInvalidValue;   // per-head buffer range
   if (a.ev_begin) {
     hipError_t e0 = hipEventRecord(a.ev_begin, st);
     if (e0 != hipSuccess) return e0;
   }
-  if (gwg) {
+  if (w4) {
+    // the 4-wave layout, instantiated in a translation unit of its own
+    // (attn_mfma_w4.hip); it checks its own grid and split plan
+    const hipError_t ew = launch_attention_w4(a, st);
+    if (ew != hipSuccess) return ew;
+  } else if (gwg) {
     // instantiated in a translation unit of its own (attn_mfma_gwg.hip), so that the
     // code of the kernels below does not change with it
     const hipError_t eg = launch_attention_gwg(a, n_tiles, (unsigned)grid, st);
@@ -968,7 +1098,7 @@ hipError_t launch_t(const AttnArgs& args, hipStream_t st) {
   if (a.ev_end) e = hipEventRecord(a.ev_end, st);
   return e;
 }
-#else
+#elif defined(LF_ATTN_GWG_TU)
 template <typename T>
 void launch_gwg_t(const AttnArgs& a, int n_tiles, unsigned grid, hipStream_t st) {
   if (a.raw && a.any_pos)
@@ -978,17 +1108,36 @@ void launch_gwg_t(const AttnArgs& a, int n_tiles, unsigned grid, hipStream_t st)
   else
     attn_mfma_kernel<T, false, false, true><<<grid, kThreads, 0, st>>>(a, n_tiles);
 }
+#else
+static_assert(kWaves == 4, "attn_mfma_w4.hip holds the 4-wave layout");
+template <typename T>
+hipError_t launch_w4_t(const AttnArgs& a, hipStream_t st) {
+  const int n_tiles = (a.S + kTile - 1) / kTile;
+  const int64_t grid = (int64_t)a.B * a.H * n_tiles;
+  if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (a.G > 0 && (a.split_len % (kBlk * kWaves) != 0 || a.n_split > n_tiles))
+    return hipErrorInvalidConfiguration;
+  if (a.raw && a.any_pos)
+    attn_mfma_kernel<T, true, true, false><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles);
+  else if (a.raw)
+    attn_mfma_kernel<T, true, false, false><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles);
+  else
+    attn_mfma_kernel<T, false, false, false><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles);
+  return hipGetLastError();
+}
 #endif
 
 }  // namespace
 
-#ifndef LF_ATTN_GWG_TU
+#if !defined(LF_ATTN_GWG_TU) && !defined(LF_ATTN_W4_TU)
 void attn_split_plan(int S, int* n_split, int* split_len) {
-  // one split per 256-row tile, at most 32 splits per (b, h); splits are whole
-  // rounds of 8 x 32 keys
-  const int n_tiles = (S + kTile - 1) / kTile;
+  // one split per tile (256 rows, or 128 in the 4-wave layout), at most 32 splits per
+  // (b, h); splits are whole rounds of (waves x 32) keys
+  const bool w4 = layout_w4(S);
+  const int tile = w4 ? kTile / 2 : kTile;
+  const int unit = w4 ? kBlk * kWaves / 2 : kBlk * kWaves;
+  const int n_tiles = (S + tile - 1) / tile;
   const int want = n_tiles < kMaxSplit ? n_tiles : kMaxSplit;
-  const int unit = kBlk * kWaves;
   int len = (S + want - 1) / want;
   len = (len + unit - 1) / unit * unit;
   *split_len = len;
@@ -1003,11 +1152,19 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
-#else
+#elif defined(LF_ATTN_GWG_TU)
 hipError_t launch_attention_gwg(const AttnArgs& a, int n_tiles, unsigned grid, hipStream_t st) {
   switch (a.dtype) {
     case 1: launch_gwg_t<f16>(a, n_tiles, grid, st); return hipGetLastError();
     case 2: launch_gwg_t<bf16>(a, n_tiles, grid, st); return hipGetLastError();
+  }
+  return hipErrorInvalidValue;
+}
+#else
+hipError_t launch_attention_w4(const AttnArgs& a, hipStream_t st) {
+  switch (a.dtype) {
+    case 1: return launch_w4_t<f16>(a, st);
+    case 2: return launch_w4_t<bf16>(a, st);
   }
   return hipErrorInvalidValue;
 }

@@ -30,6 +30,9 @@ struct AttnArgs {
   int* counters;          // [B*H] split tickets: zero on entry, left zero on exit
   int n_split;            // key splits of the global rows
   int split_len;          // keys per split (multiple of 128)
+  int wg_per_gen;         // workgroups the dispatcher places before any CU gets a second
+                          // (the CU count; set by the launch): in the 4-wave layout,
+                          // consecutive generations pair up on the CUs
   hipEvent_t ev_begin;    // if non-null: recorded right before / after the main kernel
   hipEvent_t ev_end;
 };
@@ -75,6 +78,9 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
 // The attention kernel with one extra workgroup per (b, h) for the global rows (grid =
 // band tiles + B * H; a.n_split == 1): attn_mfma_gwg.hip.
 hipError_t launch_attention_gwg(const AttnArgs& a, int n_tiles, unsigned grid, hipStream_t st);
+// The 4-wave layout (attn_mfma_w4.hip): 128-row workgroups, two per CU; split plan as
+// attn_split_plan gives it for long sequences.
+hipError_t launch_attention_w4(const AttnArgs& a, hipStream_t st);
 hipError_t launch_attention_fp32(const AttnArgs& a, hipStream_t st);
 
 // Mask precondition check: writes 4 ints to `flags` (device): bad local value,

@@ -142,6 +142,28 @@ def test_scattered_globals_full_output_split_path(lf, dtype, ci, monkeypatch):
     _compare_full(lf, inp, W, G, dtype, f"scatter-split {ci}")
 
 
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("ci", range(len(SCATTER_CASES)))
+def test_scattered_globals_full_output_4wave_layout(lf, dtype, ci, monkeypatch):
+    # the 4-wave layout long sequences take (LF_ATTN_WAVES=4), with the key-split path
+    monkeypatch.setenv("LF_ATTN_WAVES", "4")
+    monkeypatch.setenv("LF_ATTN_NO_GWG", "1")
+    inp, W, G = _scatter_inputs(ci, dtype)
+    _compare_full(lf, inp, W, G, dtype, f"scatter-4wave {ci}")
+
+
+@pytest.mark.parametrize("layout", ["4", "8"])
+def test_scattered_globals_long_sequence_both_layouts(lf, layout, monkeypatch):
+    # 8192 tokens, 16 globals spread over the sequence, 8 heads: 512 workgroups in the
+    # 4-wave layout (the second dispatch generation runs its split first), splits of
+    # two rounds over gathered global entries
+    monkeypatch.setenv("LF_ATTN_WAVES", layout)
+    B, H, S, W, G = 1, 8, 8192, 512, 16
+    pos = _positions(8192, B, S, G)
+    inp = workloads.random_attention_inputs(8192, B, H, S, W, G, "fp16", global_positions=pos)
+    _compare_full(lf, inp, W, G, "fp16", f"scatter-long-{layout}wave")
+
+
 def test_scattered_globals_stress_scale_fp16(lf):
     # N(0,1) inputs: large scores exercise the running max and its rescaling
     B, H, S, W, G = 1, 2, 1024, 256, 16

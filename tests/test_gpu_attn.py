@@ -108,6 +108,37 @@ def test_attention_parity_mid_split_path(lf, dtype, case, monkeypatch):
     _full_compare(lf, inp, W, G, dtype, f"mid-split B{B}H{H}S{S}W{W}G{G}")
 
 
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}H{c[1]}S{c[2]}W{c[3]}G{c[4]}" for c in CASES])
+def test_attention_parity_mid_4wave_layout(lf, dtype, case, monkeypatch):
+    # the 4-wave layout (128-row workgroups, 4-slot ring, a barrier per step) that long
+    # sequences take, forced on these shapes (LF_ATTN_WAVES=4, with the key-split path)
+    monkeypatch.setenv("LF_ATTN_WAVES", "4")
+    monkeypatch.setenv("LF_ATTN_NO_GWG", "1")
+    B, H, S, W, G, pad, ng = case
+    inp = workloads.random_attention_inputs(zlib.crc32(repr(case).encode()) % 100000, B, H, S, W, G, dtype,
+                                            pad_frac=pad, n_global=ng)
+    _full_compare(lf, inp, W, G, dtype, f"mid-4wave B{B}H{H}S{S}W{W}G{G}")
+
+
+LONG_CASES = [
+    # B, H, S, W, G, pad: 512 workgroups in the 4-wave layout (two dispatch
+    # generations: the second runs its split first), splits of 2 rounds, 2 query blocks
+    (1, 8, 8192, 256, 40, None),
+    (1, 8, 8192, 512, 8, (0.05, 0.15)),
+]
+
+
+@pytest.mark.parametrize("layout", ["4", "8"])
+@pytest.mark.parametrize("case", LONG_CASES, ids=[f"B{c[0]}H{c[1]}S{c[2]}W{c[3]}G{c[4]}" for c in LONG_CASES])
+def test_attention_parity_long_both_layouts(lf, case, layout, monkeypatch):
+    monkeypatch.setenv("LF_ATTN_WAVES", layout)
+    B, H, S, W, G, pad = case
+    inp = workloads.random_attention_inputs(zlib.crc32(repr(case).encode()) % 100000, B, H, S, W, G, "fp16",
+                                            pad_frac=pad)
+    _full_compare(lf, inp, W, G, "fp16", f"long-{layout}wave B{B}H{H}S{S}W{W}G{G}")
+
+
 # unit roundoff of the output / probability type
 UNIT = {"fp16": 2.0 ** -11, "bf16": 2.0 ** -8}
 
@@ -254,4 +285,22 @@ def test_full_workload_every_element(lf, wl):
     del g, out, out2
     ref = _oracle(inp, wl.W, wl.G)
     err = report(wl.name, got.double().numpy(), ref, TOL[wl.dtype])
+    assert err <= TOL[wl.dtype], f"{wl.name}: max abs err {err:.3e}"
+
+
+@pytest.mark.parametrize("wl", workloads.ATTN_WORKLOADS[1:], ids=lambda w: w.name)
+def test_full_workload_other_layout_every_element(lf, wl, monkeypatch):
+    # the same workloads in the layout their sequence length does not select (4 waves
+    # at S = 4096, 8 waves at S = 16384): both layouts at full size
+    monkeypatch.setenv("LF_ATTN_WAVES", "4" if wl.S < 8192 else "8")
+    inp = workloads.make_attention_inputs(wl)
+    g = _gpu(inp)
+    out = _run(lf, g, wl.W, wl.G)
+    torch.cuda.synchronize()
+    got = out.cpu()
+    assert torch.isfinite(got.float()).all()
+    _check_padded_zero(got, inp["local_mask"])
+    del g, out
+    ref = _oracle(inp, wl.W, wl.G)
+    err = report(wl.name + " other layout", got.double().numpy(), ref, TOL[wl.dtype])
     assert err <= TOL[wl.dtype], f"{wl.name}: max abs err {err:.3e}"
