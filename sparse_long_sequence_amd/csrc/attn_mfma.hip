@@ -966,7 +966,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     load_q<T>(qg0, (const T*)a.qg + ((size_t)c.bh * a.G + (n < a.G ? n : 0)) * 64, n < a.G);
 
   // epilogue: normalise and store the local rows
-  {
+  auto epilogue = [&]() {
     typedef typename Frag<T>::v4 v4;
     const float l_tot = cross_half_sum(l_run);
     // global rows are written by the combine
@@ -986,10 +986,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
         }
       }
     }
-  }
+  };
 
-  // split last: list entries n_list .. n_list + kStaged - 1 are in the ring, the
-  // rest of the round in the register sets
+  // split last, before the output stores: the ticket waits for every store of the wave
+  // to complete, so the partial is published and the ticket taken while no output
+  // store is in flight yet (the band accumulators stay in registers meanwhile); list
+  // entries n_list .. n_list + kStaged - 1 are in the ring, the rest of the round in
+  // the register sets
+  if (!tail) epilogue();
   if (tail) {
     __syncthreads();   // band reads done
     // entry e sits in set e % 2: a uniform branch keeps the set index static (an
@@ -1012,6 +1016,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     __syncthreads();
     global_split_run<T, RAW, ANY, true>(a, c, c.tile, ring, c.n_list % kRing, qg0);
     ticket = take_ticket<T>(a, c);
+    epilogue();
   }
   // the workgroup whose ticket completed the (b, h) merges the partials
   if (do_split) {
