@@ -38,6 +38,11 @@
  *    run in a workgroup of their own; otherwise they are split over the band tiles'
  *    workgroups and merged by the last one.  The two differ only in rounding order.
  *    LF_ATTN_NO_GWG=1 (read on every call) selects the second on every grid.
+ *    On the split path, sequences of 8192 tokens and more run 128-row workgroups,
+ *    two per CU, with the splits of alternate dispatch generations before or after
+ *    the band work; shorter ones run 256-row workgroups, one per CU.  The outputs
+ *    agree to rounding order; LF_ATTN_WAVES=4 or 8 (read on every call) forces the
+ *    128-row (4 waves) or the 256-row (8 waves) workgroups.
  *  - Return value: an lf_status.  LF_ERR_HIP means a HIP call failed while
  *    enqueuing; lf_last_error() (thread-local) holds the message.
  */
