@@ -142,13 +142,18 @@ __device__ inline int xcd_chunk(int i, int n) {
 }
 
 // Tile layout in LDS: rows of CH chunks of 16 B (8 k values each; CH = KS / 8), no
-// padding; slot s of row r holds chunk s ^ swz(r), swz(r) = r & 7 for 8-chunk rows,
-// (r >> 1) & 3 for 4-chunk rows, so the fragment reads of 8 consecutive rows (same
-// chunk) fall in 8 different 16-byte bank groups.  Load i of wave w fills chunks
-// (NL w + i) 64 + lane, i.e. row (64 / CH) (NL w + i) + lane / CH, slot lane % CH.
+// padding; slot s of row r holds chunk s ^ swz(r).  The LDS serves a 16-byte read 16
+// lanes at a time over 64 four-byte banks (measured on gfx950: a wave-wide
+// ds_read_b128 costs 5.6 cycles when those 16 lanes cover all 64 banks, 8.0 with
+// two-way conflicts), and a fragment read gives its 16 lanes 16 consecutive rows of
+// one chunk.  With 128-byte rows (CH = 8) a row's bank groups are 8 (r & 1) + slot,
+// so the slot must differ between the 8 even rows and between the 8 odd rows:
+// swz(r) = (r >> 1) & 7.  With 64-byte rows (CH = 4) the groups are 4 (r & 3) +
+// slot: swz(r) = (r >> 2) & 3.  Load i of wave w fills chunks (NL w + i) 64 + lane,
+// i.e. row (64 / CH) (NL w + i) + lane / CH, slot lane % CH.
 template <int CH>
 __device__ inline int swz(int r) {
-  return CH == 8 ? (r & 7) : ((r >> 1) & 3);
+  return CH == 8 ? ((r >> 1) & 7) : ((r >> 2) & 3);
 }
 
 template <typename T, int NL>
@@ -255,22 +260,26 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs g0, GemmArgs 
   const rsrc_t ra = make_rsrc(g.a, 0x7fffffff);
   const rsrc_t rw = make_rsrc(g.w, 0x7fffffff);
   const int lrow = lane / CH;
-  const int lchunk = (lane % CH) ^ swz<CH>(lrow);   // rows start at multiples of RPL
+  // global chunk of this lane's 16 bytes in tile row r: the swizzle of that row
+  auto lchunk = [&](int r) { return (lane % CH) ^ swz<CH>(r); };
   const int kspan = g.K / g.splits, k0 = split * kspan;
   int aoff[NLA], woff[NLW];
 #pragma unroll
   for (int i = 0; i < NLA; ++i) {
-    const int m = m0 + RPL * (NLA * wave + i) + lrow;
+    const int r = RPL * (NLA * wave + i) + lrow;
+    const int m = m0 + r;
     int arow = m;
     if (g.a_group > 0 && m < g.M) {
       const int base = (m / g.a_group) * g.a_group_stride;
       arow = base + (g.a_rows ? g.a_rows[base + m % g.a_group] : m % g.a_group);
     }
-    aoff[i] = m < g.M ? (arow * g.lda + k0 + EPC * lchunk) * (int)sizeof(T) : -1;
+    aoff[i] = m < g.M ? (arow * g.lda + k0 + EPC * lchunk(r)) * (int)sizeof(T) : -1;
   }
 #pragma unroll
-  for (int i = 0; i < NLW; ++i)
-    woff[i] = ((n0 + RPL * (NLW * wave + i) + lrow) * g.ldw + k0 + EPC * lchunk) * (int)sizeof(T);
+  for (int i = 0; i < NLW; ++i) {
+    const int r = RPL * (NLW * wave + i) + lrow;
+    woff[i] = ((n0 + r) * g.ldw + k0 + EPC * lchunk(r)) * (int)sizeof(T);
+  }
 
   const int wm = (wave % WAVES_M) * WM, wn = (wave / WAVES_M) * WN;
   f32x16 acc[NI][MI];   // [n sub-tile][m sub-tile]
