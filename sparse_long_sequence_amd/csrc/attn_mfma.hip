@@ -97,6 +97,11 @@ constexpr int kSc1 = 16;             // cache-policy bit of coherent (write-thro
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;  // running-max start: finite, so exp2 never sees inf-inf
 constexpr float kLazy = 8.0f;        // move the max only when it grows by more than 2^8
+// Helper waves (8-wave layout): four more waves, one per SIMD, compute the workgroup's
+// key split of the global rows while the band waves run the band loop.
+constexpr int kHelp = 4;
+constexpr int kHelpKeys = 64;        // split keys per helper wave (two 32-key blocks)
+constexpr int kHelpSpin = 1 << 22;   // bound of a helper's wait for its predecessor in the merge
 
 template <typename T>
 struct Slot {
@@ -752,13 +757,287 @@ __device__ void global_rows_wg(const AttnArgs& a, Slot<T>* ring, int bh) {
   global_combine<T, RAW, ANY>(a, c);
 }
 
+// ------------------------------------------------------------------ helper waves
+constexpr int kMergeRows = 16;   // query rows per pass of the helpers' merge
+// LDS of the helper waves: the states of helpers 0 .. 2 for one pass of the merge
+// (layout of a wave state: m, l, pad, pad, o[64] per row), the merge's counters and
+// the ticket's outcome.
+struct HelpLds {
+  float st[kHelp - 1][kMergeRows * kStPitch];
+  int written;   // states written by helpers 0 .. 2, over all passes
+  int read;      // passes helper 3 has read
+  int last;      // this workgroup's ticket completed the (b, h)
+};
+
+// Rows of the global-row combine (every split's partial merged, the global rows
+// written), lanes t0, t0 + stride, .. of the calling threads: thread per (row, 4
+// dims); the (m, l) and o of 16 splits per round are loaded together with coherent
+// (sc1) loads.  No barrier: used by one helper wave.
+template <typename T, bool RAW, bool ANY>
+__device__ void combine_rows(const AttnArgs& a, const Ctx<T>& c, int t0, int stride) {
+  const int G = c.G, nb = c.nb, ns = a.n_split;
+  const float* pbase = a.partials + (size_t)c.bh * ns * (size_t)G * kPartPitch;
+  const rsrc_t rall = make_rsrc(pbase, (uint32_t)ns * G * kPartPitch * 4u);
+  const int sstride = G * kPartPitch * 4;   // bytes between splits
+  T* outh = (T*)a.out + (size_t)c.b * a.out_sb + (size_t)c.h * a.out_sh;
+  for (int idx = t0; idx < nb * 16; idx += stride) {
+    const int rl = idx >> 4, d4 = (idx & 15) * 4;
+    const int pos = RAW && !ANY ? rl : a.gidx[(size_t)c.b * c.S + rl];
+    const T mval = c.mask[pos];
+    const int off_ml = rl * kPartPitch * 4, off_o = (rl * kPartPitch + 4 + d4) * 4;
+    float M = kNegBig, L = 0.0f;
+    f32x4 O = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int h = 0; h < ns; h += 16) {
+      u32x2 ml[16];
+      u32x4 pv[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const bool ok = h + j < ns;
+        ml[j] = __builtin_amdgcn_raw_buffer_load_b64(rall, ok ? (h + j) * sstride + off_ml : -1, 0, kSc1);
+        pv[j] = __builtin_amdgcn_raw_buffer_load_b128(rall, ok ? (h + j) * sstride + off_o : -1, 0, kSc1);
+      }
+      float m[16];
+      float mh = M;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        m[j] = h + j < ns ? __uint_as_float(ml[j][0]) : kNegBig;
+        mh = fmaxf(mh, m[j]);
+      }
+      const float sc = fast_exp2(M - mh);
+      L *= sc;
+      O *= sc;
+      M = mh;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float w = h + j < ns ? fast_exp2(m[j] - M) : 0.0f;
+        L += __uint_as_float(ml[j][1]) * w;
+        O += __builtin_bit_cast(f32x4, pv[j]) * w;
+      }
+    }
+    const float inv = mask_live<RAW>(Elem<T>::to_f(mval)) ? 1.0f / L : 0.0f;
+    typename Frag<T>::v4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = Elem<T>::from_f(O[i] * inv);
+    *(typename Frag<T>::v4*)(outh + (size_t)pos * a.out_ss + d4) = w;
+  }
+}
+
+// Bounded wait of a helper wave until an LDS counter reaches `target` (every wave of
+// the workgroup is resident and the waits form no cycle, so it always ends).
+__device__ inline void help_wait(const int* ctr, int target) {
+  for (int it = 0; it < kHelpSpin; ++it) {
+    if (__hip_atomic_load(ctr, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) return;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// Helper wave hw (0 .. 3) of a band workgroup whose tile takes a key split of the
+// global rows (n_b <= 32 rows, one query block): keys sp_lo + 64 hw .. + 63 of kg / vg.
+// Its work is cut into phases between the barriers the band waves execute (n_bar of
+// them in all), so that no band wave waits for it:
+//   (with five or more barriers, the loads are issued after the first one, so they
+//   arrive during the band loop's first pair of steps instead of joining the
+//   launch's first burst of loads);
+//   work phase: S^T = K Q^T with the per-key term as accumulator init, the exact row
+//     max over its 64 keys, P rounded to T, O^T = V^T P^T, V^T formed on the matrix
+//     core from row-major V; helpers 0 .. 2 write their states to LDS and helper 3
+//     merges the four in a fixed order (so the result does not depend on timing) and
+//     publishes the partial with write-through stores, 16 rows per pass;
+//   ticket phase: helper 3 waits for its stores and takes the (b, h) ticket;
+//   combine phase: the helpers of the workgroup whose ticket completed the (b, h)
+//     merge all partials and write the global rows;
+// then the remaining barriers.
+template <typename T, bool RAW, bool ANY>
+__device__ void help_run(const AttnArgs& a, const Ctx<T>& c0, int n_bar, HelpLds& hl,
+                         const int* s_nb) {
+  typedef typename Frag<T>::v8 v8;
+  // the helper's work is short and sits on the band waves' barrier schedule: issue
+  // before the (older) band waves of the SIMD when both are ready
+  __builtin_amdgcn_s_setprio(2);
+  const int hw = wave_id() - kWaves;
+  const int lane = lane_id();
+  const int n = lane & 31, g = lane >> 5;
+  Ctx<T> c = c0;
+  const bool split = a.G > 0 && c.tile < a.n_split;
+  const int sp = c.tile;
+  const int k0 = sp * a.split_len + kHelpKeys * hw;   // first key of this helper
+  const int k_hi = min(c.S, sp * a.split_len + a.split_len);
+  const float c2 = a.scale * kLog2e;
+  const size_t head = (size_t)c.bh * c.S * 64;
+  const uint32_t bytes = (uint32_t)c.S * 128u;
+  const rsrc_t rk = make_rsrc((const T*)a.kg + head, bytes);
+  const rsrc_t rv = make_rsrc((const T*)a.vg + head, bytes);
+  const rsrc_t rm = make_rsrc(c.mask, (uint32_t)c.S * 2u);
+  const int n_wait = n_bar >= 5 ? 1 : 0;
+  // K and V rows in the A-operand layout (lane (n, g): key 32 j + n, dims 16 t + 8 g ..),
+  // 16-byte loads
+  v8 qf[4];
+  v8 kf[2][4], vr[2][4];
+  unsigned short mbits = 0;
+  auto issue_loads = [&]() {
+    load_q<T>(qf, (const T*)a.qg + ((size_t)c.bh * a.G + (n < a.G ? n : 0)) * 64, n < a.G);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int off = (k0 + 32 * j + n) * 128 + 2 * (16 * t + 8 * g);
+        kf[j][t] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+        vr[j][t] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+      }
+    mbits = __builtin_amdgcn_raw_buffer_load_b16(rm, 2 * (k0 + lane), 0, 0);
+  };
+  if (split && n_wait == 0) issue_loads();
+  if (hw == 0 && lane == 0) {
+    hl.written = 0;
+    hl.read = 0;
+  }
+  __syncthreads();   // barrier 0: the band prologue's
+  c.nb = __builtin_amdgcn_readfirstlane(*s_nb);
+  if (n_wait) {
+    if (split) issue_loads();
+    __syncthreads();   // barrier 1
+  }
+  const bool work = split && c.nb > 0;
+  if (work) {
+    // per-key term: live key of the split range with a live mask value
+    const bool live = k0 + lane < k_hi && mask_live<RAW>(Elem<T>::to_f(__builtin_bit_cast(T, mbits)));
+    const uint64_t lv = __ballot(live);
+    f32x16 sc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int kk = 32 * j + 8 * (v >> 2) + 4 * g + (v & 3);
+        sc[j][v] = (lv >> kk) & 1 ? 0.0f : -INFINITY;
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) sc[j] = mfma32(kf[j][t], qf[t], sc[j]);
+    }
+    // V^T fragments from the row-major V on the matrix core: D = V_rows x E, where the
+    // B operand E places dims 16 t' .. 16 t' + 15 at columns 16 t' (exact: every
+    // product is x * 1 or x * 0), leaves lane (n, g) holding dim 32 mb + n of keys
+    // 8 (v / 4) + 4 g + v % 4 of the block, which is the PV operand's key order
+    v8 e_lo, e_hi;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      e_lo[e] = Elem<T>::from_f(n == 8 * g + e ? 1.0f : 0.0f);
+      e_hi[e] = Elem<T>::from_f(n == 16 + 8 * g + e ? 1.0f : 0.0f);
+    }
+    const float m_h = fmaxf(cross_half_max(vmax(max16(sc[0]), max16(sc[1]))) * c2, kNegBig);
+    float l_h = 0.0f;
+    f32x16 o[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      VFrag<T> vv;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        f32x16 d = mfma32(vr[j][2 * mb], e_lo, f32x16{});
+        d = mfma32(vr[j][2 * mb + 1], e_hi, d);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const typename Frag<T>::v2 pp = cvt_pair<T>(d[8 * h + e], d[8 * h + e + 1]);
+            vv.a[h][mb][e] = pp[0];
+            vv.a[h][mb][e + 1] = pp[1];
+          }
+      }
+      v8 pf[2];
+      exp_p<T>(sc[j], m_h, c2, l_h, pf);
+      pv_frag<T>(vv, pf, o);
+    }
+    l_h = cross_half_sum(l_h);
+    // merge: 16 query rows per pass; helpers 0 .. 2 write their states, helper 3 merges
+    // them with its own in the order 0, 1, 2, 3 and publishes
+    const int r_valid = min(32, c.nb);
+    float* part = a.partials + ((size_t)c.bh * a.n_split + sp) * (size_t)c.G * kPartPitch;
+    const rsrc_t rpart = make_rsrc(part, (uint32_t)c.G * kPartPitch * 4u);
+    const int n_pass = (r_valid + kMergeRows - 1) / kMergeRows;
+    for (int ps = 0; ps < n_pass; ++ps) {
+      const int r = n - kMergeRows * ps;
+      const bool mine = r >= 0 && r < kMergeRows && n < r_valid;
+      if (hw < kHelp - 1) {
+        if (ps > 0) help_wait(&hl.read, ps);   // helper 3 has read the previous pass
+        if (mine) {
+          float* row = hl.st[hw] + r * kStPitch;
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+              *(f32x4*)&row[4 + 32 * mb + 8 * jj + 4 * g] =
+                  f32x4{o[mb][4 * jj], o[mb][4 * jj + 1], o[mb][4 * jj + 2], o[mb][4 * jj + 3]};
+          if (g == 0) {
+            row[0] = m_h;
+            row[1] = l_h;
+          }
+        }
+        // one count per wave (the release orders every lane's writes before it)
+        if (lane == 0) __hip_atomic_fetch_add(&hl.written, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      } else {
+        help_wait(&hl.written, (kHelp - 1) * (ps + 1));
+        if (mine) {
+          float mw[kHelp], M = m_h;
+#pragma unroll
+          for (int w = 0; w < kHelp - 1; ++w) {
+            mw[w] = hl.st[w][r * kStPitch];
+            M = fmaxf(M, mw[w]);
+          }
+          mw[kHelp - 1] = m_h;
+          float wt[kHelp], L = 0.0f;
+#pragma unroll
+          for (int w = 0; w < kHelp; ++w) {
+            wt[w] = fast_exp2(mw[w] - M);
+            L += (w < kHelp - 1 ? hl.st[w][r * kStPitch + 1] : l_h) * wt[w];
+          }
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              const int d = 4 + 32 * mb + 8 * jj + 4 * g;
+              f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+              for (int w = 0; w < kHelp - 1; ++w) acc += *(const f32x4*)&hl.st[w][r * kStPitch + d] * wt[w];
+              acc += f32x4{o[mb][4 * jj], o[mb][4 * jj + 1], o[mb][4 * jj + 2], o[mb][4 * jj + 3]} *
+                     wt[kHelp - 1];
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), rpart,
+                                                     (n * kPartPitch + d) * 4, 0, kSc1);
+            }
+          if (g == 0) {
+            const u32x2 ml = {__float_as_uint(M), __float_as_uint(L)};
+            __builtin_amdgcn_raw_buffer_store_b64(ml, rpart, n * kPartPitch * 4, 0, kSc1);
+          }
+        }
+        __hip_atomic_store(&hl.read, ps + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+    }
+  }
+  __syncthreads();   // barrier 1 + n_wait
+  if (work && hw == kHelp - 1) {
+    __builtin_amdgcn_s_waitcnt(0);   // the partial's write-through stores are complete
+    if (lane == 0) {
+      const int old = __hip_atomic_fetch_add(a.counters + c.bh, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // every split has published: the ticket is ready for the next launch
+      if (old == a.n_split - 1)
+        __hip_atomic_store(a.counters + c.bh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      hl.last = old == a.n_split - 1;
+    }
+  }
+  __syncthreads();   // barrier 2 + n_wait
+  // the four helpers of the workgroup that completed the (b, h) write its global rows
+  if (work && hl.last) combine_rows<T, RAW, ANY>(a, c, 64 * hw + lane, 64 * kHelp);
+  for (int i = 3 + n_wait; i < n_bar; ++i) __syncthreads();
+}
+
 // One step t of a wave: the two 32-key blocks of its entry.  LDS reads first
 // (K, V^T and per-key terms of both blocks), then QK^T, the band mask on edge
 // steps only, one running-max update for the 64 keys, P, PV, then the staging of
 // entry t + kAhead and the loads of entry t + kAhead + kDepth, then (BAR: second
 // step of a pair) the barrier.  Entries t .. t + 3 are read during the step and
 // t + 5 is written.
-template <typename T, bool RAW, bool ANY, bool PAST, bool BAR>
+// LATE_V (the helper-wave layout, 168 registers per wave): the V^T fragments are read
+// after the QK^T MFMAs are issued, into the registers the K fragments leave, and
+// arrive while the max and P are computed.
+template <typename T, bool RAW, bool ANY, bool PAST, bool BAR, bool LATE_V>
 __device__ __forceinline__ void band_step(const Ctx<T>& c, Slot<T>* ring, int tt, int rg, int sb,
                                           float c2, Stage<T>& set,
                                           const typename Frag<T>::v8 qf[4], f32x16 o[2],
@@ -770,10 +1049,17 @@ __device__ __forceinline__ void band_step(const Ctx<T>& c, Slot<T>* ring, int tt
   read_k<T>(kf1, cs, 1);
   const f32x16 c0 = read_bias<T>(cs, 0), c1 = read_bias<T>(cs, 1);
   VFrag<T> vf0, vf1;
-  read_v<T>(vf0, cs, 0);
-  read_v<T>(vf1, cs, 1);
+  if (!LATE_V) {
+    read_v<T>(vf0, cs, 0);
+    read_v<T>(vf1, cs, 1);
+  }
   f32x16 s0 = qk_frag_c<T>(kf0, qf, c0);
   f32x16 s1 = qk_frag_c<T>(kf1, qf, c1);
+  if (LATE_V) {
+    __builtin_amdgcn_sched_barrier(0);
+    read_v<T>(vf0, cs, 0);
+    read_v<T>(vf1, cs, 1);
+  }
   // blocks tq = 1 .. (W - 31) / 32 of a sub-block lie wholly inside the window of
   // every row; the others get the band mask
   const int tq0 = 2 * (tt - c.ngp) - sb;
@@ -800,9 +1086,14 @@ __device__ __forceinline__ void band_step(const Ctx<T>& c, Slot<T>* ring, int tt
 // RAW: read the raw masks (else global_count and the shifted mask); ANY (with RAW):
 // global tokens at any positions, through global_idx / global_count; GWG: workgroups
 // past the band tiles compute the global rows, and the band tiles run no split.
-template <typename T, bool RAW, bool ANY, bool GWG>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_mfma_kernel(AttnArgs a, int n_tiles) {
+// HELP (8 waves, at most 32 global tokens): four helper waves compute the tile's key
+// split of the global rows beside the band waves (help_run), and the band waves run no
+// split.
+template <typename T, bool RAW, bool ANY, bool GWG, bool HELP>
+__global__ __launch_bounds__(HELP ? kThreads + 64 * kHelp : kThreads)
+__attribute__((amdgpu_waves_per_eu(HELP ? 3 : 2, HELP ? 3 : 2))) void attn_mfma_kernel(AttnArgs a, int n_tiles) {
   __shared__ __attribute__((aligned(16))) Slot<T> ring[kRing];
+  __shared__ int s_nb;
   typedef typename Frag<T>::v8 v8;
   const int lane = lane_id();
   const int wave = wave_id();   // uniform: index math on the scalar unit
@@ -841,7 +1132,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   c.gi = ANY ? a.gidx + (size_t)c.b * c.S : nullptr;
   c.gm = ANY ? (const unsigned short*)a.global_mask + (size_t)c.b * c.S : nullptr;
   const float c2 = a.scale * kLog2e;
-  const bool split = !GWG && a.G > 0 && c.tile < a.n_split;
+  if constexpr (HELP) {
+    static_assert(kWaves == 8 && !GWG, "helper waves: 8-wave band tiles");
+    __shared__ __attribute__((aligned(16))) HelpLds hl;
+    if (wave >= kWaves) {   // uniform: the whole wave
+      // the band waves execute the prologue barrier and one per pair of steps
+      help_run<T, RAW, ANY>(a, c, 1 + n_steps / 2, hl, &s_nb);
+      return;
+    }
+  }
+  const bool split = !GWG && !HELP && a.G > 0 && c.tile < a.n_split;
   // 4-wave layout: two workgroups share a CU, and the dispatcher places one on every
   // CU before it places a second, so workgroups of consecutive dispatch generations
   // (wg_per_gen workgroups each) pair up.  Odd generations run their split before the
@@ -906,7 +1206,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
     __builtin_amdgcn_sched_barrier(0);
   }
   c.nb = counter ? count_globals<T, RAW, ANY>(a, c.b, gfirst) : 0;
-  __shared__ int s_nb;
   int ticket = 0;
   if constexpr (kWaves == 8) {
     // the first entries are written before the prologue barrier (wave 0 alone writes
@@ -949,15 +1248,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int n_plain = c.split_tail ? c.n_list - kAhead - kDepth : n_steps;
   int t0 = 0;
   for (; t0 + 2 <= n_plain; t0 += 2) {
-    band_step<T, RAW, ANY, false, kBar0>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
-    band_step<T, RAW, ANY, false, true>(c, ring, t0 + 1, rg, sb, c2, st[s1i], qf, o, m_run, l_run);
+    band_step<T, RAW, ANY, false, kBar0, HELP>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
+    band_step<T, RAW, ANY, false, true, HELP>(c, ring, t0 + 1, rg, sb, c2, st[s1i], qf, o, m_run, l_run);
   }
   for (; t0 + 2 <= n_steps; t0 += 2) {
-    band_step<T, RAW, ANY, true, kBar0>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
-    band_step<T, RAW, ANY, true, true>(c, ring, t0 + 1, rg, sb, c2, st[s1i], qf, o, m_run, l_run);
+    band_step<T, RAW, ANY, true, kBar0, HELP>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
+    band_step<T, RAW, ANY, true, true, HELP>(c, ring, t0 + 1, rg, sb, c2, st[s1i], qf, o, m_run, l_run);
   }
   if (t0 < n_steps)
-    band_step<T, RAW, ANY, true, kBar0>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
+    band_step<T, RAW, ANY, true, kBar0, HELP>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
 
   // the split's queries (rows 0 .. 31 below G; rows from n_b on are computed but not
   // published) go out before the epilogue, which hides their latency
@@ -1065,6 +1364,14 @@ hipError_t launch_t(const AttnArgs& args, hipStream_t st) {
   const bool gwg = a.G > 0 && band + (int64_t)a.B * a.H <= cu_count() &&
                    !(no_gwg && no_gwg[0] == '1');
   const bool w4 = !gwg && layout_w4(a.S);
+  // helper waves for the global rows: one query block (G <= 32), one 256-key split per
+  // tile, and at least three barriers in the band loop's schedule for their phases
+  // (LF_ATTN_NO_HELP=1, read on every call, keeps the band tiles' own split)
+  const int n_steps = (a.G + kEnt - 1) / kEnt + ((a.W + 2 * kBlk - 1) / kBlk + 2) / 2;
+  const char* no_help = getenv("LF_ATTN_NO_HELP");
+  const bool help = !gwg && !w4 && !a.any_pos && a.G > 0 && a.G <= 32 &&
+                    a.split_len == kHelp * kHelpKeys &&
+                    1 + n_steps / 2 >= 3 && !(no_help && no_help[0] == '1');
   if (gwg) {
     a.n_split = 1;
     a.split_len = (a.S + kBlk * kWaves - 1) / (kBlk * kWaves) * (kBlk * kWaves);
@@ -1091,12 +1398,18 @@ hipError_t launch_t(const AttnArgs& args, hipStream_t st) {
     // code of the kernels below does not change with it
     const hipError_t eg = launch_attention_gwg(a, n_tiles, (unsigned)grid, st);
     if (eg != hipSuccess) return eg;
+  } else if (help) {
+    constexpr int kHT = kThreads + 64 * kHelp;
+    if (a.raw)
+      attn_mfma_kernel<T, true, false, false, true><<<(unsigned)grid, kHT, 0, st>>>(a, n_tiles);
+    else
+      attn_mfma_kernel<T, false, false, false, true><<<(unsigned)grid, kHT, 0, st>>>(a, n_tiles);
   } else if (a.raw && a.any_pos) {
-    attn_mfma_kernel<T, true, true, false><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles);
+    attn_mfma_kernel<T, true, true, false, false><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles);
   } else if (a.raw) {
-    attn_mfma_kernel<T, true, false, false><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles);
+    attn_mfma_kernel<T, true, false, false, false><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles);
   } else {
-    attn_mfma_kernel<T, false, false, false><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles);
+    attn_mfma_kernel<T, false, false, false, false><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -1107,11 +1420,11 @@ hipError_t launch_t(const AttnArgs& args, hipStream_t st) {
 template <typename T>
 void launch_gwg_t(const AttnArgs& a, int n_tiles, unsigned grid, hipStream_t st) {
   if (a.raw && a.any_pos)
-    attn_mfma_kernel<T, true, true, true><<<grid, kThreads, 0, st>>>(a, n_tiles);
+    attn_mfma_kernel<T, true, true, true, false><<<grid, kThreads, 0, st>>>(a, n_tiles);
   else if (a.raw)
-    attn_mfma_kernel<T, true, false, true><<<grid, kThreads, 0, st>>>(a, n_tiles);
+    attn_mfma_kernel<T, true, false, true, false><<<grid, kThreads, 0, st>>>(a, n_tiles);
   else
-    attn_mfma_kernel<T, false, false, true><<<grid, kThreads, 0, st>>>(a, n_tiles);
+    attn_mfma_kernel<T, false, false, true, false><<<grid, kThreads, 0, st>>>(a, n_tiles);
 }
 #else
 static_assert(kWaves == 4, "attn_mfma_w4.hip holds the 4-wave layout");
@@ -1123,11 +1436,11 @@ hipError_t launch_w4_t(const AttnArgs& a, hipStream_t st) {
   if (a.G > 0 && (a.split_len % (kBlk * kWaves) != 0 || a.n_split > n_tiles))
     return hipErrorInvalidConfiguration;
   if (a.raw && a.any_pos)
-    attn_mfma_kernel<T, true, true, false><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles);
+    attn_mfma_kernel<T, true, true, false, false><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles);
   else if (a.raw)
-    attn_mfma_kernel<T, true, false, false><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles);
+    attn_mfma_kernel<T, true, false, false, false><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles);
   else
-    attn_mfma_kernel<T, false, false, false><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles);
+    attn_mfma_kernel<T, false, false, false, false><<<(unsigned)grid, kThreads, 0, st>>>(a, n_tiles);
   return hipGetLastError();
 }
 #endif

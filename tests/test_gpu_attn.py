@@ -96,12 +96,17 @@ def test_attention_parity_mid(lf, dtype, case):
     _full_compare(lf, inp, W, G, dtype, f"mid B{B}H{H}S{S}W{W}G{G}")
 
 
+@pytest.mark.parametrize("helpers", ["on", "off"])
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 @pytest.mark.parametrize("case", CASES, ids=[f"B{c[0]}H{c[1]}S{c[2]}W{c[3]}G{c[4]}" for c in CASES])
-def test_attention_parity_mid_split_path(lf, dtype, case, monkeypatch):
+def test_attention_parity_mid_split_path(lf, dtype, case, helpers, monkeypatch):
     # these grids leave CUs idle, so by default the global rows run in workgroups of
-    # their own; LF_ATTN_NO_GWG=1 sends them through the key-split path instead
+    # their own; LF_ATTN_NO_GWG=1 sends them through the key-split path instead, where
+    # helper waves compute each tile's split (G <= 32, W >= 96) unless LF_ATTN_NO_HELP=1
+    # leaves it to the band waves
     monkeypatch.setenv("LF_ATTN_NO_GWG", "1")
+    if helpers == "off":
+        monkeypatch.setenv("LF_ATTN_NO_HELP", "1")
     B, H, S, W, G, pad, ng = case
     inp = workloads.random_attention_inputs(zlib.crc32(repr(case).encode()) % 100000, B, H, S, W, G, dtype,
                                             pad_frac=pad, n_global=ng)
@@ -230,6 +235,63 @@ def test_deterministic_and_guard_bands_untouched(lf):
     torch.cuda.synchronize()
     assert torch.equal(first.view(torch.int16), out.view(torch.int16))
     assert torch.isnan(buf[:guard]).all() and torch.isnan(buf[guard + n:]).all()
+
+
+HISTORY_CASES = [
+    # B, H, S, W, G, pad: key-split path with helper waves (one and two 16-row passes of
+    # their merge), plus the longformer-large shape itself
+    (1, 2, 2048, 512, 8, None),
+    (2, 2, 1024, 256, 32, (0.05, 0.1)),
+    (1, 16, 4096, 512, 8, None),
+]
+
+
+@pytest.mark.parametrize("case", HISTORY_CASES, ids=[f"B{c[0]}H{c[1]}S{c[2]}W{c[3]}G{c[4]}" for c in HISTORY_CASES])
+def test_result_independent_of_earlier_calls(lf, case, monkeypatch):
+    # A call must not depend on what earlier launches left in LDS, the scratch buffer or
+    # the partials: the same inputs give the same bits after calls on other data of the
+    # same shape (which run on the same compute units with different values).
+    monkeypatch.setenv("LF_ATTN_NO_GWG", "1")
+    B, H, S, W, G, pad = case
+    mk = lambda seed: _gpu(workloads.random_attention_inputs(seed, B, H, S, W, G, "fp16", pad_frac=pad))
+    x, y, z = mk(101), mk(202), mk(303)
+    outs = []
+    for other in (None, y, z):
+        if other is not None:
+            _run(lf, other, W, G)
+        outs.append(_run(lf, x, W, G))
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(outs[0].view(torch.int16), o.view(torch.int16)), "result depends on earlier calls"
+
+
+@pytest.mark.parametrize("case", [c for c in CASES if 0 < c[4] <= 32 and c[3] >= 96],
+                         ids=lambda c: f"B{c[0]}H{c[1]}S{c[2]}W{c[3]}G{c[4]}")
+def test_helper_waves_match_band_tile_split(lf, case, monkeypatch):
+    # the same launch with the global-row split in helper waves and in the band waves:
+    # local rows are bit-identical (same band arithmetic); global rows differ in how the
+    # keys are grouped under one running max (P is rounded to the type relative to that
+    # max) and in the merge order, so each path is within u |out| + 2.001 u max|vg| of
+    # the exact result (the bound derived for the stress test) and the two are within
+    # twice that of each other
+    monkeypatch.setenv("LF_ATTN_NO_GWG", "1")
+    B, H, S, W, G, pad, ng = case
+    inp = workloads.random_attention_inputs(zlib.crc32(repr(case).encode()) % 100000, B, H, S, W, G, "fp16",
+                                            pad_frac=pad, n_global=ng)
+    g = _gpu(inp)
+    a = _run(lf, g, W, G).cpu()
+    monkeypatch.setenv("LF_ATTN_NO_HELP", "1")
+    b = _run(lf, g, W, G).cpu()
+    gm = inp["global_mask"]
+    u = UNIT["fp16"]
+    vmax = inp["vg"].double().abs().amax(dim=(2, 3))[:, :, None, None]
+    for bb in range(B):
+        glob = (gm[bb] == 0).numpy()
+        assert torch.equal(a[bb][:, ~glob].view(torch.int16), b[bb][:, ~glob].view(torch.int16))
+        d = (a[bb][:, glob].double() - b[bb][:, glob].double()).abs()
+        bound = 2 * (u * b[bb][:, glob].double().abs() + 2.001 * u * vmax[bb])
+        print(f"helpers vs band split, b={bb}: max |diff| {float(d.max()) if d.numel() else 0.0:.3e}")
+        assert torch.all(d <= bound)
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16", "fp32"])
