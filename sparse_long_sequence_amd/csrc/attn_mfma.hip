@@ -835,8 +835,8 @@ __device__ inline void help_wait(const int* ctr, int target) {
 // global rows (n_b <= 32 rows, one query block): keys sp_lo + 64 hw .. + 63 of kg / vg.
 // Its work is cut into phases between the barriers the band waves execute (n_bar of
 // them in all), so that no band wave waits for it:
-//   (with five or more barriers, the loads are issued after the first one, so they
-//   arrive during the band loop's first pair of steps instead of joining the
+//   loads (with five or more barriers they are issued after the first one and with
+//   six or more K and V go out one pair of steps apart, so they do not join the
 //   launch's first burst of loads);
 //   work phase: S^T = K Q^T with the per-key term as accumulator init, the exact row
 //     max over its 64 keys, P rounded to T, O^T = V^T P^T, V^T formed on the matrix
@@ -868,13 +868,16 @@ __device__ void help_run(const AttnArgs& a, const Ctx<T>& c0, int n_bar, HelpLds
   const rsrc_t rk = make_rsrc((const T*)a.kg + head, bytes);
   const rsrc_t rv = make_rsrc((const T*)a.vg + head, bytes);
   const rsrc_t rm = make_rsrc(c.mask, (uint32_t)c.S * 2u);
-  const int n_wait = n_bar >= 5 ? 1 : 0;
+  // with barriers to spare, the loads go out after the band waves' first burst of
+  // loads, K in the band loop's first pair of steps and V in the second, so that their
+  // 64 KB per workgroup spread over the loop's own traffic
+  const int n_wait = n_bar >= 6 ? 2 : n_bar >= 5 ? 1 : 0;
   // K and V rows in the A-operand layout (lane (n, g): key 32 j + n, dims 16 t + 8 g ..),
   // 16-byte loads
   v8 qf[4];
   v8 kf[2][4], vr[2][4];
   unsigned short mbits = 0;
-  auto issue_loads = [&]() {
+  auto issue_k = [&]() {   // the queries, K rows and the keys' mask values
     load_q<T>(qf, (const T*)a.qg + ((size_t)c.bh * a.G + (n < a.G ? n : 0)) * 64, n < a.G);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -882,11 +885,22 @@ __device__ void help_run(const AttnArgs& a, const Ctx<T>& c0, int n_bar, HelpLds
       for (int t = 0; t < 4; ++t) {
         const int off = (k0 + 32 * j + n) * 128 + 2 * (16 * t + 8 * g);
         kf[j][t] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
-        vr[j][t] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
       }
     mbits = __builtin_amdgcn_raw_buffer_load_b16(rm, 2 * (k0 + lane), 0, 0);
   };
-  if (split && n_wait == 0) issue_loads();
+  auto issue_v = [&]() {   // the V rows
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int off = (k0 + 32 * j + n) * 128 + 2 * (16 * t + 8 * g);
+        vr[j][t] = __builtin_bit_cast(v8, __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0));
+      }
+  };
+  if (split && n_wait == 0) {
+    issue_k();
+    issue_v();
+  }
   if (hw == 0 && lane == 0) {
     hl.written = 0;
     hl.read = 0;
@@ -894,8 +908,15 @@ __device__ void help_run(const AttnArgs& a, const Ctx<T>& c0, int n_bar, HelpLds
   __syncthreads();   // barrier 0: the band prologue's
   c.nb = __builtin_amdgcn_readfirstlane(*s_nb);
   if (n_wait) {
-    if (split) issue_loads();
+    if (split) {
+      issue_k();
+      if (n_wait == 1) issue_v();
+    }
     __syncthreads();   // barrier 1
+    if (n_wait == 2) {
+      if (split) issue_v();
+      __syncthreads();   // barrier 2
+    }
   }
   const bool work = split && c.nb > 0;
   if (work) {
