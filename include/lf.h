@@ -107,7 +107,9 @@ int lf_mask_shift(int dtype, const void* local_mask, int B, int S, void* local_b
  * row with one live key can reach, so excluding the key gives the same result, and the
  * kernels exclude it (-inf) instead of adding the bias.
  * fp16 / bf16: one launch on MFMA with fp32 accumulation, reading both masks itself.
- * fp32: the index extraction and mask shift, then the vector-ALU kernel.
+ * fp32: the index extraction and mask shift, then the vector-ALU kernel; when the
+ * global rows' keys are split (G > 0, sequences of more than one 256-row tile), a
+ * third launch combines their per-split partial states.
  * Scratch, per (device, stream), never waiting for the host: the split tickets of the
  * global-row merge sit in a slot of a static device array (64 slots per device, one per
  * stream that calls; zero-filled on the stream when the slot is handed out, left zero
@@ -128,7 +130,7 @@ int lf_attn_forward(int dtype, const void* q, const void* k, const void* v,
  * lf_attn_forward for callers that cannot allocate device memory: code under stream
  * capture, tight serving loops, harnesses that forbid allocation.  Same arguments,
  * computation, work split and results (bit for bit) as lf_attn_forward.  It calls no
- * allocator: its split tickets and global-row partials (fp32: the preprocessed masks)
+ * allocator: its split tickets and global-row partials (fp32: and the preprocessed masks)
  * live in one static device array per device, 32 MiB, held until the process ends
  * (lf_attn_forward_noalloc_max_scratch() bytes of it for partials, the rest for 16384
  * tickets).  The array's device address is looked up once per device (on the first
@@ -183,7 +185,8 @@ size_t lf_attn_workspace_bytes(int dtype, int B, int H, int S, int W, int G);
 /*
  * Same computation as lf_attn_forward on already-preprocessed masks: global_idx /
  * global_count from lf_init_global_idx and local_bias from lf_mask_shift.  It
- * allocates nothing and is one kernel launch.  `workspace` (device, 256-byte
+ * allocates nothing and is one kernel launch (fp32 with split global-row keys: two,
+ * the second combining the splits).  `workspace` (device, 256-byte
  * aligned, ws_bytes >= lf_attn_workspace_bytes) starts with B*H int32 split
  * tickets followed by the partial results of the global rows.  The tickets must be
  * zero before the first call that uses the workspace (zero-fill it once after

@@ -565,7 +565,8 @@ namespace {
 
 // Scratch of one lf_attn_forward-family call, as offsets into one region.  fp16 /
 // bf16: [tickets (with_tickets)][global-row partials (G > 0)][index, count (any_pos)];
-// fp32: [index][count][shifted mask] (the vector-ALU kernel reads preprocessed masks).
+// fp32: [index][count][shifted mask] (the vector-ALU kernel reads preprocessed masks)
+// [global-row partials (G > 0; combined by a second launch, no tickets)].
 struct AttnScratch {
   size_t tickets_off, partials_off, idx_off, cnt_off, bias_off, total;
 };
@@ -579,6 +580,11 @@ AttnScratch attn_scratch(int dtype, int B, int H, int S, int G, bool any_pos, bo
     c.idx_off = off; off += align256(n_bs * sizeof(int32_t));
     c.cnt_off = off; off += align256((size_t)B * sizeof(int32_t));
     c.bias_off = off; off += align256(n_bs * dtype_size(dtype));
+    if (G > 0) {
+      const AttnWs w = attn_ws(B, H, S, G);
+      c.partials_off = off;
+      off += w.total - w.partials_off;
+    }
     c.total = off;
     return c;
   }
@@ -622,8 +628,9 @@ hipError_t run_attn_forward(int dtype, const void* q, const void* k, const void*
     hipError_t he = lf::launch_prep(dtype, global_mask, local_mask, B, S, gidx, gcnt, bias,
                                     nullptr, 0, st);
     if (he != hipSuccess) return he;
+    if (G > 0) partials = (float*)(scratch + sc.partials_off);
     lf::AttnArgs a = make_args(dtype, q, k, v, qg, kg, vg, gidx, gcnt, bias, B, H, S, W, G, out,
-                               nullptr, nullptr, ws);
+                               nullptr, partials, ws);
     a.any_pos = any_pos ? 1 : 0;
     a.global_mask = global_mask;
     return run_attention(a, st);

@@ -1,6 +1,6 @@
 """Timing driver for the library's entry points on seeded synthetic inputs.
 
-    python sparse_long_sequence_amd/perf.py attn  [--iters N] [--shape large|padded|long]
+    python sparse_long_sequence_amd/perf.py attn  [--iters N] [--shape large|padded|long|tiny|large_fp32]
     python sparse_long_sequence_amd/perf.py attn_any [--iters N]  # same, 8 globals spread out
     python sparse_long_sequence_amd/perf.py prep  [--iters N]   # index compaction + mask shift
     python sparse_long_sequence_amd/perf.py layer [--iters N] [--dtype fp16|bf16|fp32]
@@ -60,7 +60,10 @@ def _time(fn, iters: int, warmup: int) -> float:
 
 
 ATTN_SHAPES = {"large": workloads.LARGE_FP16, "padded": workloads.PADDED_FP16,
-               "long": workloads.LONG_BF16}
+               "long": workloads.LONG_BF16, "tiny": workloads.TINY_FP32,
+               # the longformer-large shape in fp32 (vector-ALU attention)
+               "large_fp32": workloads.AttnWorkload("longformer_large_fp32_B1_H16_S4096_W512_G8",
+                                                    1, 16, 4096, 512, 8, "fp32", 20260002)}
 
 
 def run_attn(iters: int, warmup: int, shape: str = "large") -> dict:
