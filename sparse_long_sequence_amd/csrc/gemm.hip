@@ -305,17 +305,49 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_kernel(GemmArgs g0, GemmArgs 
     if (ks + D < nk) issue(std::integral_constant<int, j + D>{}, ks + D);
     const T* ca = abuf(J);
     const T* cw = wbuf(J);
+    // 256 x 256 tiles (8 MFMAs per round): fragments in two register sets, the reads
+    // of round kk + 1 out before the MFMAs of round kk, so their latency hides behind
+    // those MFMAs (1 % on the encoder layer; the smaller tiles were slower with it)
+    constexpr int NKK = KS / (2 * EPC);   // rounds of two chunks (the g halves)
+    constexpr bool kPipe = NI * MI >= 8;
+    v8 wf[2][NI], xf[2][MI];
+    auto read_round = [&](int kk, v8* w_, v8* x_) {
 #pragma unroll
-    for (int kk = 0; kk < KS / (2 * EPC); ++kk) {   // two chunks (the g halves) per round
-      v8 wf[NI], xf[MI];
+      for (int i = 0; i < NI; ++i) w_[i] = frag(cw, wn + 32 * i + n, 2 * kk + gq);
 #pragma unroll
-      for (int i = 0; i < NI; ++i) wf[i] = frag(cw, wn + 32 * i + n, 2 * kk + gq);
+      for (int q = 0; q < MI; ++q) x_[q] = frag(ca, wm + 32 * q + n, 2 * kk + gq);
+    };
+    if constexpr (kPipe) {
+      read_round(0, wf[0], xf[0]);
 #pragma unroll
-      for (int q = 0; q < MI; ++q) xf[q] = frag(ca, wm + 32 * q + n, 2 * kk + gq);
+      for (int kk = 0; kk < NKK; ++kk) {
+        if (kk + 1 < NKK) read_round(kk + 1, wf[(kk + 1) & 1], xf[(kk + 1) & 1]);
 #pragma unroll
-      for (int i = 0; i < NI; ++i)
+        for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int q = 0; q < MI; ++q) acc[i][q] = mfma32(wf[i], xf[q], acc[i][q]);
+          for (int q = 0; q < MI; ++q)
+            acc[i][q] = mfma32(wf[kk & 1][i], xf[kk & 1][q], acc[i][q]);
+      }
+      // the order for the scheduler (it would otherwise sink each round's reads below
+      // the previous round's MFMAs, into the same registers): rounds 0 and 1 read,
+      // then per round its MFMAs followed by the next-but-one round's reads
+      constexpr int RD = NI + MI;                                   // LDS reads per round
+      constexpr int MF = NI * MI * (sizeof(T) == 4 ? 4 : 1);        // MFMAs per round
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * RD, 0);
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        __builtin_amdgcn_sched_group_barrier(0x008, MF, 0);
+        if (kk + 2 < NKK) __builtin_amdgcn_sched_group_barrier(0x100, RD, 0);
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        read_round(kk, wf[0], xf[0]);
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+          for (int q = 0; q < MI; ++q) acc[i][q] = mfma32(wf[0][i], xf[0][q], acc[i][q]);
+      }
     }
     if (ks + D < nk) wait_vm<(D - 1) * NL>();
     else wait_vm<0>();
