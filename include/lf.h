@@ -43,11 +43,13 @@
  *    the band work; shorter ones run 256-row workgroups, one per CU.  The outputs
  *    agree to rounding order; LF_ATTN_WAVES=4 or 8 (read on every call) forces the
  *    128-row (4 waves) or the 256-row (8 waves) workgroups.  In the 256-row
- *    workgroups with at most 32 leading global tokens (and W >= 96), four more
+ *    workgroups with at most 32 leading global tokens (and W >= 160), four more
  *    waves compute the tile's key split of the global rows, its merge and the last
- *    tile's combine while the band waves run the band loop; LF_ATTN_NO_HELP=1
- *    (read on every call) leaves the split to the band waves, after their loop.
- *    Local rows are bit-identical either way; global rows agree to rounding.
+ *    tile's combine while the band waves run the band loop, and the band waves take
+ *    the global keys inside their first and last band steps (blocks there that lie
+ *    outside every row's window) rather than in a step of their own;
+ *    LF_ATTN_NO_HELP=1 (read on every call) leaves the split to the band waves,
+ *    after their loop.  Local and global rows agree to rounding order either way.
  *  - Return value: an lf_status.  LF_ERR_HIP means a HIP call failed while
  *    enqueuing; lf_last_error() (thread-local) holds the message.
  */

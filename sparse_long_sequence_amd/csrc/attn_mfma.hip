@@ -410,7 +410,7 @@ __device__ inline void load_q(typename Frag<T>::v8 qf[4], const T* __restrict__ 
 // ------------------------------------------------------------------ workgroup context
 template <typename T>
 struct Ctx {
-  int b, h, bh, tile, S, W, G, nb, ngp, r0, kbase, n_list;
+  int b, h, bh, tile, S, W, G, nb, ngp, r0, kbase, n_list, npb;
   bool split;                // this tile runs a key split of the global rows
   bool split_tail;           // ... after its band work (its first round staged by the band loop)
   int sp_lo, sp_hi;          // key range of the split
@@ -677,6 +677,17 @@ __device__ inline int wave_entry(const Ctx<T>& c, int t, int rg) {
   return t < c.ngp ? t : t + rg;
 }
 
+// Ring slot of list entry i.  FOLD (the helper-wave layout, exactly one global-key
+// entry): the global entry stays in the last slot for the whole loop and the band
+// entries cycle through the other kRing - 1.  Seven slots suffice for the band: in
+// the pair of steps (t, t + 1) entries t .. t + 4 are read and t + 5, t + 6 are
+// written, which take the slots of entries t - 2 and t - 1, both last read before
+// the barrier that ended the previous pair.
+template <bool FOLD>
+__device__ inline int ring_slot(int i) {
+  return FOLD ? (i == 0 ? kRing - 1 : (i - 1) % (kRing - 1)) : i % kRing;
+}
+
 __device__ inline int xcd_remap(int i, int n) {
   // consecutive workgroup ids go round-robin over the 8 XCDs: give each XCD a
   // contiguous run of logical tiles, so neighbouring tiles of one head share K / V
@@ -835,9 +846,10 @@ __device__ inline void help_wait(const int* ctr, int target) {
 // global rows (n_b <= 32 rows, one query block): keys sp_lo + 64 hw .. + 63 of kg / vg.
 // Its work is cut into phases between the barriers the band waves execute (n_bar of
 // them in all), so that no band wave waits for it:
-//   loads (with five or more barriers they are issued after the first one and with
-//   six or more K and V go out one pair of steps apart, so they do not join the
-//   launch's first burst of loads);
+//   loads (with four or more barriers they are issued after the first one and with
+//   five or more K and V go out one pair of steps apart, so they do not join the
+//   launch's first burst of loads; the combine then runs after the band waves' last
+//   barrier, beside their last step and epilogue);
 //   work phase: S^T = K Q^T with the per-key term as accumulator init, the exact row
 //     max over its 64 keys, P rounded to T, O^T = V^T P^T, V^T formed on the matrix
 //     core from row-major V; helpers 0 .. 2 write their states to LDS and helper 3
@@ -871,7 +883,7 @@ __device__ void help_run(const AttnArgs& a, const Ctx<T>& c0, int n_bar, HelpLds
   // with barriers to spare, the loads go out after the band waves' first burst of
   // loads, K in the band loop's first pair of steps and V in the second, so that their
   // 64 KB per workgroup spread over the loop's own traffic
-  const int n_wait = n_bar >= 6 ? 2 : n_bar >= 5 ? 1 : 0;
+  const int n_wait = n_bar >= 5 ? 2 : n_bar >= 4 ? 1 : 0;
   // K and V rows in the A-operand layout (lane (n, g): key 32 j + n, dims 16 t + 8 g ..),
   // 16-byte loads
   v8 qf[4];
@@ -1058,37 +1070,52 @@ __device__ void help_run(const AttnArgs& a, const Ctx<T>& c0, int n_bar, HelpLds
 // LATE_V (the helper-wave layout, 168 registers per wave): the V^T fragments are read
 // after the QK^T MFMAs are issued, into the registers the K fragments leave, and
 // arrive while the max and P are computed.
-template <typename T, bool RAW, bool ANY, bool PAST, bool BAR, bool LATE_V>
+// FOLD (the helper-wave layout): sub-block 1's first band block (tq = -1) and
+// sub-block 0's last one (tq = 2 npb - 1 >= nband) lie wholly outside the window of
+// every row of the sub-block; in their place the wave takes the global keys (block 0
+// of the global entry, which holds them all when there are at most 32), so no step of
+// the loop is spent on the global keys alone (sub-block 1 substitutes block 0 at the
+// first band step, sub-block 0 block 1 at the last; wave-uniform scalar selects of the
+// LDS base).  The global keys' scores then join the running max one step apart in the
+// two sub-blocks instead of first: the same sums in another order.
+template <typename T, bool RAW, bool ANY, bool PAST, bool BAR, bool LATE_V, bool FOLD>
 __device__ __forceinline__ void band_step(const Ctx<T>& c, Slot<T>* ring, int tt, int rg, int sb,
                                           float c2, Stage<T>& set,
                                           const typename Frag<T>::v8 qf[4], f32x16 o[2],
                                           float& m_run, float& l_run) {
   typedef typename Frag<T>::v8 v8;
-  const Slot<T>& cs = ring[wave_entry(c, tt, rg) % kRing];
+  const Slot<T>& cs = ring[ring_slot<FOLD>(wave_entry(c, tt, rg))];
+  const int bt = tt - c.ngp;
+  const bool gs0 = FOLD && sb == 1 && bt == 0;
+  const bool gs1 = FOLD && sb == 0 && bt == c.npb - 1;
+  const Slot<T>& cs0 = gs0 ? ring[kRing - 1] : cs;
+  const Slot<T>& cs1 = gs1 ? ring[kRing - 1] : cs;
+  const int j1 = gs1 ? 0 : 1;
   KFrag<T> kf0, kf1;
-  read_k<T>(kf0, cs, 0);
-  read_k<T>(kf1, cs, 1);
-  const f32x16 c0 = read_bias<T>(cs, 0), c1 = read_bias<T>(cs, 1);
+  read_k<T>(kf0, cs0, 0);
+  read_k<T>(kf1, cs1, j1);
+  const f32x16 c0 = read_bias<T>(cs0, 0), c1 = read_bias<T>(cs1, j1);
   VFrag<T> vf0, vf1;
   if (!LATE_V) {
-    read_v<T>(vf0, cs, 0);
-    read_v<T>(vf1, cs, 1);
+    read_v<T>(vf0, cs0, 0);
+    read_v<T>(vf1, cs1, j1);
   }
   f32x16 s0 = qk_frag_c<T>(kf0, qf, c0);
   f32x16 s1 = qk_frag_c<T>(kf1, qf, c1);
   if (LATE_V) {
     __builtin_amdgcn_sched_barrier(0);
-    read_v<T>(vf0, cs, 0);
-    read_v<T>(vf1, cs, 1);
+    read_v<T>(vf0, cs0, 0);
+    read_v<T>(vf1, cs1, j1);
   }
   // blocks tq = 1 .. (W - 31) / 32 of a sub-block lie wholly inside the window of
-  // every row; the others get the band mask
-  const int tq0 = 2 * (tt - c.ngp) - sb;
+  // every row; the others get the band mask (a folded global block none: block 1
+  // with an unbounded window keeps every key)
+  const int tq0 = 2 * bt - sb;
   const bool inner0 = tq0 >= 1 && kBlk * tq0 + kBlk - 1 <= c.W;
   const bool inner1 = tq0 + 1 >= 1 && kBlk * (tq0 + 1) + kBlk - 1 <= c.W;
   if (tt >= c.ngp && !(inner0 && inner1)) {
-    band_mask(s0, tq0, c.W);
-    band_mask(s1, tq0 + 1, c.W);
+    band_mask(s0, gs0 ? 1 : tq0, gs0 ? 0x7fffffff : c.W);
+    band_mask(s1, gs1 ? 1 : tq0 + 1, gs1 ? 0x7fffffff : c.W);
   }
   const float ms = cross_half_max(vmax(max16(s0), max16(s1))) * c2;
   if (__builtin_expect(__ballot(ms > m_run + kLazy) != 0ull, 0)) rescale(ms, o, m_run, l_run);
@@ -1098,7 +1125,7 @@ __device__ __forceinline__ void band_step(const Ctx<T>& c, Slot<T>* ring, int tt
   pv_frag<T>(vf0, p0, o);
   pv_frag<T>(vf1, p1, o);
   const int e = tt + kAhead;
-  store_entry<T, RAW, ANY, PAST>(ring[e % kRing], set, c, e);
+  store_entry<T, RAW, ANY, PAST>(ring[ring_slot<FOLD>(e)], set, c, e);
   __builtin_amdgcn_sched_barrier(0);
   load_entry<T, ANY, PAST>(set, c, e + kDepth);
   if (BAR) __syncthreads();
@@ -1147,7 +1174,11 @@ __attribute__((amdgpu_waves_per_eu(HELP ? 3 : 2, HELP ? 3 : 2))) void attn_mfma_
   const int nband = (c.W + 2 * kBlk - 1) / kBlk;
   const int npb = (nband + 2) / 2;
   const int n_steps = c.ngp + npb;
+  c.npb = npb;
   c.n_list = c.ngp + npb + kRowGroups - 1;
+  // HELP: the one global-key entry is folded into the band steps (band_step), so the
+  // loop runs steps kF .. n_steps - 1 (the list keeps the global entry as entry 0)
+  constexpr int kF = HELP ? 1 : 0;
   const size_t head = (size_t)c.bh * c.S * 64;
   c.mask = (const T*)(RAW ? a.local_mask : a.bias) + (size_t)c.b * c.S;
   c.gi = ANY ? a.gidx + (size_t)c.b * c.S : nullptr;
@@ -1158,7 +1189,7 @@ __attribute__((amdgpu_waves_per_eu(HELP ? 3 : 2, HELP ? 3 : 2))) void attn_mfma_
     __shared__ __attribute__((aligned(16))) HelpLds hl;
     if (wave >= kWaves) {   // uniform: the whole wave
       // the band waves execute the prologue barrier and one per pair of steps
-      help_run<T, RAW, ANY>(a, c, 1 + n_steps / 2, hl, &s_nb);
+      help_run<T, RAW, ANY>(a, c, 1 + (n_steps - kF) / 2, hl, &s_nb);
       return;
     }
   }
@@ -1199,9 +1230,9 @@ __attribute__((amdgpu_waves_per_eu(HELP ? 3 : 2, HELP ? 3 : 2))) void attn_mfma_
     load_q<T>(qg0, (const T*)a.qg + ((size_t)c.bh * a.G + (n < a.G ? n : 0)) * 64, n < a.G);
   }
   __builtin_amdgcn_sched_barrier(0);
-  Stage<T> pro[kAhead];
+  Stage<T> pro[kAhead + kF];
 #pragma unroll
-  for (int i = 0; i < kAhead; ++i) load_entry<T, ANY, true>(pro[i], c, i);
+  for (int i = 0; i < kAhead + kF; ++i) load_entry<T, ANY, true>(pro[i], c, i);
   // Q before the register sets: in the loop its wait count then never holds back
   // the sets in flight
   v8 qf[4];
@@ -1223,7 +1254,7 @@ __attribute__((amdgpu_waves_per_eu(HELP ? 3 : 2, HELP ? 3 : 2))) void attn_mfma_
   Stage<T> st[kDepth];
 #pragma unroll
   for (int u = 0; u < kDepth; ++u) {
-    load_entry<T, ANY, true>(st[(kAhead + u) % kDepth], c, kAhead + u);
+    load_entry<T, ANY, true>(st[(kAhead + kF + u) % kDepth], c, kAhead + kF + u);
     __builtin_amdgcn_sched_barrier(0);
   }
   c.nb = counter ? count_globals<T, RAW, ANY>(a, c.b, gfirst) : 0;
@@ -1232,7 +1263,8 @@ __attribute__((amdgpu_waves_per_eu(HELP ? 3 : 2, HELP ? 3 : 2))) void attn_mfma_
     // the first entries are written before the prologue barrier (wave 0 alone writes
     // the per-key terms, with its own count)
 #pragma unroll
-    for (int i = 0; i < kAhead; ++i) store_entry<T, RAW, ANY, true>(ring[i], pro[i], c, i);
+    for (int i = 0; i < kAhead + kF; ++i)
+      store_entry<T, RAW, ANY, true>(ring[ring_slot<HELP>(i)], pro[i], c, i);
     if (counter && lane == 0) s_nb = c.nb;
     __syncthreads();
     c.nb = __builtin_amdgcn_readfirstlane(s_nb);
@@ -1258,7 +1290,7 @@ __attribute__((amdgpu_waves_per_eu(HELP ? 3 : 2, HELP ? 3 : 2))) void attn_mfma_
 
   f32x16 o[2] = {f32x16{}, f32x16{}};
   float m_run = kNegBig, l_run = 0.0f;
-  constexpr int s0i = kAhead % kDepth, s1i = (kAhead + 1) % kDepth;
+  constexpr int s0i = (kAhead + kF) % kDepth, s1i = (kAhead + kF + 1) % kDepth;
   // Barriers: 8 waves, one per pair of steps (an entry written at step t is read from
   // step t + 2 on; the slot it overwrites, entry t - 3's, was last read before the
   // previous barrier); 4 waves, one per step (written at t, read from t + 1; the slot
@@ -1267,17 +1299,17 @@ __attribute__((amdgpu_waves_per_eu(HELP ? 3 : 2, HELP ? 3 : 2))) void attn_mfma_
   // past it (the split's first round)
   constexpr bool kBar0 = !kPairs;
   const int n_plain = c.split_tail ? c.n_list - kAhead - kDepth : n_steps;
-  int t0 = 0;
+  int t0 = kF;
   for (; t0 + 2 <= n_plain; t0 += 2) {
-    band_step<T, RAW, ANY, false, kBar0, HELP>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
-    band_step<T, RAW, ANY, false, true, HELP>(c, ring, t0 + 1, rg, sb, c2, st[s1i], qf, o, m_run, l_run);
+    band_step<T, RAW, ANY, false, kBar0, HELP, HELP>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
+    band_step<T, RAW, ANY, false, true, HELP, HELP>(c, ring, t0 + 1, rg, sb, c2, st[s1i], qf, o, m_run, l_run);
   }
   for (; t0 + 2 <= n_steps; t0 += 2) {
-    band_step<T, RAW, ANY, true, kBar0, HELP>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
-    band_step<T, RAW, ANY, true, true, HELP>(c, ring, t0 + 1, rg, sb, c2, st[s1i], qf, o, m_run, l_run);
+    band_step<T, RAW, ANY, true, kBar0, HELP, HELP>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
+    band_step<T, RAW, ANY, true, true, HELP, HELP>(c, ring, t0 + 1, rg, sb, c2, st[s1i], qf, o, m_run, l_run);
   }
   if (t0 < n_steps)
-    band_step<T, RAW, ANY, true, kBar0, HELP>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
+    band_step<T, RAW, ANY, true, kBar0, HELP, HELP>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
 
   // the split's queries (rows 0 .. 31 below G; rows from n_b on are computed but not
   // published) go out before the epilogue, which hides their latency
@@ -1388,11 +1420,12 @@ hipError_t launch_t(const AttnArgs& args, hipStream_t st) {
   // helper waves for the global rows: one query block (G <= 32), one 256-key split per
   // tile, and at least three barriers in the band loop's schedule for their phases
   // (LF_ATTN_NO_HELP=1, read on every call, keeps the band tiles' own split)
-  const int n_steps = (a.G + kEnt - 1) / kEnt + ((a.W + 2 * kBlk - 1) / kBlk + 2) / 2;
+  // (with helpers the global-key entry is folded into the band steps: npb steps)
+  const int npb = ((a.W + 2 * kBlk - 1) / kBlk + 2) / 2;
   const char* no_help = getenv("LF_ATTN_NO_HELP");
   const bool help = !gwg && !w4 && !a.any_pos && a.G > 0 && a.G <= 32 &&
                     a.split_len == kHelp * kHelpKeys &&
-                    1 + n_steps / 2 >= 3 && !(no_help && no_help[0] == '1');
+                    1 + npb / 2 >= 3 && !(no_help && no_help[0] == '1');
   if (gwg) {
     a.n_split = 1;
     a.split_len = (a.S + kBlk * kWaves - 1) / (kBlk * kWaves) * (kBlk * kWaves);
