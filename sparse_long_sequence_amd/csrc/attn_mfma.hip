@@ -1323,19 +1323,28 @@ __attribute__((amdgpu_waves_per_eu(HELP ? 3 : 2, HELP ? 3 : 2))) void attn_mfma_
     const float l_tot = cross_half_sum(l_run);
     // global rows are written by the combine
     const bool local = srow < c.S && (ANY ? (row_gflag & 0x7fff) != 0 : srow >= c.nb);
-    if (local) {
-      const bool live = mask_live<RAW>(Elem<T>::to_f(row_mask));
-      const float inv = live ? 1.0f / l_tot : 0.0f;
-      T* dst = (T*)a.out + (size_t)c.b * a.out_sb + (size_t)c.h * a.out_sh + (size_t)srow * a.out_ss;
+    const bool live = mask_live<RAW>(Elem<T>::to_f(row_mask));
+    const float inv = live ? 1.0f / l_tot : 0.0f;
+    T* dst = (T*)a.out + (size_t)c.b * a.out_sb + (size_t)c.h * a.out_sh + (size_t)srow * a.out_ss;
+    // lanes n and n + 32 hold alternate groups of 4 dims of one row; each sends the
+    // other the group it lacks (every lane active), so that lane (n, 0) stores dims
+    // 16p .. 16p + 7 and lane (n, 1) dims 16p + 8 .. 16p + 15 of each 32-dim half as
+    // one 16-byte store: half the store instructions, 32 contiguous bytes per row each
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          v4 w;
+      for (int p = 0; p < 2; ++p) {
+        v4 x, y;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) w[i] = Elem<T>::from_f(live ? o[mb][4 * jj + i] * inv : 0.0f);
-          *(v4*)(dst + 32 * mb + 8 * jj + 4 * g) = w;
+        for (int i = 0; i < 4; ++i) {
+          x[i] = Elem<T>::from_f(live ? o[mb][8 * p + i] * inv : 0.0f);
+          y[i] = Elem<T>::from_f(live ? o[mb][8 * p + 4 + i] * inv : 0.0f);
         }
+        const u32x2 xb = __builtin_bit_cast(u32x2, x), yb = __builtin_bit_cast(u32x2, y);
+        const u32x2 sd = g ? xb : yb;
+        const u32x2 rb = {(uint32_t)__shfl_xor((int)sd[0], 32), (uint32_t)__shfl_xor((int)sd[1], 32)};
+        const u32x4 w = g ? u32x4{rb[0], rb[1], yb[0], yb[1]} : u32x4{xb[0], xb[1], rb[0], rb[1]};
+        if (local) *(u32x4*)(dst + 32 * mb + 16 * p + 8 * g) = w;
       }
     }
   };
