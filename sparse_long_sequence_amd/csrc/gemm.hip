@@ -93,6 +93,23 @@ __device__ __forceinline__ void epilogue4(const GemmArgs& g, int m, int nb, cons
   }
 }
 
+// Stores of 16-bit outputs w[jj] = columns 8 jj + 4 gq .. + 3 of one row (jj = 0..3;
+// dst = the row's column 0 of the 32-column tile): lanes n and n + 32 hold the two
+// halves of each 8-column group and send each other the half the other lacks (every
+// lane of the pair active), so lane gq stores columns 16 p + 8 gq .. + 7 (p = 0, 1) as
+// one 16-byte store: half the store instructions of 8-byte stores.
+template <typename T>
+__device__ __forceinline__ void store_pairs16(T* dst, int gq, const typename Elem<T>::vec4 w[4]) {
+  static_assert(sizeof(T) == 2, "16-bit outputs");
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const u32x2 x = __builtin_bit_cast(u32x2, w[2 * p]), y = __builtin_bit_cast(u32x2, w[2 * p + 1]);
+    const u32x2 sd = gq ? x : y;
+    const u32x2 rb = {(uint32_t)__shfl_xor((int)sd[0], 32), (uint32_t)__shfl_xor((int)sd[1], 32)};
+    *(u32x4*)(dst + 16 * p + 8 * gq) = gq ? u32x4{rb[0], rb[1], y[0], y[1]} : u32x4{x[0], x[1], rb[0], rb[1]};
+  }
+}
+
 // Epilogue of one 32 x 32 MFMA tile: the lane's 16 sums are columns cbase + 8 jj +
 // 4 gq .. + 3 (jj = 0..3) of output row m, with their bias bv[jj] and residual
 // rv[jj] already in registers; cbase (a multiple of 32) is the same for the whole
@@ -115,14 +132,27 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& g, int m, int cbas
     const int ti = cbase / g.D, nn = cbase - ti * g.D;
     const int h = nn >> 6, d0 = nn & 63;
     const int bb = m / g.rows, rr = m - bb * g.rows;
-    T* dst = (T*)g.heads[ti] + (((size_t)bb * g.H + h) * g.rows + rr) * 64 + d0 + 4 * gq;
+    T* dst = (T*)g.heads[ti] + (((size_t)bb * g.H + h) * g.rows + rr) * 64 + d0;
+    v4 w[4];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      v4 w;
+    for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = Elem<T>::from_f(acc[4 * jj + e] + Elem<T>::to_f(bv[jj][e]));
-      *(v4*)(dst + 8 * jj) = w;
+      for (int e = 0; e < 4; ++e) w[jj][e] = Elem<T>::from_f(acc[4 * jj + e] + Elem<T>::to_f(bv[jj][e]));
+    if constexpr (sizeof(T) == 2) {
+      store_pairs16<T>(dst, gq, w);
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) *(v4*)(dst + 8 * jj + 4 * gq) = w[jj];
     }
+    return;
+  }
+  if constexpr (EPI == kEpiGelu && sizeof(T) == 2) {
+    v4 w[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[jj][e] = Elem<T>::from_f(gelu(acc[4 * jj + e] + Elem<T>::to_f(bv[jj][e])));
+    store_pairs16<T>((T*)g.out + (size_t)m * g.ldo + cbase, gq, w);
     return;
   }
 #pragma unroll
