@@ -1216,6 +1216,11 @@ __attribute__((amdgpu_waves_per_eu(HELP ? 3 : 2, HELP ? 3 : 2))) void attn_mfma_
   // the count to the other waves at the prologue barrier.  (Every workgroup of a
   // batch row reads the same mask values: one request per workgroup instead of one
   // per wave keeps that cache line from becoming a hot spot.)
+  // helper layout: a tile whose rows are all padding (or past S) has all-zero output;
+  // its band waves skip the loop and keep only its barriers (the helper waves still
+  // compute the tile's key split of the global rows on their schedule)
+  __shared__ int s_live[kWaves];
+  bool tile_dead = false;
   const bool counter = wave == 0;
   const int gfirst = counter ? count_load<T, RAW, ANY>(a, c.b) : 0;
   __builtin_amdgcn_sched_barrier(0);
@@ -1266,8 +1271,19 @@ __attribute__((amdgpu_waves_per_eu(HELP ? 3 : 2, HELP ? 3 : 2))) void attn_mfma_
     for (int i = 0; i < kAhead + kF; ++i)
       store_entry<T, RAW, ANY, true>(ring[ring_slot<HELP>(i)], pro[i], c, i);
     if (counter && lane == 0) s_nb = c.nb;
+    if constexpr (HELP) {
+      // does any of the wave's rows exist and carry a live mask value?
+      const bool wlive = __ballot(srow < c.S && mask_live<RAW>(Elem<T>::to_f(row_mask))) != 0ull;
+      if (lane == 0) s_live[wave] = wlive ? 1 : 0;
+    }
     __syncthreads();
     c.nb = __builtin_amdgcn_readfirstlane(s_nb);
+    if constexpr (HELP) {
+      int any = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) any |= s_live[w];
+      tile_dead = __builtin_amdgcn_readfirstlane(any) == 0;
+    }
   } else {
     if (counter && lane == 0) s_nb = c.nb;
     __syncthreads();
@@ -1300,6 +1316,10 @@ __attribute__((amdgpu_waves_per_eu(HELP ? 3 : 2, HELP ? 3 : 2))) void attn_mfma_
   constexpr bool kBar0 = !kPairs;
   const int n_plain = c.split_tail ? c.n_list - kAhead - kDepth : n_steps;
   int t0 = kF;
+  if (HELP && tile_dead) {
+    for (int i = 0; i < (n_steps - kF) / 2; ++i) __syncthreads();
+    t0 = n_steps;
+  }
   for (; t0 + 2 <= n_plain; t0 += 2) {
     band_step<T, RAW, ANY, false, kBar0, HELP, HELP>(c, ring, t0, rg, sb, c2, st[s0i], qf, o, m_run, l_run);
     band_step<T, RAW, ANY, false, true, HELP, HELP>(c, ring, t0 + 1, rg, sb, c2, st[s1i], qf, o, m_run, l_run);
