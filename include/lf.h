@@ -43,7 +43,7 @@
  *    the band work; shorter ones run 256-row workgroups, one per CU.  The outputs
  *    agree to rounding order; LF_ATTN_WAVES=4 or 8 (read on every call) forces the
  *    128-row (4 waves) or the 256-row (8 waves) workgroups.  In the 256-row
- *    workgroups with at most 32 leading global tokens (and W >= 160), four more
+ *    workgroups with at most 32 global tokens (and W >= 160), four more
  *    waves compute the tile's key split of the global rows, its merge and the last
  *    tile's combine while the band waves run the band loop, and the band waves take
  *    the global keys inside their first and last band steps (blocks there that lie

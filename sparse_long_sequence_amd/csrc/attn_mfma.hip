@@ -1452,7 +1452,7 @@ hipError_t launch_t(const AttnArgs& args, hipStream_t st) {
   // (with helpers the global-key entry is folded into the band steps: npb steps)
   const int npb = ((a.W + 2 * kBlk - 1) / kBlk + 2) / 2;
   const char* no_help = getenv("LF_ATTN_NO_HELP");
-  const bool help = !gwg && !w4 && !a.any_pos && a.G > 0 && a.G <= 32 &&
+  const bool help = !gwg && !w4 && (!a.any_pos || a.raw) && a.G > 0 && a.G <= 32 &&
                     a.split_len == kHelp * kHelpKeys &&
                     1 + npb / 2 >= 3 && !(no_help && no_help[0] == '1');
   if (gwg) {
@@ -1483,7 +1483,9 @@ hipError_t launch_t(const AttnArgs& args, hipStream_t st) {
     if (eg != hipSuccess) return eg;
   } else if (help) {
     constexpr int kHT = kThreads + 64 * kHelp;
-    if (a.raw)
+    if (a.raw && a.any_pos)
+      attn_mfma_kernel<T, true, true, false, true><<<(unsigned)grid, kHT, 0, st>>>(a, n_tiles);
+    else if (a.raw)
       attn_mfma_kernel<T, true, false, false, true><<<(unsigned)grid, kHT, 0, st>>>(a, n_tiles);
     else
       attn_mfma_kernel<T, false, false, false, true><<<(unsigned)grid, kHT, 0, st>>>(a, n_tiles);
