@@ -30,7 +30,11 @@
 // where band entry j holds keys r0 - W/2 + 64j ..; row group rg needs band blocks
 // 2rg .. 2rg + nband (nband = (W + 63) / 32), i.e. band entries rg .. rg + npb - 1.
 // At step t every wave reads entry t (global phase) or t + rg (band phase: the row
-// groups walk the band on a diagonal, so none of them idles); entry t + kAhead is
+// groups walk the band on a diagonal, so none of them idles).  In the helper-wave
+// layout (at most 32 global tokens) there is no global phase: the global entry stays
+// in the ring's last slot and each sub-block takes its keys in place of a band block
+// that lies outside all of its rows' windows (sub-block 1's first, sub-block 0's last),
+// the band entries cycling through the other slots.  Entry t + kAhead is
 // written into the ring from registers and the loads of entry t + kAhead + 2 are
 // issued.  8 waves: kAhead = 5, steps in pairs with one barrier per pair (an entry
 // written at step t is first read at step t + 2, after the barrier that ends the pair,
